@@ -1,0 +1,137 @@
+"""Pins for oracle.prep: LayerNorm, RoPE, bf16 / e4m3 rounding, power-of-two
+scales.  Each check compares against something other than the oracle itself:
+closed forms, a library routine (torch CPU casts and layer_norm), or a
+hand-computed fixture."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import prep
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_layernorm_closed_form():
+    # each output row has mean 0 and biased variance var/(var+eps)
+    g = np.random.default_rng(1)
+    x = g.standard_normal((64, 128)) * 3 + 1.5
+    eps = 1e-6
+    y = prep.layer_norm(x, eps)
+    var = x.var(axis=1)
+    np.testing.assert_allclose(y.mean(axis=1), 0, atol=1e-12)
+    np.testing.assert_allclose(y.var(axis=1), var / (var + eps), rtol=1e-12)
+
+
+def test_layernorm_vs_torch():
+    g = np.random.default_rng(2)
+    x = g.standard_normal((32, 128))
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (128,), eps=1e-6).numpy()
+    np.testing.assert_allclose(prep.layer_norm(x, 1e-6), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layernorm_large_eps_changes_scale():
+    # a dropped eps would fail this: constant-free row of variance 1 -> 1/sqrt(1+eps)
+    x = np.array([[1.0, -1.0, 1.0, -1.0]])
+    y = prep.layer_norm(x, eps=3.0)
+    np.testing.assert_allclose(y, x / 2.0, rtol=1e-15)
+
+
+def test_rope_hand_fixture():
+    rows = {l.split()[0]: l.split()[1:] for l in open(os.path.join(GOLD, "rope_hand.txt"))
+            if l.strip() and not l.startswith("#")}
+    x = np.array([[float(v) for v in rows["x"]]])
+    pos = np.array([int(rows["pos"][0])])
+    out = prep.rope_leading(x, pos, rope_dim=4, rope_main_dim=4, theta=1e4)
+    np.testing.assert_allclose(out[0], [float(v) for v in rows["out"]], rtol=1e-14)
+
+
+def test_rope_properties():
+    g = np.random.default_rng(3)
+    D, R = 128, 64
+    q = g.standard_normal((5, 3, D))
+    k = g.standard_normal((5, D))
+    # position 0 is the identity
+    np.testing.assert_array_equal(prep.rope_leading(q, np.zeros(5), R, 64, 1e4), q)
+    pos = np.array([0, 1, 17, 500, 4095])
+    qr = prep.rope_leading(q, pos, R, 64, 1e4)
+    # every (i, i+R/2) pair keeps its norm; dims beyond R are untouched
+    half = R // 2
+    n0 = q[..., :half] ** 2 + q[..., half:R] ** 2
+    n1 = qr[..., :half] ** 2 + qr[..., half:R] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=1e-12)
+    np.testing.assert_array_equal(qr[..., R:], q[..., R:])
+    # dot products over the rotated dims depend only on the position difference
+    a, b = g.standard_normal(D), g.standard_normal(D)
+    def dot(m, n):
+        ra = prep.rope_leading(a[None], np.array([m]), R, 64, 1e4)[0]
+        rb = prep.rope_leading(b[None], np.array([n]), R, 64, 1e4)[0]
+        return ra @ rb
+    np.testing.assert_allclose(dot(10, 3), dot(107, 100), rtol=1e-9)
+    np.testing.assert_allclose(dot(3, 10), dot(1003, 1010), rtol=1e-9)
+    assert abs(dot(10, 3) - dot(10, 4)) > 1e-6
+
+
+def test_round_bf16_vs_torch():
+    g = np.random.default_rng(4)
+    x = np.concatenate([g.standard_normal(100000) * 10.0 ** g.integers(-30, 30, 100000),
+                        [0.0, -0.0, 1.0, 3.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 2 ** -130]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(prep.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_round_e4m3_vs_torch():
+    g = np.random.default_rng(5)
+    x = np.concatenate([g.uniform(-448, 448, 50000), g.standard_normal(50000) * 2.0 ** -6,
+                        [0.0, 448.0, -448.0, 2 ** -9, 2 ** -10, 3 * 2 ** -10, 1.0625, 1.1875]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(prep.round_e4m3(x.astype(np.float64)), ref)
+
+
+def test_ue8m0_scale_properties():
+    g = np.random.default_rng(6)
+    amax = np.concatenate([np.abs(g.standard_normal(10000)) * 10.0 ** g.integers(-8, 8, 10000),
+                           448.0 * 2.0 ** np.arange(-10, 10), [448.0 * (1 + 2 ** -40)]])
+    s = prep.ue8m0_scale(amax)
+    m, _ = np.frexp(s)
+    assert np.all(m == 0.5)                     # powers of two
+    assert np.all(amax <= 448.0 * s)            # no saturation
+    assert np.all(amax > 448.0 * s / 2)         # smallest such power
+    assert prep.ue8m0_scale(np.array([0.0]))[0] == 1.0
+    np.testing.assert_array_equal(prep.ue8m0_scale(448.0 * 2.0 ** np.arange(-3, 4)), 2.0 ** np.arange(-3, 4))
+
+
+def test_quant_roundtrip_and_idempotent():
+    g = np.random.default_rng(7)
+    x = g.standard_normal((50, 4, 128))
+    codes, s = prep.quant_e4m3_blocks(x, 128)
+    assert np.all(np.abs(codes) <= 448)
+    # codes are e4m3 values
+    np.testing.assert_array_equal(prep.round_e4m3(codes), codes)
+    deq = codes * np.repeat(s, 128, axis=-1)
+    # relative error of e4m3 rounding is at most 2^-4 for normal codes
+    big = np.abs(codes) >= 2 ** -6
+    assert np.all(np.abs(deq - x)[big] <= 2 ** -4 * np.abs(x)[big] + 1e-300)
+    codes2, s2 = prep.quant_e4m3_blocks(deq, 128)
+    np.testing.assert_array_equal(codes2 * np.repeat(s2, 128, axis=-1), deq)
+
+
+def test_fp8_fold_equals_dequantised_definition():
+    # score(q8, k8, w*sq, sk) equals the definition on dequantised values because
+    # the scales are positive and relu is positively homogeneous
+    from oracle import indexer
+    g = np.random.default_rng(8)
+    H, D, N = 4, 128, 6
+    q = g.standard_normal((1, H, D))
+    k = g.standard_normal((N, D))
+    w = g.random((1, H)).astype(np.float32).astype(np.float64)   # fp32 weights: the fold is exact
+    p = prep.prepare_indexer_inputs(q, k, w, np.zeros(1), np.zeros(N), "fp8")
+    q8, sq = prep.quant_e4m3_blocks(q, D)
+    kn = prep.layer_norm(k)
+    k8, sk = prep.quant_e4m3_blocks(kn, D)
+    deq_q = q8 * sq
+    deq_k = k8 * sk
+    ref = indexer.score_row(deq_q[0], deq_k, w[0])
+    got = indexer.score_row(p["q"][0], p["k"], p["w"][0], p["k_scale"])
+    np.testing.assert_allclose(got, ref, rtol=1e-12)
