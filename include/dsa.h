@@ -1,0 +1,226 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) hot path on AMD
+ * Instinct MI355X (gfx950): lightning indexer -> per-row top-k -> sparse MLA.
+ *
+ * Sources.  The method is described on three pages: the vime docs page
+ * "Day-0 Model Plugins", vime pull request #502 with its review comments, and
+ * the vLLM API page "vllm.models.kimi_k3.nvidia.dsa" (classes KimiK3DSAAttention,
+ * KimiK3DSAIndexer, KimiK3DSAIndexerKNorm).  Each entry point below names the
+ * passage that defines its operation.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (HIP device memory), row-major and
+ *     densely packed unless a leading dimension (ld_*) is given.  The caller owns
+ *     every buffer; the library never allocates, frees or retains memory.
+ *   - Packed (THD) sequences: the tokens of several sequences are concatenated;
+ *     key indices are global positions in the packed key buffer.
+ *   - A row's key window is the half-open range [row_starts[t], row_ends[t]).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream: no host synchronisation, no host<->device
+ *     copies, no device-dependent host control flow, so the calls can be captured
+ *     in a HIP graph.  The library holds no state and is safe to call from
+ *     several host threads.
+ *   - Every call returns DSA_OK (0) or a negative dsa_status.  Arguments are
+ *     validated on the host before anything is enqueued; on error nothing is
+ *     enqueued and no output is touched.  Device-side preconditions (windows
+ *     inside [0, n_k], indices in range, no NaN scores in a window) are not
+ *     checked; violating them gives unspecified output but stays inside the
+ *     buffers described here, except where noted.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1, /* null pointer, negative size, ld too small ... */
+  DSA_ERR_UNSUPPORTED = -2, /* shape / dtype combination without a kernel    */
+  DSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required    */
+  DSA_ERR_LAUNCH = -4,      /* the HIP runtime rejected a kernel launch      */
+} dsa_status;
+
+typedef enum dsa_dtype {
+  DSA_DTYPE_F32 = 0,      /* float32                                    */
+  DSA_DTYPE_BF16 = 1,     /* bfloat16                                   */
+  DSA_DTYPE_FP8_E4M3 = 2, /* OCP float8 e4m3fn (max 448), one byte each */
+} dsa_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* dsa_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int dsa_version(void);
+
+/*
+ * dsa_row_windows -- per-row key windows of packed sequences.
+ *
+ * Passage: the window rule of the fallback top-k in review comment 3 of vime
+ * pull request #502 (column c of a row is valid when row_starts <= c < row_ends),
+ * combined with the packed-position rebase of review comment 1 (indices are
+ * offsets into the packed key buffer, sample offsets advance by the sample's
+ * full token length).
+ *
+ *   cu_seqlens_q, cu_seqlens_k  int32 [n_seqs + 1], exclusive prefix sums of the
+ *                               query and key counts of each sequence.  The
+ *                               queries of sequence b are its LAST q_len tokens.
+ *   n_rows                      = cu_seqlens_q[n_seqs] (passed by the caller so
+ *                               that no device value is read on the host).
+ *   causal                      1: the query at local position p of sequence b
+ *                               sees keys [cu_k[b], cu_k[b] + k_len - q_len + p + 1)
+ *                               (every key up to and including its own token;
+ *                               prefill q_len == k_len gives end = t + 1, decode
+ *                               q_len == 1 gives the whole cache).  0: the whole
+ *                               sequence [cu_k[b], cu_k[b+1]).
+ *   row_starts, row_ends        int32 [n_rows] outputs.
+ * A causal window that would end before it starts (k_len < q_len) is empty.
+ */
+int dsa_row_windows(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int32_t n_seqs, int64_t n_rows, int32_t causal,
+                    int32_t* row_starts, int32_t* row_ends, void* stream);
+
+/*
+ * dsa_indexer_prep -- prepare indexer operands from raw projections.
+ *
+ * Passages (vLLM API page "vllm.models.kimi_k3.nvidia.dsa"):
+ *   KimiK3DSAIndexerKNorm          LayerNorm of the shared index key, weight 1,
+ *                                  bias 0, computed in fp32, cast to the output type;
+ *   KimiK3DSAIndexer._apply_index_rope
+ *                                  RoPE on the leading rope_dim dims of every head
+ *                                  (q) and of the key, half-split pairing (dim i
+ *                                  with dim i + rope_dim/2), after the key norm,
+ *                                  frequencies = the leading rope_dim/2 frequencies
+ *                                  theta^(-2i/rope_main_dim) of the main cache;
+ *   KimiK3DSAIndexer.__init__ / score
+ *                                  power-of-two ("ue8m0") scales per head_dim block,
+ *                                  read as fp32; the query scale is folded into the
+ *                                  per-head weights.
+ *
+ *   q_raw   f32 [n_q, n_heads, head_dim]   k_raw f32 [n_k, head_dim]
+ *   w       f32 [n_q, n_heads]             pos_q int32 [n_q], pos_k int32 [n_k]
+ *           (positions inside each sequence; ignored when rope_dim == 0, may be NULL then)
+ *   dtype   output type of q_out / k_out: F32, BF16 or FP8_E4M3.
+ *   q_out   [n_q, n_heads, head_dim] of dtype;  k_out [n_k, head_dim] of dtype.
+ *   w_out   f32 [n_q, n_heads]: w (F32/BF16) or w * q_scale (FP8_E4M3).
+ *   k_scale_out  f32 [n_k]: the key scale for FP8_E4M3, else ignored (may be NULL).
+ * Scale rule (FP8_E4M3): s = the smallest power of two with amax <= 448 * s
+ * (s = 1 for an all-zero block); codes = round-to-nearest-even(x / s).
+ * Supported: head_dim <= 256 and even; rope_dim even and <= head_dim.
+ */
+int dsa_indexer_prep(const float* q_raw, const float* k_raw, const float* w,
+                     const int32_t* pos_q, const int32_t* pos_k,
+                     int64_t n_q, int64_t n_k, int32_t n_heads, int32_t head_dim,
+                     int32_t rope_dim, int32_t rope_main_dim, float rope_theta,
+                     float eps, int32_t dtype,
+                     void* q_out, void* k_out, float* w_out, float* k_scale_out,
+                     void* stream);
+
+/*
+ * dsa_indexer_scores -- lightning-indexer scores over each row's window.
+ *
+ * Passage: the operands KimiK3DSAIndexer.forward and .score build on the vLLM API
+ * page "vllm.models.kimi_k3.nvidia.dsa" (per-head queries, one shared key per
+ * token, per-head weights with the query scale folded in, fp32 key scales), scored
+ * with the DSA lightning-indexer formula
+ *     score[t, s] = k_scale[s] * sum_h w[t, h] * max(0, q[t, h, :] . k[s, :])
+ * for row_starts[t] <= s < row_ends[t].
+ *
+ *   q        [n_q, n_heads, head_dim] of dtype
+ *   k        [n_k, head_dim] of dtype
+ *   k_scale  f32 [n_k] (FP8_E4M3 only; must be NULL otherwise)
+ *   w        f32 [n_q, n_heads]
+ *   scores   f32 [n_q, ld_scores], ld_scores >= n_k.  ONLY in-window entries are
+ *            written; everything else is left untouched (it may hold garbage).
+ * Accumulation is fp32.  Supported: BF16 and FP8_E4M3 with head_dim == 128 and
+ * 1 <= n_heads <= 64 (matrix-core path); F32 with head_dim <= 256, n_heads <= 64
+ * and n_heads * head_dim <= 8192.
+ */
+int dsa_indexer_scores(const void* q, const void* k, const float* k_scale,
+                       const float* w, const int32_t* row_starts,
+                       const int32_t* row_ends, int64_t n_q, int64_t n_k,
+                       int32_t n_heads, int32_t head_dim, int32_t dtype,
+                       float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * dsa_topk -- per-row top-k of a score matrix, with windows and -1 padding.
+ *
+ * Passage: the fallback top-k of review comment 3 of vime pull request #502
+ * (torch_dsa_topk with the suggested window mask): columns outside
+ * [row_starts, row_ends) are never selected; k_eff = min(index_topk, number of
+ * selectable columns); the remaining slots are -1.  Readings fixed here: ties go
+ * to the lowest column; -inf is never selected (+inf is); -0.0 equals +0.0; the
+ * selected columns are written in ASCENDING column order, then the -1 padding.
+ *
+ *   scores    f32 [n_q, ld_scores]; only in-window entries are read.
+ *   topk_idx  int32 [n_q, index_topk], every entry written (global columns).
+ *   workspace may be NULL when dsa_topk_workspace_size(...) returns 0.
+ * Bit-exact: the result is a function of the fp32 score bits only.
+ * Supported: 1 <= index_topk <= 65536; windows within [0, n_cols].
+ */
+size_t dsa_topk_workspace_size(int64_t n_q, int64_t n_cols, int32_t index_topk);
+int dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_starts,
+             const int32_t* row_ends, int64_t n_q, int64_t n_cols,
+             int32_t index_topk, int32_t* topk_idx, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_indexer_topk -- indexer scores followed by the top-k, one call.
+ *
+ * Passage: KimiK3DSAIndexer.score on the vLLM API page
+ * "vllm.models.kimi_k3.nvidia.dsa", which scores the current rows and writes
+ * their top-k into a caller-owned int32 index buffer in one op.  Same operands
+ * and semantics as dsa_indexer_scores followed by dsa_topk; the score matrix is
+ * not an output.  workspace: at least dsa_indexer_topk_workspace_size(...) bytes,
+ * 256-byte aligned; its contents on entry do not matter.
+ */
+size_t dsa_indexer_topk_workspace_size(int64_t n_q, int64_t n_k, int32_t n_heads,
+                                       int32_t head_dim, int32_t dtype,
+                                       int32_t index_topk);
+int dsa_indexer_topk(const void* q, const void* k, const float* k_scale,
+                     const float* w, const int32_t* row_starts,
+                     const int32_t* row_ends, int64_t n_q, int64_t n_k,
+                     int32_t n_heads, int32_t head_dim, int32_t dtype,
+                     int32_t index_topk, int32_t* topk_idx, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_mla_fwd -- MLA attention over the selected latent rows only.
+ *
+ * Passage: the vLLM API page "vllm.models.kimi_k3.nvidia.dsa" (module text and
+ * KimiK3DSAAttention): the MLA layers run with is_sparse=True so that the sparse
+ * attention backend consumes the indexer's top-k indices; in the absorbed MLA
+ * form every head reads the same latent row per key (kv_lora_rank latent dims
+ * followed by the rope dims), and the value is the latent part.
+ *
+ * For query t, head h, with J = the entries of topk_idx[t] that are not -1:
+ *   l_j = sm_scale * q[t, h, :d_qk] . kv[J_j, :d_qk]
+ *   out[t, h, :] = sum_j softmax(l)_j * kv[J_j, :d_v],  lse[t, h] = logsumexp_j l_j
+ * An all -1 row gives out = 0 and lse = -inf.  Duplicates count as listed.
+ *
+ *   q         [n_q, n_heads, d_qk] of dtype (F32 or BF16)
+ *   kv        [n_kv, d_qk] of dtype; V = the first d_v columns of the same rows
+ *   topk_idx  int32 [n_q, index_topk]; entries in [0, n_kv) or -1
+ *   out       [n_q, n_heads, d_v] of dtype;  lse f32 [n_q, n_heads] or NULL
+ *   workspace at least dsa_sparse_mla_workspace_size(...) bytes (may be 0).
+ * Softmax statistics and accumulation are fp32; probabilities enter the
+ * value product in the input type.  Supported: BF16 with d_qk == 576,
+ * d_v == 512, n_heads a multiple of 32; F32 with d_qk <= 256, d_v <= d_qk.
+ */
+size_t dsa_sparse_mla_workspace_size(int64_t n_q, int32_t n_heads, int32_t d_qk,
+                                     int32_t d_v, int32_t index_topk,
+                                     int32_t dtype);
+int dsa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* topk_idx,
+                       int64_t n_q, int64_t n_kv, int32_t n_heads, int32_t d_qk,
+                       int32_t d_v, int32_t index_topk, float sm_scale,
+                       int32_t dtype, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -1,0 +1,40 @@
+// Internal launchers (host side) of the DSA kernels.  Argument validation is
+// done by the C-ABI layer (dsa_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+hipError_t launch_row_windows(const int32_t* cu_q, const int32_t* cu_k, int32_t n_seqs,
+                              int64_t n_rows, int32_t causal, int32_t* row_starts,
+                              int32_t* row_ends, hipStream_t stream);
+
+hipError_t launch_indexer_prep(const float* q_raw, const float* k_raw, const float* w,
+                               const int32_t* pos_q, const int32_t* pos_k, int64_t n_q,
+                               int64_t n_k, int32_t n_heads, int32_t head_dim,
+                               int32_t rope_dim, int32_t rope_main_dim, float theta,
+                               float eps, int32_t dtype, void* q_out, void* k_out,
+                               float* w_out, float* k_scale_out, hipStream_t stream);
+
+hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_starts,
+                       const int32_t* row_ends, int64_t n_q, int32_t K, int32_t* out,
+                       hipStream_t stream);
+
+hipError_t launch_indexer_scores(const void* q, const void* k, const float* k_scale,
+                                 const float* w, const int32_t* row_starts,
+                                 const int32_t* row_ends, int64_t n_q, int64_t n_k,
+                                 int32_t n_heads, int32_t head_dim, int32_t dtype,
+                                 float* scores, int64_t ld, hipStream_t stream);
+
+size_t mla_workspace_bytes(int64_t n_q, int32_t n_heads, int32_t d_qk, int32_t d_v,
+                           int32_t index_topk, int32_t dtype);
+
+hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx,
+                             int64_t n_q, int64_t n_kv, int32_t n_heads, int32_t d_qk,
+                             int32_t d_v, int32_t K, float sm_scale, int32_t dtype,
+                             void* out, float* lse, void* workspace, hipStream_t stream);
+
+}  // namespace dsa

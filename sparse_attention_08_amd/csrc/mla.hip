@@ -1,0 +1,400 @@
+// Sparse MLA attention over the top-k selected latent rows (gfx950).
+//
+// Absorbed MLA: every head of a query reads the same latent row per selected
+// key (512 latent dims followed by 64 rope dims, 1152 bytes in bf16); the value
+// is the latent part.  For each query t and head h:
+//   out[t,h,:] = softmax_j(sm_scale * q[t,h,:] . kv[J_j,:]) @ kv[J, :512]
+// over J = the non -1 entries of topk_idx[t].
+//
+// bf16 kernel: one workgroup = one query x 128 heads (4 waves x 32 heads), or a
+// slice of its selected keys when the key list is split (few queries: decode).
+// Per tile of 32 selected keys:
+//   gather    the 32 latent rows are read with 16-byte loads (a 1152-byte row is
+//             9 x 128-byte lines) into LDS twice: row-major (padded to 1168 bytes,
+//             conflict-free b128 fragment reads) for Q.K, and transposed
+//             (V^T [512 x 32], padded rows) for P.V;
+//   S^T=K.Q^T v_mfma_f32_32x32x16_bf16 with keys on M and the wave's 32 heads on
+//             N: lane l holds 16 keys of head l%32, so the softmax max/sum over
+//             keys is in-lane plus one exchange with lane l^32.  Q^T stays in
+//             registers for the whole query (36 K-steps of 16 dims);
+//   softmax   fp32, natural-exp; the running max is only moved (and the output
+//             rescaled) when a tile's max exceeds it by more than 8, so the
+//             probabilities stay <= e^8 and the rescale is rare;
+//   O += P.V  the S^T accumulator, rounded to bf16, IS the A operand of the next
+//             MFMA (heads on M, keys on K): the keys of a lane half are taken in
+//             the order the accumulator holds them, and V^T is stored with that
+//             key permutation, so no shuffle of P is needed.  O [32 heads x 512]
+//             stays in 256 accumulator registers per lane.
+// The row sum uses the bf16-rounded probabilities, so the output is an exact
+// convex combination of value rows up to fp32 accumulation.
+//
+// Split mode writes per-split (normalised output, lse) in fp32 to the workspace;
+// a combine kernel merges them with the log-sum-exp weights.
+// The fp32 kernel (small head dims) is plain VALU code.
+#include <cmath>
+
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kKT = 32;                         // selected keys per tile
+constexpr int kRowBytes = kDqk * 2;             // 1152
+constexpr int kKvStride = kRowBytes + 16;       // 1168: padded LDS row
+constexpr int kVtStride = kKT * 2 + 16;         // 80 bytes per V^T row
+constexpr int kQSteps = kDqk / 16 / 2;          // 18 K-steps per wave (half of d_qk)
+constexpr int kVTiles = kDv / 32 / 2;           // 8 value tiles per wave (half of d_v)
+constexpr int kThreads = 512;                   // 8 waves: 4 head groups x 2 halves
+constexpr int kHeadsPerBlock = 128;
+constexpr int kChunksPerRow = kRowBytes / 16;   // 72
+constexpr int kChunks = kKT * kChunksPerRow;    // 2304
+constexpr float kRescaleSlack = 8.0f;
+
+// Row (head offset inside the wave's 32) that accumulator register r of a
+// 32x32 MFMA output holds in lane half `half`.
+__device__ __forceinline__ int acc_row(int r, int half) {
+  return 8 * (r >> 2) + 4 * half + (r & 3);
+}
+
+// Position of key j (0..31) inside a V^T row: each 16-key K-step is stored so
+// that lane half g reads keys {4g..4g+3, 8+4g..8+4g+3} as 8 consecutive entries.
+__device__ __forceinline__ int vt_pos(int j) {
+  return (j & 16) | (((j >> 2) & 1) << 3) | (((j >> 3) & 1) << 2) | (j & 3);
+}
+
+// One workgroup: one query, 128 heads.  Wave w: head group g = w & 3 (32 heads),
+// half h = w >> 2.  Half h computes the partial S^T over dims [288h, 288h+288),
+// the two partials are added through LDS (both waves then hold the same S and run
+// the same softmax), and half h accumulates output columns [256h, 256h+256).
+// Everything lives in VGPRs (Q^T half: 72, O half: 128 per lane).
+__global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
+    const int32_t* __restrict__ idx, int H, int K, float sm_scale,
+    __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_lse, int nsplit) {
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[kKT * kKvStride];
+  __shared__ __attribute__((aligned(16))) uint8_t vts[kDv * kVtStride];
+  __shared__ float sx[kThreads / kWave][16][kWave];
+  __shared__ int sidx[kKT];
+
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int half = lane >> 5;
+  const int grp = wave & 3;
+  const int hs = wave >> 2;  // which half of d_qk (Q.K) and of d_v (P.V)
+  const int h0 = int(blockIdx.y) * kHeadsPerBlock + grp * 32;
+  const int head = h0 + (lane & 31);
+  const bool hvalid = head < H;
+
+  // Q^T fragments: lane holds q[t, head, 288*hs + 16*st + 8*half .. +8]
+  bf16x8_t qf[kQSteps];
+  {
+    const __bf16* qr =
+        q + (t * H + (hvalid ? head : 0)) * int64_t(kDqk) + (kDqk / 2) * hs + 8 * half;
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qr + 16 * st);
+      qf[st] = hvalid ? v : bf16x8_t{};
+    }
+  }
+
+  f32x16_t o[kVTiles];
+#pragma unroll
+  for (int n = 0; n < kVTiles; ++n) o[n] = f32x16_t{};
+  float m_run = -INFINITY;  // per head (lane column), same in both lane halves
+  float l_run = 0.0f;       // per head, partial over this lane half's keys
+
+  const int ntiles = (K + kKT - 1) / kKT;
+  const int i0 = int(int64_t(ntiles) * blockIdx.z / nsplit);
+  int i1 = int(int64_t(ntiles) * (blockIdx.z + 1) / nsplit);
+  const int32_t* irow = idx + t * K;
+
+  // Trailing tiles that hold only -1 padding are not visited (the top-k rows
+  // are -1 padded at the end).  Padding elsewhere is masked per key.
+  {
+    int last = -1;
+    const int j1 = min(K, i1 * kKT);
+    for (int j = i0 * kKT + tid; j < j1; j += kThreads)
+      if (irow[j] >= 0) last = j;
+    if (tid == 0) sidx[0] = -1;
+    __syncthreads();
+    if (last >= 0) atomicMax(&sidx[0], last);
+    __syncthreads();
+    last = sidx[0];
+    i1 = last < 0 ? i0 : last / kKT + 1;
+    __syncthreads();
+  }
+
+  for (int i = i0; i < i1; ++i) {
+    if (tid < kKT) {
+      const int j = i * kKT + tid;
+      sidx[tid] = j < K ? irow[j] : -1;
+    }
+    __syncthreads();
+    const uint32_t vmask = uint32_t(__ballot(sidx[lane & 31] >= 0));
+    // gather: thread = (key pair kp, chunk group cg) copies chunks cg, cg+32,
+    // cg+64 of keys 2kp and 2kp+1 row-major, and writes their value parts into
+    // V^T as dwords holding the two keys' entries (adjacent V^T positions).
+    {
+      const int kp = tid & 15;
+      const int cg = tid >> 4;
+      const int r0 = sidx[2 * kp], r1 = sidx[2 * kp + 1];
+      const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
+      const uint8_t* g0 = kvb + int64_t(r0 < 0 ? 0 : r0) * kRowBytes;
+      const uint8_t* g1 = kvb + int64_t(r1 < 0 ? 0 : r1) * kRowBytes;
+      uint8_t* d0 = kvs + (2 * kp) * kKvStride;
+      uint8_t* dvt = vts + vt_pos(2 * kp) * 2;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const int cc = cg + 32 * c;
+        if (cc < kChunksPerRow) {
+          i32x4_t a = {}, b = {};
+          if (r0 >= 0) a = *reinterpret_cast<const i32x4_t*>(g0 + cc * 16);
+          if (r1 >= 0) b = *reinterpret_cast<const i32x4_t*>(g1 + cc * 16);
+          *reinterpret_cast<i32x4_t*>(d0 + cc * 16) = a;
+          *reinterpret_cast<i32x4_t*>(d0 + kKvStride + cc * 16) = b;
+          if (cc < kDv / 8) {
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+              const uint32_t lo = (uint32_t(a[x >> 1]) >> (16 * (x & 1))) & 0xFFFFu;
+              const uint32_t hi = (uint32_t(b[x >> 1]) >> (16 * (x & 1))) & 0xFFFFu;
+              *reinterpret_cast<uint32_t*>(dvt + (cc * 8 + x) * kVtStride) = lo | (hi << 16);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // partial S^T = K . Q^T over this wave's half of d_qk (keys on M, heads on N)
+    f32x16_t s = f32x16_t{};
+    const uint8_t* ka = kvs + (lane & 31) * kKvStride + hs * kDqk + half * 16;
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8_t*>(ka + st * 32), qf[st], s, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sx[wave][r][lane] = s[r];
+    __syncthreads();
+    float mt = -INFINITY;
+    const uint32_t mv = vmask >> (4 * half);  // bit 8*(r/4) + r%4 = key of register r
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float other = sx[wave ^ 4][r][lane];
+      const float full = hs == 0 ? s[r] + other : other + s[r];  // same bits in both halves
+      s[r] = ((mv >> (8 * (r >> 2) + (r & 3))) & 1u) ? full * sm_scale : -INFINITY;
+      mt = fmaxf(mt, s[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool grow = mt > m_run + kRescaleSlack;
+    if (__ballot(grow) != 0ull) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = grow ? (m_run == -INFINITY ? 0.0f : __expf(m_run - m_new)) : 1.0f;
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ar = __shfl(alpha, acc_row(r, half));
+#pragma unroll
+        for (int n = 0; n < kVTiles; ++n) o[n][r] *= ar;
+      }
+    }
+    bf16x8_t p0, p1;
+    float ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = s[r] == -INFINITY ? 0.0f : __expf(s[r] - m_run);
+      const uint16_t pb = f32_to_bf16_bits(p);
+      ps += bf16_bits_to_f32(pb);
+      const __bf16 pv = __builtin_bit_cast(__bf16, pb);
+      if (r < 8) p0[r] = pv;
+      else p1[r - 8] = pv;
+    }
+    l_run += ps;
+
+    // O[:, 256*hs .. +256] += P . V
+    const uint8_t* vb = vts + (hs * kVTiles * 32 + (lane & 31)) * kVtStride + half * 16;
+#pragma unroll
+    for (int n = 0; n < kVTiles; ++n) {
+      const bf16x8_t v0 = *reinterpret_cast<const bf16x8_t*>(vb + n * 32 * kVtStride);
+      const bf16x8_t v1 = *reinterpret_cast<const bf16x8_t*>(vb + n * 32 * kVtStride + 32);
+      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, v0, o[n], 0, 0, 0);
+      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, v1, o[n], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_h = l_tot > 0.0f ? m_run + __logf(l_tot) : -INFINITY;
+  const int col0 = hs * kVTiles * 32 + (lane & 31);
+  if (nsplit == 1) {
+    if (lse && half == 0 && hs == 0 && hvalid) lse[t * H + head] = lse_h;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hr = h0 + acc_row(r, half);
+      const float ir = __shfl(inv, acc_row(r, half));
+      if (hr < H) {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(out) + (t * H + hr) * int64_t(kDv) + col0;
+#pragma unroll
+        for (int n = 0; n < kVTiles; ++n) orow[n * 32] = f32_to_bf16_bits(o[n][r] * ir);
+      }
+    }
+  } else {
+    const int64_t slot = t * nsplit + blockIdx.z;
+    if (half == 0 && hs == 0 && hvalid) part_lse[slot * H + head] = lse_h;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hr = h0 + acc_row(r, half);
+      const float ir = __shfl(inv, acc_row(r, half));
+      if (hr < H) {
+        float* orow = part_o + (slot * H + hr) * int64_t(kDv) + col0;
+#pragma unroll
+        for (int n = 0; n < kVTiles; ++n) orow[n * 32] = o[n][r] * ir;
+      }
+    }
+  }
+}
+
+// Merge split partials: out = sum_s e^{lse_s - L} o_s with L = logsumexp_s lse_s.
+__global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse,
+                                                          int H, int nsplit,
+                                                          __bf16* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y;
+  float mx = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_lse[(t * nsplit + s) * H + h]);
+  float wsum = 0.0f;
+  float acc[kDv / 128] = {};
+  for (int s = 0; s < nsplit; ++s) {
+    const float ls = part_lse[(t * nsplit + s) * H + h];
+    const float ws = ls == -INFINITY ? 0.0f : __expf(ls - mx);
+    wsum += ws;
+    const float* po = part_o + ((t * nsplit + s) * H + h) * int64_t(kDv);
+#pragma unroll
+    for (int x = 0; x < kDv / 128; ++x) acc[x] = fmaf(ws, po[threadIdx.x + 128 * x], acc[x]);
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(out) + (t * H + h) * int64_t(kDv);
+#pragma unroll
+  for (int x = 0; x < kDv / 128; ++x) orow[threadIdx.x + 128 * x] = f32_to_bf16_bits(acc[x] * inv);
+  if (lse && threadIdx.x == 0) lse[t * H + h] = wsum > 0.0f ? mx + __logf(wsum) : -INFINITY;
+}
+
+// fp32 inputs: one workgroup per (query, head).
+__global__ __launch_bounds__(128) void mla_f32_kernel(const float* __restrict__ q,
+                                                      const float* __restrict__ kv,
+                                                      const int32_t* __restrict__ idx, int H,
+                                                      int K, int dqk, int dv, float sm_scale,
+                                                      float* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  extern __shared__ float sm[];  // q row [dqk], logits [K], reduction [4]
+  float* sq = sm;
+  float* sl = sm + dqk;
+  float* red = sl + K;
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* qr = q + (t * H + h) * int64_t(dqk);
+  for (int d = tid; d < dqk; d += 128) sq[d] = qr[d];
+  __syncthreads();
+  const int32_t* irow = idx + t * K;
+  float mx = -INFINITY;
+  for (int j = tid; j < K; j += 128) {
+    const int r = irow[j];
+    float l = -INFINITY;
+    if (r >= 0) {
+      const float* kr = kv + int64_t(r) * dqk;
+      float dot = 0.0f;
+      for (int d = 0; d < dqk; ++d) dot = fmaf(sq[d], kr[d], dot);
+      l = dot * sm_scale;
+    }
+    sl[j] = l;
+    mx = fmaxf(mx, l);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float den = 0.0f;
+  for (int j = tid; j < K; j += 128) {
+    const float p = sl[j] == -INFINITY ? 0.0f : __expf(sl[j] - mx);
+    sl[j] = p;
+    den += p;
+  }
+  den = wave_sum(den);
+  if ((tid & 63) == 0) red[2 + (tid >> 6)] = den;
+  __syncthreads();
+  den = red[2] + red[3];
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  for (int d = tid; d < dv; d += 128) {
+    float acc = 0.0f;
+    for (int j = 0; j < K; ++j) {
+      const int r = irow[j];
+      if (r >= 0) acc = fmaf(sl[j], kv[int64_t(r) * dqk + d], acc);
+    }
+    out[(t * H + h) * int64_t(dv) + d] = acc * inv;
+  }
+  if (lse && tid == 0) lse[t * H + h] = den > 0.0f ? mx + __logf(den) : -INFINITY;
+}
+
+// Number of key splits per query for the bf16 kernel (shared by the launcher
+// and the workspace query).
+int mla_splits(int64_t n_q, int32_t n_heads, int32_t K) {
+  const int64_t blocks = n_q * ((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  const int ntiles = (K + kKT - 1) / kKT;
+  if (blocks >= 192) return 1;
+  int s = int((256 + blocks - 1) / blocks);
+  if (s > ntiles) s = ntiles;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+size_t mla_workspace_bytes(int64_t n_q, int32_t n_heads, int32_t d_qk, int32_t d_v,
+                           int32_t K, int32_t dtype) {
+  (void)d_qk;
+  if (dtype != 1) return 0;
+  const int s = mla_splits(n_q, n_heads, K);
+  if (s == 1) return 0;
+  return size_t(n_q) * s * n_heads * (size_t(d_v) + 1) * sizeof(float);
+}
+
+hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, int64_t n_q,
+                             int64_t n_kv, int32_t n_heads, int32_t d_qk, int32_t d_v,
+                             int32_t K, float sm_scale, int32_t dtype, void* out, float* lse,
+                             void* workspace, hipStream_t stream) {
+  (void)n_kv;
+  if (n_q == 0) return hipSuccess;
+  if (dtype == 0) {
+    const size_t smem = (size_t(d_qk) + K + 4) * sizeof(float);
+    hipLaunchKernelGGL(mla_f32_kernel, dim3(unsigned(n_q), n_heads), dim3(128), smem, stream,
+                       static_cast<const float*>(q), static_cast<const float*>(kv), idx,
+                       n_heads, K, d_qk, d_v, sm_scale, static_cast<float*>(out), lse);
+    return hipGetLastError();
+  }
+  const int s = mla_splits(n_q, n_heads, K);
+  const unsigned hb = unsigned((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = s > 1 ? part_o + size_t(n_q) * s * n_heads * d_v : nullptr;
+  hipLaunchKernelGGL(mla_bf16_kernel, dim3(unsigned(n_q), hb, s), dim3(kThreads), 0, stream,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(kv), idx, n_heads,
+                     K, sm_scale, static_cast<__bf16*>(out), lse, part_o, part_lse, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || s == 1) return e;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(unsigned(n_q), n_heads), dim3(128), 0, stream,
+                     part_o, part_lse, n_heads, s, static_cast<__bf16*>(out), lse);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

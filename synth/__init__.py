@@ -224,3 +224,45 @@ def sample_rows(n_rows: int, index_topk: int, seed: int, n_random: int = 256,
     g = np.random.default_rng([SEED_ROOT, 99, seed])
     picks.update(int(x) for x in g.integers(0, n_rows, size=min(n_random, n_rows)))
     return np.array(sorted(picks), np.int64)
+
+
+# ----------------------------------------------------------------------------
+# device-side draws for large tensors (torch's counter-based Philox generator,
+# seeded per config and tensor).  Both sides read the same device tensor: the
+# kernels directly, the oracle through a host copy of the rows it checks.
+# ----------------------------------------------------------------------------
+def _torch_seed(config_id: int, tensor_id: int, salt: int = 0) -> int:
+    return (SEED_ROOT << 32) ^ (config_id << 20) ^ (tensor_id << 8) ^ salt
+
+
+def device_normal(w: Workload, tensor_id: int, shape, device, scale: float = 1.0, salt: int = 0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(w.config_id, tensor_id, salt))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(scale)
+    return x
+
+
+def device_uniform(w: Workload, tensor_id: int, shape, device, salt: int = 0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(w.config_id, tensor_id, salt))
+    return torch.rand(tuple(shape), generator=g, device=device, dtype=torch.float32)
+
+
+def device_inputs(w: Workload, device, lay: Layout | None = None, mla: bool = True,
+                  signed_weights: bool = False):
+    """Raw fp32 device tensors of a workload: index q [Nq,H,D], index k [Nk,D],
+    weights [Nq,H], MLA q [Nq,Hm,d_qk] and latent kv [Nk,d_qk] (when ``mla``)."""
+    lay = layout(w) if lay is None else lay
+    out = dict(layout=lay)
+    out["q_raw"] = device_normal(w, T_IDX_Q, (lay.n_q, w.n_heads, w.head_dim), device)
+    out["k_raw"] = device_normal(w, T_IDX_K, (lay.n_k, w.head_dim), device)
+    out["w"] = (device_normal(w, T_SIGN, (lay.n_q, w.n_heads), device) if signed_weights
+                else device_uniform(w, T_IDX_W, (lay.n_q, w.n_heads), device))
+    if mla:
+        out["mla_q"] = device_normal(w, T_MLA_Q, (lay.n_q, w.mla_heads, w.d_qk), device, w.mla_scale)
+        out["mla_kv"] = device_normal(w, T_MLA_KV, (lay.n_k, w.d_qk), device, w.mla_scale)
+    return out

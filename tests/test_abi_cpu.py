@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/dsa.h declares, and rejects invalid arguments before
+anything is enqueued (those calls return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+LIB = os.path.join(ROOT, "sparse_attention_08_amd", "libdsa.so")
+
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdsa.so is not built (run __graft_entry__.build())")
+    import torch  # noqa: F401  load torch's HIP runtime first, as the binding does
+    import sparse_attention_08_amd as b
+    return b.load(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_sparse_mla_fwd",
+              "dsa_row_windows"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    import sparse_attention_08_amd as b
+    assert sorted(b.EXPORTS) == declared_functions()
+
+
+def test_status_strings_and_version(lib):
+    assert lib.dsa_version() >= 100
+    assert lib.dsa_status_string(0) == b"ok"
+    for s in (INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert lib.dsa_status_string(s) not in (b"ok", b"unknown status")
+
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+FAKE32 = ctypes.c_void_p(0x2000)
+
+
+def test_topk_rejects_bad_arguments(lib):
+    # index_topk < 1
+    assert lib.dsa_topk(FAKE, 16, FAKE, FAKE, 4, 16, 0, FAKE, None, 0, None) == INVALID
+    # ld < n_cols
+    assert lib.dsa_topk(FAKE, 8, FAKE, FAKE, 4, 16, 4, FAKE, None, 0, None) == INVALID
+    # null scores
+    assert lib.dsa_topk(None, 16, FAKE, FAKE, 4, 16, 4, FAKE, None, 0, None) == INVALID
+    # negative sizes
+    assert lib.dsa_topk(FAKE, 16, FAKE, FAKE, -1, 16, 4, FAKE, None, 0, None) == INVALID
+    # empty problem is fine and enqueues nothing
+    assert lib.dsa_topk(None, 16, None, None, 0, 16, 4, None, None, 0, None) == 0
+
+
+def test_indexer_rejects_bad_arguments(lib):
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("q", FAKE32), ("k", FAKE32), ("ks", None), ("w", FAKE), ("rs", FAKE), ("re", FAKE),
+        ("nq", 4), ("nk", 8), ("h", 64), ("d", 128), ("dt", 1), ("sc", FAKE), ("ld", 8), ("st", None))]
+    assert lib.dsa_indexer_scores(*args(h=65)) == UNSUPPORTED
+    assert lib.dsa_indexer_scores(*args(d=64)) == UNSUPPORTED
+    assert lib.dsa_indexer_scores(*args(ld=7)) == INVALID
+    assert lib.dsa_indexer_scores(*args(dt=2)) == INVALID            # fp8 needs k_scale
+    assert lib.dsa_indexer_scores(*args(ks=FAKE)) == INVALID         # bf16 must not get k_scale
+    assert lib.dsa_indexer_scores(*args(dt=7)) == INVALID
+    assert lib.dsa_indexer_scores(*args(q=ctypes.c_void_p(0x1008))) == UNSUPPORTED  # misaligned
+    assert lib.dsa_indexer_scores(*args(w=None)) == INVALID
+    assert lib.dsa_indexer_scores(*args(dt=0, d=300)) == UNSUPPORTED
+
+
+def test_indexer_topk_workspace_is_checked(lib):
+    need = lib.dsa_indexer_topk_workspace_size(4, 8, 64, 128, 1, 4)
+    assert need > 0
+    st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, 4, 8, 64, 128, 1, 4, FAKE,
+                              None, 0, None)
+    assert st == WORKSPACE
+    st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, 4, 8, 64, 128, 1, 4, FAKE,
+                              FAKE32, need - 1, None)
+    assert st == WORKSPACE
+
+
+def test_mla_rejects_bad_arguments(lib):
+    base = dict(q=FAKE32, kv=FAKE32, idx=FAKE, nq=4, nkv=16, h=128, dqk=576, dv=512, k=2048,
+                sm=0.04, dt=1, out=FAKE32, lse=None, ws=None, wsb=0, st=None)
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.dsa_sparse_mla_fwd(*a.values())
+    assert call(dqk=512) == UNSUPPORTED
+    assert call(h=100) == UNSUPPORTED
+    assert call(dv=600) == INVALID
+    assert call(dt=2) == UNSUPPORTED
+    assert call(k=0) == INVALID
+    assert call(out=None) == INVALID
+    # decode-sized call needs split workspace
+    need = lib.dsa_sparse_mla_workspace_size(4, 128, 576, 512, 2048, 1)
+    assert need > 0
+    assert call() == WORKSPACE
+
+
+def test_windows_and_prep_reject_bad_arguments(lib):
+    assert lib.dsa_row_windows(FAKE, FAKE, 0, 4, 1, FAKE, FAKE, None) == INVALID
+    assert lib.dsa_row_windows(FAKE, FAKE, 1, 4, 2, FAKE, FAKE, None) == INVALID
+    assert lib.dsa_row_windows(None, FAKE, 1, 4, 1, FAKE, FAKE, None) == INVALID
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 2, 128, 63, 64, 1e4, 1e-6, 1, FAKE, FAKE, FAKE, None, None]
+    assert lib.dsa_indexer_prep(*a) == INVALID                      # odd rope_dim
+    a[9] = 64; a[13] = 2
+    assert lib.dsa_indexer_prep(*a) == INVALID                      # fp8 needs k_scale_out

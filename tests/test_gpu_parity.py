@@ -1,0 +1,311 @@
+"""GPU parity of every entry point against the CPU oracle, on small and medium
+seeded inputs that span several tiles and ragged tails, plus the edge cases
+(empty and one-key windows, windows shorter than index_topk, ties, -inf,
+garbage outside windows, rows longer than the LDS-resident limit).
+
+All calls go through the C ABI (ctypes binding).  Oracle inputs come from
+``synth`` and ``oracle.prep`` only; the HIP path gets the same canonical values."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import indexer as o_idx
+from oracle import mla as o_mla
+from oracle import prep as o_prep
+from oracle import topk as o_topk
+from oracle import windows as o_win
+from parity import check_mla, check_scores, check_topk_e2e, dev, host, i32, say
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.WORKLOADS["tiny"]
+P4K = synth.WORKLOADS["prefill4k"]
+
+
+# ---------------------------------------------------------------------------
+# input builders (oracle side)
+# ---------------------------------------------------------------------------
+def canonical_indexer(w, lay, dtype, signed=False, H=None, rope=True):
+    H = w.n_heads if H is None else H
+    q_raw = synth.index_q_raw(w, 0, lay.n_q)[:, :H]
+    k_raw = synth.index_k_raw(w, 0, lay.n_k)
+    wt = synth.index_weights(w, 0, lay.n_q, signed=signed)[:, :H]
+    rd = w.rope_dim if rope else 0
+    p = o_prep.prepare_indexer_inputs(q_raw, k_raw, wt, lay.positions(), lay.key_positions(),
+                                      dtype, rd, w.rope_main_dim, w.rope_theta)
+    rs, re = o_win.row_windows(lay.cu_q, lay.cu_k, causal=True)
+    return p, rs, re
+
+
+def to_device_indexer(p, dtype):
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dtype]
+    q, k = dev(p["q"], tdt), dev(p["k"], tdt)
+    w = dev(p["w"])
+    ks = None if p["k_scale"] is None else dev(p["k_scale"])
+    return q, k, w, ks
+
+
+def oracle_scores_f32(p, rs, re):
+    S, C = o_idx.scores_dense(p["q"], p["k"], p["w"], rs, re, p["k_scale"], with_cond=True,
+                              fill=np.nan)
+    return S, C
+
+
+# ---------------------------------------------------------------------------
+# windows
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("lens,decode", [([256], False), ([5, 1, 300, 77, 1024], False),
+                                         ([17000, 3, 40000], True), ([0, 4, 0, 9], False)])
+def test_row_windows(dsa, lens, decode):
+    say(f"row_windows lens={lens} decode={decode}")
+    lay = synth.layout_from_lengths(lens, decode)
+    for causal in (True, False):
+        rs, re = dsa.dsa_row_windows(i32(lay.cu_q), i32(lay.cu_k), lay.n_q, causal)
+        ors, ore = o_win.row_windows(lay.cu_q, lay.cu_k, causal)
+        np.testing.assert_array_equal(host(rs), ors)
+        np.testing.assert_array_equal(host(re), ore)
+
+
+# ---------------------------------------------------------------------------
+# top-k (bit-exact on identical fp32 scores)
+# ---------------------------------------------------------------------------
+def _topk_case(dsa, S, rs, re, K, what):
+    say(f"topk {what}: rows={S.shape[0]} cols={S.shape[1]} K={K}")
+    g = host(dsa.dsa_topk(dev(S), i32(rs), i32(re), K))
+    o = o_topk.topk(S, rs, re, K)
+    bad = np.nonzero((g != o).any(axis=1))[0]
+    assert bad.size == 0, f"{what}: rows differ, first {bad[:5]}: gpu {g[bad[0]][:12]} oracle {o[bad[0]][:12]}"
+
+
+def test_topk_tiny_oracle_scores(dsa):
+    lay = synth.layout(TINY)
+    p, rs, re = canonical_indexer(TINY, lay, "f32")
+    S, _ = oracle_scores_f32(p, rs, re)
+    S32 = np.where(np.isnan(S), np.float32(-1e4), S).astype(np.float32)
+    _topk_case(dsa, S32, rs, re, TINY.index_topk, "tiny")
+
+
+def test_topk_ties_and_specials(dsa):
+    g = np.random.default_rng(101)
+    pool = np.array([-np.inf, -3.0, -0.0, 0.0, 1.0, 2.5, np.inf], np.float32)
+    n_q, n = 300, 700
+    S = pool[g.integers(0, len(pool), (n_q, n))]
+    rs = g.integers(0, n, n_q).astype(np.int32)
+    re = np.minimum(n, rs + g.integers(0, 500, n_q)).astype(np.int32)
+    rs[:3] = [0, 5, 9]; re[:3] = [0, 5, 10]                 # empty, empty, one key
+    for K in (1, 7, 64, 333):
+        _topk_case(dsa, S, rs, re, K, f"ties K={K}")
+
+
+def test_topk_garbage_outside_windows(dsa):
+    g = np.random.default_rng(102)
+    lay = synth.layout_from_lengths([700, 1500, 3000, 90, 2100])
+    rs, re = o_win.row_windows(lay.cu_q, lay.cu_k)
+    S = np.where(g.random((lay.n_q, lay.n_k)) < 0.5, 1e4, -1e4).astype(np.float32)
+    for t in range(lay.n_q):
+        S[t, rs[t]:re[t]] = g.standard_normal(re[t] - rs[t]).astype(np.float32)
+    _topk_case(dsa, S, rs, re, 1024, "thd garbage")
+
+
+def test_topk_long_rows_global_path(dsa):
+    # windows longer than the LDS-resident limit (8192) use the global passes
+    g = np.random.default_rng(103)
+    n_q, n = 24, 70000
+    S = g.standard_normal((n_q, n)).astype(np.float32)
+    S[::3] = np.round(S[::3] * 4) / 4                       # heavy ties on some rows
+    rs = np.zeros(n_q, np.int32)
+    re = np.array([n, 8192, 8193, 9000, 30000, 65536] * 4, np.int32)
+    _topk_case(dsa, S, rs, re, 2048, "long rows")
+
+
+def test_topk_prefill4k_oracle_scores(dsa):
+    # full prefill4k score matrix from the oracle (fp64 -> fp32), causal windows
+    lay = synth.layout(P4K)
+    p, rs, re = canonical_indexer(P4K, lay, "bf16")
+    say("oracle scores prefill4k ...")
+    S = np.full((lay.n_q, lay.n_k), -1e4, np.float32)
+    for t in range(lay.n_q):
+        S[t, :re[t]] = o_idx.score_row(p["q"][t], p["k"][:re[t]], p["w"][t])
+    _topk_case(dsa, S, rs, re, P4K.index_topk, "prefill4k")
+
+
+# ---------------------------------------------------------------------------
+# indexer scores
+# ---------------------------------------------------------------------------
+def _indexer_case(dsa, w, lay, dtype, what, signed=False, H=None, rope=True, rows=None):
+    p, rs, re = canonical_indexer(w, lay, dtype, signed, H, rope)
+    q, k, wt, ks = to_device_indexer(p, dtype)
+    say(f"indexer {what}: n_q={lay.n_q} n_k={lay.n_k} H={q.shape[1]} dtype={dtype}")
+    G = host(dsa.dsa_indexer_scores(q, k, wt, i32(rs), i32(re), k_scale=ks))
+    rtol = 1e-3 if dtype == "f32" else 2e-2
+    rows = range(lay.n_q) if rows is None else rows
+    worst = 0.0
+    for t in rows:
+        a, b = rs[t], re[t]
+        ksw = None if p["k_scale"] is None else p["k_scale"][a:b]
+        o, c = o_idx.score_row(p["q"][t], p["k"][a:b], p["w"][t], ksw, with_cond=True)
+        worst = max(worst, check_scores(G[t, a:b], o, c, rtol, f"{what} row {t}"))
+        assert np.isnan(G[t, :a]).all() and np.isnan(G[t, b:]).all(), f"{what}: wrote outside window"
+    say(f"  max rel err {worst:.2e}")
+
+
+def test_indexer_tiny_f32(dsa):
+    _indexer_case(dsa, TINY, synth.layout(TINY), "f32", "tiny")
+
+
+def test_indexer_bf16_prefill_small(dsa):
+    _indexer_case(dsa, P4K, synth.layout_from_lengths([777]), "bf16", "bf16 T=777")
+
+
+def test_indexer_bf16_thd_signed_weights(dsa):
+    lay = synth.layout_from_lengths([33, 400, 1, 290])
+    _indexer_case(dsa, P4K, lay, "bf16", "bf16 thd signed", signed=True)
+
+
+def test_indexer_bf16_fewer_heads(dsa):
+    _indexer_case(dsa, P4K, synth.layout_from_lengths([300, 45]), "bf16", "bf16 H=20", H=20)
+    _indexer_case(dsa, P4K, synth.layout_from_lengths([300]), "bf16", "bf16 H=40", H=40)
+
+
+def test_indexer_bf16_decode_rows(dsa):
+    lay = synth.layout_from_lengths([5000, 33, 12000, 20001], decode=True)
+    _indexer_case(dsa, P4K, lay, "bf16", "bf16 decode", rope=False)
+
+
+def test_indexer_fp8_small(dsa):
+    w = synth.WORKLOADS["fp8_64k"]
+    _indexer_case(dsa, w, synth.layout_from_lengths([600]), "fp8", "fp8 T=600", rope=False)
+    _indexer_case(dsa, w, synth.layout_from_lengths([3000], decode=True), "fp8", "fp8 decode",
+                  rope=False)
+
+
+# ---------------------------------------------------------------------------
+# fused indexer + top-k (end to end against oracle scores + oracle top-k)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("lens,K", [([1200], 256), ([300, 900, 64], 128)])
+def test_indexer_topk_end_to_end(dsa, lens, K):
+    lay = synth.layout_from_lengths(lens)
+    p, rs, re = canonical_indexer(P4K, lay, "bf16")
+    q, k, wt, _ = to_device_indexer(p, "bf16")
+    say(f"indexer_topk lens={lens} K={K}")
+    G = host(dsa.dsa_indexer_topk(q, k, wt, i32(rs), i32(re), K))
+    ndiff = 0
+    for t in range(lay.n_q):
+        a, b = rs[t], re[t]
+        o, c = o_idx.score_row(p["q"][t], p["k"][a:b], p["w"][t], with_cond=True)
+        full = np.full(lay.n_k, -np.inf); full[a:b] = o
+        tau = np.zeros(lay.n_k); tau[a:b] = 2e-2 * np.maximum(np.abs(o), c / 128)
+        oi = o_topk.topk_row(full.astype(np.float32), a, b, K)
+        ndiff += check_topk_e2e(G[t], oi, full, tau, f"row {t}")
+    say(f"  columns differing within tolerance: {ndiff}")
+
+
+# ---------------------------------------------------------------------------
+# sparse MLA
+# ---------------------------------------------------------------------------
+def _random_topk_rows(g, n_q, n_kv, K, windows=None, holes=False):
+    """Index rows shaped like top-k output: ascending columns, then -1 padding."""
+    out = np.full((n_q, K), -1, np.int32)
+    for t in range(n_q):
+        a, b = (0, n_kv) if windows is None else windows[t]
+        n = min(K, b - a)
+        n = int(g.integers(max(0, n // 2), n + 1)) if g.random() < 0.3 else n
+        sel = np.sort(g.choice(np.arange(a, b), size=n, replace=False)) if n else np.zeros(0)
+        out[t, :n] = sel
+        if holes and n > 4:
+            out[t, g.integers(0, n, 3)] = -1           # -1 inside the list too
+    return out
+
+
+def _mla_case(dsa, q, kv, idx, sm, d_v, bf16, what, rows=None):
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    qd, kvd = dev(q, tdt), dev(kv, tdt)
+    say(f"mla {what}: n_q={q.shape[0]} H={q.shape[1]} n_kv={kv.shape[0]} K={idx.shape[1]}")
+    out, lse = dsa.dsa_sparse_mla_fwd(qd, kvd, i32(idx), sm, d_v)
+    rows = range(q.shape[0]) if rows is None else list(rows)
+    oo, ol = o_mla.sparse_mla(q, kv, idx, sm, d_v, rows=rows)
+    err = check_mla(host(out)[rows], oo, host(lse)[rows], ol, bf16, what)
+    say(f"  max abs err {err:.2e}")
+
+
+def test_mla_tiny_f32(dsa):
+    lay = synth.layout(TINY)
+    p, rs, re = canonical_indexer(TINY, lay, "f32")
+    S, _ = oracle_scores_f32(p, rs, re)
+    idx = o_topk.topk(np.where(np.isnan(S), -np.inf, S).astype(np.float32), rs, re, TINY.index_topk)
+    q = o_prep.round_f32(synth.mla_q(TINY, 0, lay.n_q))
+    kv = o_prep.round_f32(synth.mla_kv(TINY, 0, lay.n_k))
+    _mla_case(dsa, q, kv, idx, TINY.sm_scale, TINY.d_v, False, "tiny f32")
+
+
+def test_mla_bf16_prefill_medium(dsa):
+    g = np.random.default_rng(201)
+    n_q, n_kv = 96, 3000
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q))
+    kv = o_prep.round_bf16(synth.mla_kv(P4K, 0, n_kv))
+    idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk, holes=True)
+    idx[0] = -1                                            # empty row
+    idx[1, 1:] = -1                                        # one key
+    _mla_case(dsa, q, kv, idx, P4K.sm_scale, P4K.d_v, True, "bf16 prefill")
+
+
+def test_mla_bf16_peaky_and_split(dsa):
+    g = np.random.default_rng(202)
+    n_q, n_kv = 6, 5000                                    # few queries: split-K path
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q) * 800.0)  # large logits: rescale path
+    kv = o_prep.round_bf16(synth.mla_kv(P4K, 0, n_kv))
+    idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk, holes=True)
+    _mla_case(dsa, q, kv, idx, P4K.sm_scale, P4K.d_v, True, "bf16 split peaky")
+
+
+def test_mla_bf16_fewer_heads(dsa):
+    g = np.random.default_rng(203)
+    n_q, n_kv = 40, 700
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q)[:, :96])
+    kv = o_prep.round_bf16(synth.mla_kv(P4K, 0, n_kv))
+    idx = _random_topk_rows(g, n_q, n_kv, 512)
+    _mla_case(dsa, q, kv, idx, P4K.sm_scale, P4K.d_v, True, "bf16 H=96")
+
+
+# ---------------------------------------------------------------------------
+# input preparation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_indexer_prep(dsa, dtype):
+    lay = synth.layout_from_lengths([300, 1000, 5000])
+    w = P4K
+    q_raw = synth.index_q_raw(w, 0, lay.n_q)
+    k_raw = synth.index_k_raw(w, 0, lay.n_k)
+    wt = synth.index_weights(w, 0, lay.n_q)
+    rope = 0 if dtype == "fp8" else w.rope_dim
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dtype]
+    say(f"prep {dtype}")
+    q, k, wo, ks = dsa.dsa_indexer_prep(dev(q_raw), dev(k_raw), dev(wt),
+                                        i32(lay.positions()), i32(lay.key_positions()),
+                                        out_dtype=tdt, rope_dim=rope, rope_main_dim=w.rope_main_dim,
+                                        rope_theta=w.rope_theta)
+    p = o_prep.prepare_indexer_inputs(q_raw, k_raw, wt, lay.positions(), lay.key_positions(),
+                                      dtype, rope, w.rope_main_dim, w.rope_theta)
+    gq, gk, gw = host(q), host(k), host(wo)
+    if dtype == "f32":
+        np.testing.assert_allclose(gq, p["q"], rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(gk, p["k"], rtol=1e-5, atol=1e-5)
+        np.testing.assert_array_equal(gw, p["w"])
+    elif dtype == "bf16":
+        # the device computes in fp32 and rounds once: apart by at most one bf16
+        # step plus the fp32 rounding of the rotation (absolute, |x| ~ 1), which
+        # dominates where the two rotated terms cancel
+        for g_, o_ in ((gq, p["q"]), (gk, p["k"])):
+            step = np.exp2(np.floor(np.log2(np.maximum(np.abs(o_), 1e-30))) - 7)
+            assert np.all(np.abs(g_ - o_) <= step * 1.0001 + 2e-6)
+            assert np.mean(g_ != o_) < 0.02
+        np.testing.assert_array_equal(gw, p["w"])
+    else:
+        np.testing.assert_array_equal(host(ks), p["k_scale"])          # scales identical
+        np.testing.assert_array_equal(gq, p["q"])                      # no norm: codes identical
+        np.testing.assert_array_equal(gw, p["w"])                      # folded weights identical
+        mism = gk != p["k"]                                            # LayerNorm'd keys: fp32 vs fp64
+        assert np.mean(mism) < 0.01
+        step = np.exp2(np.floor(np.log2(np.maximum(np.abs(p["k"]), 2.0 ** -6))) - 3)
+        assert np.all(np.abs(gk - p["k"])[mism] <= step[mism] * 1.0001)
