@@ -1,0 +1,233 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+One step = one pass of the hot path over the 4K-token prefill workload
+(one causal sequence T=4096, bf16): lightning-indexer scores -> per-row top-k
+(index_topk 2048) -> sparse MLA (128 heads, d_qk 576, d_v 512).  The indexer
+operands are prepared once (key LayerNorm + RoPE + bf16) by the library's prep
+kernel before timing; all inputs are seeded synthetic data resident in HBM.
+
+Printed: ONE JSON line.  ``value`` is the step throughput in indexer q.k pairs
+per second (valid causal (t, s) pairs / step time); ``components`` holds the
+three per-stage rates of the metric, each timed with HIP events around its own
+launches on the launch stream; ``roofline`` is for the dominant kernel;
+``cpu_baseline`` is the float64 CPU oracle timed on a row sample of the same
+workload on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+MLA_FLOP_PER_PAIR = 2 * 128 * (576 + 512)   # 278,528
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_08_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "counters_prefill4k.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(host_inputs, seconds: float = 20.0):
+    """Oracle (float64 numpy) over a stratified row sample of the same workload
+    (the same seeded inputs the GPU run uses): indexer scores of each sampled
+    row, its top-k, and sparse attention over the selection.  Rate in the unit
+    of ``value``: indexer pairs per second of oracle time."""
+    import numpy as np
+    import synth
+    from oracle import indexer as o_idx, mla as o_mla, prep as o_prep, topk as o_topk, windows as o_win
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    w = synth.WORKLOADS["prefill4k"]
+    lay = synth.layout(w)
+    rows = host_inputs["rows"]
+    rs, re = o_win.row_windows(lay.cu_q, lay.cu_k)
+    kv = o_prep.round_bf16(host_inputs["mla_kv"])
+    pk = o_prep.prepare_indexer_inputs(np.zeros((1, w.n_heads, w.head_dim)), host_inputs["k_raw"],
+                                       np.zeros((1, w.n_heads)), np.zeros(1), lay.key_positions(),
+                                       "bf16", w.rope_dim, w.rope_main_dim, w.rope_theta)
+    t0 = time.perf_counter()
+    pairs = 0
+    done = 0
+    for i, t in enumerate(rows):
+        t = int(t)
+        pq = o_prep.prepare_indexer_inputs(host_inputs["q_raw"][i:i + 1], pk["k"][:1],
+                                           host_inputs["w"][i:i + 1], np.array([t]), np.zeros(1),
+                                           "bf16", w.rope_dim, w.rope_main_dim, w.rope_theta)
+        a, b = int(rs[t]), int(re[t])
+        s = o_idx.score_row(pq["q"][0], pk["k"][a:b], pq["w"][0])
+        full = np.full(lay.n_k, -np.inf, np.float32)
+        full[a:b] = s
+        idx = o_topk.topk_row(full, a, b, w.index_topk)
+        o_mla.attend_row(o_prep.round_bf16(host_inputs["mla_q"][i]), kv, idx, w.sm_scale, w.d_v)
+        pairs += b - a
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": pairs / dt, "unit": "indexer pairs/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {lay.n_q} query rows in a seeded random order (stopped after "
+                      f"{seconds:.0f} s or all rows), each through indexer scores, top-k and sparse "
+                      f"MLA in float64: {pairs} indexer pairs in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_08_amd as dsa
+    import synth
+
+    dsa.load()
+    dev = "cuda"
+    w = synth.WORKLOADS["prefill4k"]
+    lay = synth.layout(w)
+    i32 = lambda x: torch.from_numpy(np.asarray(x, np.int32)).to(dev)
+    inp = synth.device_inputs(w, dev, lay)
+    rs, re = dsa.dsa_row_windows(i32(lay.cu_q), i32(lay.cu_k), lay.n_q)
+    q, k, wt, _ = dsa.dsa_indexer_prep(inp["q_raw"], inp["k_raw"], inp["w"], i32(lay.positions()),
+                                       i32(lay.key_positions()), torch.bfloat16, w.rope_dim,
+                                       w.rope_main_dim, w.rope_theta)
+    mq = inp["mla_q"].to(torch.bfloat16)
+    mkv = inp["mla_kv"].to(torch.bfloat16)
+    host_inputs = None
+    if not args.no_cpu:
+        rows = np.random.default_rng(5).permutation(lay.n_q)   # seeded order, time-bounded
+        rt = torch.from_numpy(rows).to(dev)
+        host_inputs = {"rows": rows, "k_raw": inp["k_raw"].cpu().numpy(),
+                       "mla_kv": inp["mla_kv"].cpu().numpy(),
+                       "q_raw": inp["q_raw"][rt].cpu().numpy(), "w": inp["w"][rt].cpu().numpy(),
+                       "mla_q": inp["mla_q"][rt].cpu().numpy()}
+    del inp
+    K = w.index_topk
+    scores = torch.full((lay.n_q, lay.n_k), float("-inf"), dtype=torch.float32, device=dev)
+    idx = torch.empty((lay.n_q, K), dtype=torch.int32, device=dev)
+    out = torch.empty((lay.n_q, w.mla_heads, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((lay.n_q, w.mla_heads), dtype=torch.float32, device=dev)
+    ws_bytes = dsa.sparse_mla_workspace(lay.n_q, w.mla_heads, w.d_qk, w.d_v, K, 1)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    stage_ms = {"indexer": [], "topk": [], "mla": []}
+
+    def step(record: bool):
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        dsa.dsa_indexer_scores(q, k, wt, rs, re, scores=scores)
+        e[1].record()
+        dsa.dsa_topk(scores, rs, re, K, out=idx)
+        e[2].record()
+        dsa.dsa_sparse_mla_fwd(mq, mkv, idx, w.sm_scale, w.d_v, out=out, lse=lse, workspace=ws)
+        e[3].record()
+        return e if record else None
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = [step(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e in evs:
+        stage_ms["indexer"].append(e[0].elapsed_time(e[1]))
+        stage_ms["topk"].append(e[1].elapsed_time(e[2]))
+        stage_ms["mla"].append(e[2].elapsed_time(e[3]))
+    ms_step = wall * 1e3 / args.steps
+
+    pairs = lay.n_q * (lay.n_q + 1) // 2                               # valid (t, s), s <= t
+    mla_pairs = sum(min(t + 1, K) for t in range(lay.n_q))            # selected (t, j)
+    avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
+    idx_flop = pairs * 2 * w.n_heads * w.head_dim
+    mla_flop = mla_pairs * MLA_FLOP_PER_PAIR
+    topk_bytes = pairs * 4 + lay.n_q * K * 4                          # valid scores read + idx written
+    components = {
+        "indexer_pairs_per_s": pairs / (avg["indexer"] * 1e-3),
+        "indexer_tflops": idx_flop / (avg["indexer"] * 1e-3) / 1e12,
+        "topk_rows_per_s": lay.n_q / (avg["topk"] * 1e-3),
+        "topk_gbs": topk_bytes / (avg["topk"] * 1e-3) / 1e9,
+        "sparse_mla_tflops": mla_flop / (avg["mla"] * 1e-3) / 1e12,
+        "stage_ms": {s: round(v, 4) for s, v in avg.items()},
+    }
+    # dominant kernel of the step
+    dom = max(avg, key=avg.get)
+    if dom == "mla":
+        ach = mla_flop / (avg["mla"] * 1e-3) / 1e12
+        roof = {"kernel": "mla_bf16_kernel", "bound": "mfma", "achieved": ach,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                "traffic": traffic_from_profile("mla_bf16_kernel")}
+    elif dom == "indexer":
+        ach = idx_flop / (avg["indexer"] * 1e-3) / 1e12
+        roof = {"kernel": "indexer_rows_kernel", "bound": "mfma", "achieved": ach,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                "traffic": traffic_from_profile("indexer_rows_kernel")}
+    else:
+        ach = topk_bytes / (avg["topk"] * 1e-3) / 1e9
+        roof = {"kernel": "topk_rows_kernel", "bound": "hbm", "achieved": ach,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": traffic_from_profile("topk_rows_kernel")}
+
+    line = {
+        "metric": "indexer q·k pairs/s + top-k rows/s + sparse-MLA TFLOP/s (4K prefill)",
+        "value": pairs / (ms_step * 1e-3),
+        "unit": "indexer pairs/s (whole step: indexer + top-k + sparse MLA)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill4k: one causal sequence T=4096, bf16; indexer 64 heads x 128 "
+                               "(RoPE on 64 dims), fp32 head weights; index_topk 2048; sparse MLA "
+                               "128 heads, d_qk 576, d_v 512",
+                   "global_batch": 1, "seq_len": lay.n_q, "parallelism": "none (1 GPU)"},
+        "components": components,
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(host_inputs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
