@@ -42,16 +42,23 @@ namespace {
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kKT = 32;                         // selected keys per tile
-constexpr int kRowBytes = kDqk * 2;             // 1152
-constexpr int kKvStride = kRowBytes + 16;       // 1168: padded LDS row
-constexpr int kVtStride = kKT * 2 + 16;         // 80 bytes per V^T row
+constexpr int kRowBytes = kDqk * 2;             // 1152 bytes = 72 chunks of 16
+constexpr int kRowChunks = kRowBytes / 16 + 1;  // 73: one pad chunk per LDS row
+constexpr int kKvStride = kRowChunks * 16;      // 1168: padded LDS row
+constexpr int kTileChunks = kKT * kRowChunks;   // 2336
+constexpr int kDmaPerTile = (kTileChunks + kWave - 1) / kWave;  // 37 wave loads of 1 KB
 constexpr int kQSteps = kDqk / 16 / 2;          // 18 K-steps per wave (half of d_qk)
 constexpr int kVTiles = kDv / 32 / 2;           // 8 value tiles per wave (half of d_v)
 constexpr int kThreads = 512;                   // 8 waves: 4 head groups x 2 halves
+constexpr int kWaves = kThreads / kWave;
+constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // 5
 constexpr int kHeadsPerBlock = 128;
-constexpr int kChunksPerRow = kRowBytes / 16;   // 72
-constexpr int kChunks = kKT * kChunksPerRow;    // 2304
+constexpr int kMaxIdx = 2048;                   // selected keys per workgroup (LDS-staged)
 constexpr float kRescaleSlack = 8.0f;
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
 
 // Row (head offset inside the wave's 32) that accumulator register r of a
 // 32x32 MFMA output holds in lane half `half`.
@@ -59,10 +66,34 @@ __device__ __forceinline__ int acc_row(int r, int half) {
   return 8 * (r >> 2) + 4 * half + (r & 3);
 }
 
-// Position of key j (0..31) inside a V^T row: each 16-key K-step is stored so
-// that lane half g reads keys {4g..4g+3, 8+4g..8+4g+3} as 8 consecutive entries.
-__device__ __forceinline__ int vt_pos(int j) {
-  return (j & 16) | (((j >> 2) & 1) << 3) | (((j >> 3) & 1) << 2) | (j & 3);
+struct MlaShared {
+  float sx[kWaves][16][kWave];    // partial S^T exchange between the two d_qk halves
+  int idx[kMaxIdx];               // this workgroup's slice of the top-k row
+  int last;
+};
+
+// Issue the LDS-DMA loads of one tile (local tile number lt): wave-load j copies
+// LDS chunks [64j, 64j+64) of the padded tile; chunk c is (key c/73, 16-byte
+// piece c%73 of that key's latent row; piece 72 is the row pad and repeats piece
+// 71).  A -1 index loads row 0 (its scores are masked).
+__device__ __forceinline__ void dma_tile(uint8_t* buf, const int* sidx, int lt,
+                                         const uint8_t* __restrict__ kv, int wave, int lane) {
+  // keep the per-lane address arithmetic inside the loop: hoisted, it would be
+  // spilled, and the scratch reloads would wait on the DMA counter
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int u = 0; u < kDmaPerWave; ++u) {
+    const int j = wave + kWaves * u;
+    const int c = j * kWave + lane;
+    if (j < kDmaPerTile && c < kTileChunks) {
+      const int key = c / kRowChunks;
+      int cc = c - key * kRowChunks;
+      cc = cc < kRowChunks - 1 ? cc : kRowChunks - 2;
+      const int r = sidx[lt * kKT + key];
+      const uint8_t* src = kv + int64_t(r < 0 ? 0 : r) * kRowBytes + cc * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(buf + j * kWave * 16), 16, 0, 0);
+    }
+  }
 }
 
 // One workgroup: one query, 128 heads.  Wave w: head group g = w & 3 (32 heads),
@@ -70,15 +101,96 @@ __device__ __forceinline__ int vt_pos(int j) {
 // the two partials are added through LDS (both waves then hold the same S and run
 // the same softmax), and half h accumulates output columns [256h, 256h+256).
 // Everything lives in VGPRs (Q^T half: 72, O half: 128 per lane).
+__shared__ __attribute__((aligned(16))) uint8_t g_kv0[kKT * kKvStride];
+__shared__ __attribute__((aligned(16))) uint8_t g_kv1[kKT * kKvStride];
+
+template <int kBuf>
+__device__ __forceinline__ void mla_tile(MlaShared& sh, const bf16x8_t (&qf)[kQSteps],
+                                         f32x16_t (&o)[kVTiles], float& m_run, float& l_run,
+                                         uint32_t vmask, float sm_scale, int wave, int lane) {
+  const uint8_t* buf = kBuf == 0 ? g_kv0 : g_kv1;
+  const int half = lane >> 5;
+  const int hs = wave >> 2;
+
+  // partial S^T = K . Q^T over this wave's half of d_qk (keys on M, heads on N)
+  f32x16_t s = f32x16_t{};
+  const uint8_t* ka = buf + (lane & 31) * kKvStride + hs * kDqk + half * 16;
+#pragma unroll
+  for (int st = 0; st < kQSteps; ++st)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(ka + st * 32),
+                                                qf[st], s, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sh.sx[wave][r][lane] = s[r];
+  // LDS-only exchange: wait for this wave's LDS writes, then a plain barrier (a
+  // full __syncthreads would also wait for the in-flight LDS-DMA of the next tile)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  float mt = -INFINITY;
+  const uint32_t mv = vmask >> (4 * half);  // bit 8*(r/4) + r%4 = key of register r
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float other = sh.sx[wave ^ 4][r][lane];
+    const float full = hs == 0 ? s[r] + other : other + s[r];  // same bits in both halves
+    s[r] = ((mv >> (8 * (r >> 2) + (r & 3))) & 1u) ? full * sm_scale : -INFINITY;
+    mt = fmaxf(mt, s[r]);
+  }
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const bool grow = mt > m_run + kRescaleSlack;
+  if (__ballot(grow) != 0ull) {
+    const float m_new = grow ? mt : m_run;
+    const float alpha = grow ? (m_run == -INFINITY ? 0.0f : __expf(m_run - m_new)) : 1.0f;
+    l_run *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float ar = __shfl(alpha, acc_row(r, half));
+#pragma unroll
+      for (int n = 0; n < kVTiles; ++n) o[n][r] *= ar;
+    }
+  }
+  bf16x8_t p0, p1;
+  float ps = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p = s[r] == -INFINITY ? 0.0f : __expf(s[r] - m_run);
+    const uint16_t pb = f32_to_bf16_bits(p);
+    ps += bf16_bits_to_f32(pb);
+    const __bf16 pv = __builtin_bit_cast(__bf16, pb);
+    if (r < 8) p0[r] = pv;
+    else p1[r - 8] = pv;
+  }
+  l_run += ps;
+
+  // O[:, 256*hs .. +256] += P . V.  The B operand (8 keys x 1 value column per
+  // lane) is read from the row-major tile with ds_read_b64_tr_b16: in each group
+  // of 16 lanes, lane 4m+q reads 4 value columns of key row k0+m and the
+  // transpose hands lane i the 4 keys k0..k0+3 of column n0+i.  Lane half h
+  // needs keys {4h..4h+3} (first read) and {8+4h..8+4h+3} (second read) of each
+  // 16-key step, the order in which P sits in the S^T accumulator.
+  const int grp = lane >> 4;      // 16-lane group
+  const int li = lane & 15;
+  const int n0 = 16 * (grp & 1);  // value column offset of the group inside a 32-wide tile
+  const uint8_t* vb = buf + (li >> 2) * kKvStride + (hs * kVTiles * 32 + n0 + 4 * (li & 3)) * 2;
+#pragma unroll
+  for (int n = 0; n < kVTiles; ++n) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint8_t* base = vb + (16 * ks + 4 * half) * kKvStride + n * 64;
+      const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
+      const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kKvStride));
+      const bf16x8_t v = __builtin_bit_cast(
+          bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ks == 0 ? p0 : p1, v, o[n], 0, 0, 0);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ idx, int H, int K, float sm_scale,
     __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_lse, int nsplit) {
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[kKT * kKvStride];
-  __shared__ __attribute__((aligned(16))) uint8_t vts[kDv * kVtStride];
-  __shared__ float sx[kThreads / kWave][16][kWave];
-  __shared__ int sidx[kKT];
+  __shared__ __attribute__((aligned(16))) MlaShared sh;
 
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -90,6 +202,34 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   const int h0 = int(blockIdx.y) * kHeadsPerBlock + grp * 32;
   const int head = h0 + (lane & 31);
   const bool hvalid = head < H;
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
+
+  const int ntiles = (K + kKT - 1) / kKT;
+  const int i0 = int(int64_t(ntiles) * blockIdx.z / nsplit);
+  int i1 = int(int64_t(ntiles) * (blockIdx.z + 1) / nsplit);
+  const int32_t* irow = idx + t * K;
+
+  // Stage this workgroup's index slice in LDS (padded with -1 to whole tiles) and
+  // drop trailing tiles that hold only -1 padding (top-k rows are -1 padded at
+  // the end); padding elsewhere is masked per key.
+  {
+    if (tid == 0) sh.last = -1;
+    __syncthreads();
+    int last = -1;
+    const int jbase = i0 * kKT;
+    for (int x = tid; x < (i1 - i0) * kKT; x += kThreads) {
+      const int j = jbase + x;
+      const int r = j < K ? irow[j] : -1;
+      sh.idx[x] = r;
+      if (r >= 0) last = x;
+    }
+    if (last >= 0) atomicMax(&sh.last, last);
+    __syncthreads();
+    last = sh.last;
+    i1 = last < 0 ? i0 : i0 + last / kKT + 1;
+  }
+  const int nt = i1 - i0;
+  if (nt > 0) dma_tile(g_kv0, sh.idx, 0, kvb, wave, lane);
 
   // Q^T fragments: lane holds q[t, head, 288*hs + 16*st + 8*half .. +8]
   bf16x8_t qf[kQSteps];
@@ -109,124 +249,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   float m_run = -INFINITY;  // per head (lane column), same in both lane halves
   float l_run = 0.0f;       // per head, partial over this lane half's keys
 
-  const int ntiles = (K + kKT - 1) / kKT;
-  const int i0 = int(int64_t(ntiles) * blockIdx.z / nsplit);
-  int i1 = int(int64_t(ntiles) * (blockIdx.z + 1) / nsplit);
-  const int32_t* irow = idx + t * K;
-
-  // Trailing tiles that hold only -1 padding are not visited (the top-k rows
-  // are -1 padded at the end).  Padding elsewhere is masked per key.
-  {
-    int last = -1;
-    const int j1 = min(K, i1 * kKT);
-    for (int j = i0 * kKT + tid; j < j1; j += kThreads)
-      if (irow[j] >= 0) last = j;
-    if (tid == 0) sidx[0] = -1;
+  for (int lt = 0; lt < nt; lt += 2) {
+    // tile lt (buffer 0); the DMA of tile lt+1 into buffer 1 overlaps it
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (last >= 0) atomicMax(&sidx[0], last);
+    if (lt + 1 < nt) dma_tile(g_kv1, sh.idx, lt + 1, kvb, wave, lane);
+    mla_tile<0>(sh, qf, o, m_run, l_run, uint32_t(__ballot(sh.idx[lt * kKT + (lane & 31)] >= 0)),
+                sm_scale, wave, lane);
+    if (lt + 1 >= nt) break;
+    // tile lt+1 (buffer 1)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    last = sidx[0];
-    i1 = last < 0 ? i0 : last / kKT + 1;
-    __syncthreads();
-  }
-
-  for (int i = i0; i < i1; ++i) {
-    if (tid < kKT) {
-      const int j = i * kKT + tid;
-      sidx[tid] = j < K ? irow[j] : -1;
-    }
-    __syncthreads();
-    const uint32_t vmask = uint32_t(__ballot(sidx[lane & 31] >= 0));
-    // gather: thread = (key pair kp, chunk group cg) copies chunks cg, cg+32,
-    // cg+64 of keys 2kp and 2kp+1 row-major, and writes their value parts into
-    // V^T as dwords holding the two keys' entries (adjacent V^T positions).
-    {
-      const int kp = tid & 15;
-      const int cg = tid >> 4;
-      const int r0 = sidx[2 * kp], r1 = sidx[2 * kp + 1];
-      const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
-      const uint8_t* g0 = kvb + int64_t(r0 < 0 ? 0 : r0) * kRowBytes;
-      const uint8_t* g1 = kvb + int64_t(r1 < 0 ? 0 : r1) * kRowBytes;
-      uint8_t* d0 = kvs + (2 * kp) * kKvStride;
-      uint8_t* dvt = vts + vt_pos(2 * kp) * 2;
-#pragma unroll
-      for (int c = 0; c < 3; ++c) {
-        const int cc = cg + 32 * c;
-        if (cc < kChunksPerRow) {
-          i32x4_t a = {}, b = {};
-          if (r0 >= 0) a = *reinterpret_cast<const i32x4_t*>(g0 + cc * 16);
-          if (r1 >= 0) b = *reinterpret_cast<const i32x4_t*>(g1 + cc * 16);
-          *reinterpret_cast<i32x4_t*>(d0 + cc * 16) = a;
-          *reinterpret_cast<i32x4_t*>(d0 + kKvStride + cc * 16) = b;
-          if (cc < kDv / 8) {
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              const uint32_t lo = (uint32_t(a[x >> 1]) >> (16 * (x & 1))) & 0xFFFFu;
-              const uint32_t hi = (uint32_t(b[x >> 1]) >> (16 * (x & 1))) & 0xFFFFu;
-              *reinterpret_cast<uint32_t*>(dvt + (cc * 8 + x) * kVtStride) = lo | (hi << 16);
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-
-    // partial S^T = K . Q^T over this wave's half of d_qk (keys on M, heads on N)
-    f32x16_t s = f32x16_t{};
-    const uint8_t* ka = kvs + (lane & 31) * kKvStride + hs * kDqk + half * 16;
-#pragma unroll
-    for (int st = 0; st < kQSteps; ++st)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8_t*>(ka + st * 32), qf[st], s, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sx[wave][r][lane] = s[r];
-    __syncthreads();
-    float mt = -INFINITY;
-    const uint32_t mv = vmask >> (4 * half);  // bit 8*(r/4) + r%4 = key of register r
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float other = sx[wave ^ 4][r][lane];
-      const float full = hs == 0 ? s[r] + other : other + s[r];  // same bits in both halves
-      s[r] = ((mv >> (8 * (r >> 2) + (r & 3))) & 1u) ? full * sm_scale : -INFINITY;
-      mt = fmaxf(mt, s[r]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool grow = mt > m_run + kRescaleSlack;
-    if (__ballot(grow) != 0ull) {
-      const float m_new = grow ? mt : m_run;
-      const float alpha = grow ? (m_run == -INFINITY ? 0.0f : __expf(m_run - m_new)) : 1.0f;
-      l_run *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float ar = __shfl(alpha, acc_row(r, half));
-#pragma unroll
-        for (int n = 0; n < kVTiles; ++n) o[n][r] *= ar;
-      }
-    }
-    bf16x8_t p0, p1;
-    float ps = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = s[r] == -INFINITY ? 0.0f : __expf(s[r] - m_run);
-      const uint16_t pb = f32_to_bf16_bits(p);
-      ps += bf16_bits_to_f32(pb);
-      const __bf16 pv = __builtin_bit_cast(__bf16, pb);
-      if (r < 8) p0[r] = pv;
-      else p1[r - 8] = pv;
-    }
-    l_run += ps;
-
-    // O[:, 256*hs .. +256] += P . V
-    const uint8_t* vb = vts + (hs * kVTiles * 32 + (lane & 31)) * kVtStride + half * 16;
-#pragma unroll
-    for (int n = 0; n < kVTiles; ++n) {
-      const bf16x8_t v0 = *reinterpret_cast<const bf16x8_t*>(vb + n * 32 * kVtStride);
-      const bf16x8_t v1 = *reinterpret_cast<const bf16x8_t*>(vb + n * 32 * kVtStride + 32);
-      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, v0, o[n], 0, 0, 0);
-      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, v1, o[n], 0, 0, 0);
-    }
-    __syncthreads();
+    if (lt + 2 < nt) dma_tile(g_kv0, sh.idx, lt + 2, kvb, wave, lane);
+    mla_tile<1>(sh, qf, o, m_run, l_run,
+                uint32_t(__ballot(sh.idx[(lt + 1) * kKT + (lane & 31)] >= 0)), sm_scale, wave, lane);
   }
 
   // epilogue
@@ -352,11 +388,14 @@ __global__ __launch_bounds__(128) void mla_f32_kernel(const float* __restrict__ 
 int mla_splits(int64_t n_q, int32_t n_heads, int32_t K) {
   const int64_t blocks = n_q * ((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
   const int ntiles = (K + kKT - 1) / kKT;
-  if (blocks >= 192) return 1;
-  int s = int((256 + blocks - 1) / blocks);
-  if (s > ntiles) s = ntiles;
-  if (s > 16) s = 16;
-  return s < 1 ? 1 : s;
+  const int min_s = (ntiles + kMaxIdx / kKT - 1) / (kMaxIdx / kKT);  // <= kMaxIdx keys each
+  int s = 1;
+  if (blocks < 192) {
+    s = int((256 + blocks - 1) / blocks);
+    if (s > ntiles) s = ntiles;
+    if (s > 16) s = 16;
+  }
+  return s < min_s ? min_s : (s < 1 ? 1 : s);
 }
 
 }  // namespace
