@@ -3,7 +3,7 @@
 #include <climits>
 #include <cstdint>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "dsa_launch.h"
 
 namespace {

@@ -12,11 +12,12 @@
 // logits never leave the registers.
 //
 // Two work layouts:
-//   rows kernel (prefill)  8 waves = 8 consecutive query rows share each 32-key
-//                          tile staged in LDS (padded rows: conflict-free b128
-//                          reads); q and w of a row stay in registers for the
-//                          whole key loop; row blocks are issued latest-first so
-//                          the longest causal rows start first.
+//   rows kernel (prefill)  8 waves = 8 consecutive query rows share 256-key
+//                          chunks staged in LDS by LDS-DMA (XOR-swizzled rows:
+//                          conflict-free b128 fragment reads); q and w of a row
+//                          stay in registers for the whole key loop; row blocks
+//                          are issued latest-first so the longest causal rows
+//                          start first.
 //   rowsplit kernel (decode) one long row per workgroup slice: each wave streams
 //                          its own 32-key tiles straight from global memory (the
 //                          keys are read once, so there is nothing to share).
@@ -82,49 +83,165 @@ struct QueryRow {
     }
   }
 
-  // Scores of the 32 keys whose fragments are in kb; lanes l and l^32 both end
-  // with the score of key l%32.
-  __device__ __forceinline__ float score(const typename Op::frag_t (&kb)[Op::kSteps]) const {
-    f32x16_t acc[MT];
+  // Logits of the 32 keys whose fragments are in kb (heads on M, keys on N).
+  __device__ __forceinline__ void mma(const typename Op::frag_t (&kb)[Op::kSteps],
+                                      f32x16_t (&acc)[MT]) const {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
 #pragma unroll
     for (int st = 0; st < Op::kSteps; ++st)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mfma(qa[mt][st], kb[st], acc[mt]);
+  }
+
+  // ReLU, head weights and the head sum; lanes l and l^32 both end with the
+  // score of key l%32.  ReLU is a signed-integer max on the float bits:
+  // non-negative floats keep their bits, every negative float (and -0.0) has
+  // negative bits and becomes +0.0 -- one v_max_i32 instead of the two VALU ops
+  // of an IEEE fmaxf.
+  __device__ __forceinline__ float epilogue(const f32x16_t (&acc)[MT]) const {
     float p = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p = fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.0f), p);
-    return p + __shfl_xor(p, 32);
+      for (int r = 0; r < 16; ++r)
+        p = fmaf(wv[mt][r], __int_as_float(max(__float_as_int(acc[mt][r]), 0)), p);
+    // v_permlane32_swap: lanes 0-31 and 32-63 exchange this value
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p),
+                                                     false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+
+  __device__ __forceinline__ float score(const typename Op::frag_t (&kb)[Op::kSteps]) const {
+    f32x16_t acc[MT];
+    mma(kb, acc);
+    return epilogue(acc);
   }
 };
 
 // ---------------------------------------------------------------------------
-// prefill: 8 query rows per workgroup, key tiles shared through LDS
+// prefill: 8 query rows per workgroup (one per wave), keys staged through LDS in
+// chunks of 256 by LDS-DMA one chunk ahead (two buffers, one workgroup barrier
+// per 8 tiles, so the two waves of a SIMD drift apart and one wave's ReLU/weight
+// epilogue runs while the other's MFMAs occupy the matrix core).  LDS rows are unpadded; 16-byte pieces
+// are XOR-swizzled by the key so that the fragment reads are conflict-free.
 // ---------------------------------------------------------------------------
 constexpr int kRowsPerBlock = 8;
 constexpr int kRowsThreads = kRowsPerBlock * kWave;
+constexpr int kChunkKeys = 256;
+constexpr int kChunkTiles = kChunkKeys / kKeyTile;
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// LDS position (in 16-byte pieces) of piece cc of local key kl.
+template <class Op>
+__device__ __forceinline__ int swz(int kl, int cc) {
+  return Op::kRowBytes == 256 ? (cc ^ (kl & 15)) : (cc ^ ((kl >> 1) & 7));
+}
+
+template <class Op>
+__device__ __forceinline__ void dma_chunk(uint8_t* buf, const uint8_t* __restrict__ k,
+                                          int key0, int n_k, int wave, int lane) {
+  constexpr int kPieces = Op::kRowBytes / 16;            // per key
+  constexpr int kKeysPerLoad = kWave / kPieces;          // keys per 1 KB wave load
+  constexpr int kLoads = kChunkKeys / kKeysPerLoad;      // wave loads per chunk
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int u = 0; u < (kLoads + kRowsPerBlock - 1) / kRowsPerBlock; ++u) {
+    const int j = wave + kRowsPerBlock * u;
+    if (j < kLoads) {
+      const int kl = j * kKeysPerLoad + lane / kPieces;  // local key of this lane's piece
+      const int p = lane % kPieces;                      // its LDS position
+      int key = key0 + kl;
+      key = key < n_k ? key : n_k - 1;                   // past the end: any valid row
+      const uint8_t* src = k + int64_t(key) * Op::kRowBytes + swz<Op>(kl, p) * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(buf + j * kWave * 16), 16, 0, 0);
+    }
+  }
+}
+
+// K fragments of one 32-key tile (local keys kt*32 .. +32) from a chunk buffer.
+template <class Op>
+__device__ __forceinline__ void load_kfrags(const uint8_t* buf, int kt, int lane,
+                                            typename Op::frag_t (&kb)[Op::kSteps]) {
+  const int kl = kt * kKeyTile + (lane & 31);
+  const uint8_t* row = buf + kl * Op::kRowBytes;
+  constexpr int kFragPieces = Op::kFragBytes / 16;
+#pragma unroll
+  for (int st = 0; st < Op::kSteps; ++st) {
+    const int cc = (2 * st + (lane >> 5)) * kFragPieces;
+    if constexpr (kFragPieces == 1) {
+      kb[st] = *reinterpret_cast<const typename Op::frag_t*>(row + swz<Op>(kl, cc) * 16);
+    } else {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + swz<Op>(kl, cc) * 16);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(row + swz<Op>(kl, cc + 1) * 16);
+      kb[st] = __builtin_bit_cast(typename Op::frag_t,
+                                  __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+}
+
+// Two chunk buffers as separate LDS objects, so that the compiler can tell the
+// in-flight LDS-DMA target apart from the buffer being read (it then inserts no
+// wait for the DMA before those reads).
+constexpr int kChunkBytesMax = kChunkKeys * 256;
+__shared__ __attribute__((aligned(16))) uint8_t g_kb0[kChunkBytesMax];
+__shared__ __attribute__((aligned(16))) uint8_t g_kb1[kChunkBytesMax];
+
+template <int kBuf>
+__device__ __forceinline__ uint8_t* kbuf() {
+  return kBuf == 0 ? g_kb0 : g_kb1;
+}
+
+// Scores of one wave's row over chunk c (keys key0 .. key0+255), which sits in
+// buffer kCur; the DMA of chunk c+1 goes to the other buffer kNn.
+template <class Op, int MT, int kCur, int kNn>
+__device__ __forceinline__ void rows_chunk(int c, int nchunks, int key0, int hi, int n_k,
+                                           const uint8_t* __restrict__ k,
+                                           const float* __restrict__ k_scale,
+                                           const QueryRow<Op, MT>& qr, bool active, int a, int b,
+                                           float* srow, int wave, int lane) {
+  // per-lane key scales of this chunk, read before the next DMA is issued so that
+  // waiting for them never waits for that DMA
+  float ksc[kChunkTiles];
+#pragma unroll
+  for (int kt = 0; kt < kChunkTiles; ++kt) {
+    const int s = key0 + kt * kKeyTile + (lane & 31);
+    ksc[kt] = (k_scale != nullptr && s < hi) ? k_scale[s] : 1.0f;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA pieces of chunk c landed
+  __syncthreads();                // ... everyone's; all waves are done with chunk c-1
+  if (c + 1 < nchunks) dma_chunk<Op>(kbuf<kNn>(), k, key0 + kChunkKeys, n_k, wave, lane);
+  if (!active || key0 >= b || key0 + kChunkKeys <= a) return;
+  // Plain per-tile order (fragment reads, MFMAs, epilogue): the two waves that
+  // share a SIMD interleave each other's MFMA and VALU phases, which measured
+  // faster than interleaving one wave's next-tile MFMAs with its own epilogue.
+#pragma unroll
+  for (int kt = 0; kt < kChunkTiles; ++kt) {
+    const int s0 = key0 + kt * kKeyTile;
+    if (s0 >= b || s0 + kKeyTile <= a) continue;
+    typename Op::frag_t kb[Op::kSteps];
+    load_kfrags<Op>(kbuf<kCur>(), kt, lane, kb);
+    const float p = qr.score(kb) * ksc[kt];
+    const int s = s0 + lane;
+    if (lane < 32 && s >= a && s < b) srow[s] = p;
+  }
+}
 
 template <class Op, int MT>
 __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const float* __restrict__ w,
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ row_ends,
-    int64_t n_q, int H, float* __restrict__ scores, int64_t ld, int nsplit) {
-  constexpr int kStride = Op::kRowBytes + 16;  // padded LDS row
-  constexpr int kChunksPerKey = Op::kRowBytes / 16;
-  constexpr int kChunks = kKeyTile * kChunksPerKey;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kKeyTile * kStride];
+    int64_t n_q, int n_k, int H, float* __restrict__ scores, int64_t ld) {
   __shared__ int win[2 * kRowsPerBlock];
   __shared__ int span[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int64_t nrb = (n_q + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int64_t t0 = (nrb - 1 - int64_t(blockIdx.x)) * kRowsPerBlock;
+  const int64_t t0 = (nrb - 1 - int64_t(blockIdx.x)) * kRowsPerBlock;  // latest rows first
 
   if (tid < kRowsPerBlock) {
     const int64_t t = t0 + tid;
@@ -151,47 +268,22 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
   __syncthreads();
   const int lo = span[0], hi = span[1];
   if (hi <= lo) return;
-  const int ntiles = (hi - lo + kKeyTile - 1) / kKeyTile;
-  const int i0 = int(int64_t(ntiles) * blockIdx.y / nsplit);
-  const int i1 = int(int64_t(ntiles) * (blockIdx.y + 1) / nsplit);
-  if (i0 >= i1) return;
+  const int nchunks = (hi - lo + kChunkKeys - 1) / kChunkKeys;
+  dma_chunk<Op>(kbuf<0>(), k, lo, n_k, wave, lane);
 
   const int64_t t = t0 + wave;
   const int a = win[wave], b = win[kRowsPerBlock + wave];
   const bool active = b > a;
   QueryRow<Op, MT> qr;
   if (active) qr.load(q, w, t, H, lane);
+  float* srow = scores + t * ld;
 
-  const int ck = tid / kChunksPerKey, cc = tid % kChunksPerKey;
-  i32x4_t pre = {};
-  auto fetch = [&](int i) {
-    const int s = lo + i * kKeyTile + ck;
-    i32x4_t v = {};
-    if (tid < kChunks && s < hi)
-      v = *reinterpret_cast<const i32x4_t*>(k + int64_t(s) * Op::kRowBytes + cc * 16);
-    pre = v;
-  };
-  fetch(i0);
-  const int half = lane >> 5;
-  for (int i = i0; i < i1; ++i) {
-    __syncthreads();
-    if (tid < kChunks) *reinterpret_cast<i32x4_t*>(tile + ck * kStride + cc * 16) = pre;
-    __syncthreads();
-    if (i + 1 < i1) fetch(i + 1);
-    const int s0 = lo + i * kKeyTile;
-    if (active && s0 < b && s0 + kKeyTile > a) {
-      typename Op::frag_t kb[Op::kSteps];
-      const uint8_t* src = tile + (lane & 31) * kStride + half * Op::kFragBytes;
-#pragma unroll
-      for (int st = 0; st < Op::kSteps; ++st)
-        kb[st] = *reinterpret_cast<const typename Op::frag_t*>(src + st * 2 * Op::kFragBytes);
-      float p = qr.score(kb);
-      const int s = s0 + lane;
-      if (lane < 32 && s >= a && s < b) {
-        if (k_scale) p *= k_scale[s];
-        scores[t * ld + s] = p;
-      }
-    }
+  for (int c = 0; c < nchunks; c += 2) {
+    rows_chunk<Op, MT, 0, 1>(c, nchunks, lo + c * kChunkKeys, hi, n_k, k, k_scale, qr, active,
+                             a, b, srow, wave, lane);
+    if (c + 1 >= nchunks) break;
+    rows_chunk<Op, MT, 1, 0>(c + 1, nchunks, lo + (c + 1) * kChunkKeys, hi, n_k, k, k_scale, qr,
+                             active, a, b, srow, wave, lane);
   }
 }
 
@@ -283,11 +375,8 @@ hipError_t launch_mfma(const void* q, const void* k, const float* k_scale, const
                        scores, ld, nsplit);
   } else {
     const int64_t nrb = (n_q + kRowsPerBlock - 1) / kRowsPerBlock;
-    int nsplit = int((n_k + 2047) / 2048);
-    nsplit = nsplit < 1 ? 1 : (nsplit > 8 ? 8 : nsplit);
-    hipLaunchKernelGGL((indexer_rows_kernel<Op, MT>), dim3(unsigned(nrb), nsplit),
-                       dim3(kRowsThreads), 0, stream, qb, kb, k_scale, w, rs, re, n_q, H,
-                       scores, ld, nsplit);
+    hipLaunchKernelGGL((indexer_rows_kernel<Op, MT>), dim3(unsigned(nrb)), dim3(kRowsThreads), 0,
+                       stream, qb, kb, k_scale, w, rs, re, n_q, int(n_k), H, scores, ld);
   }
   return hipGetLastError();
 }

@@ -259,6 +259,25 @@ def test_mla_bf16_peaky_and_split(dsa):
     _mla_case(dsa, q, kv, idx, P4K.sm_scale, P4K.d_v, True, "bf16 split peaky")
 
 
+def test_mla_bf16_large_logit_growth(dsa):
+    # The logits rise by ~200 along the (ascending) key order while staying smooth
+    # near the top (noise std ~0.5): far beyond the slack over a first-tile
+    # reference max, so the affected (query, head group) slices take the exact
+    # recomputation path.  The trend lives in a rope dim, so values stay ~N(0, 0.01).
+    g = np.random.default_rng(204)
+    n_kv = 4096
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    kv[:, 512] += np.linspace(0.0, 40.0, n_kv, dtype=np.float32)
+    kv = o_prep.round_bf16(kv)
+    for n_q, what in ((12, "split"), (200, "prefill")):
+        q = synth.mla_q(P4K, 0, n_q)
+        q[:, :, 512] += 120.0
+        q = o_prep.round_bf16(q)
+        idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk)
+        _mla_case(dsa, q, kv, idx, P4K.sm_scale, P4K.d_v, True, f"bf16 logit growth {what}",
+                  rows=range(0, n_q, 3))
+
+
 def test_mla_bf16_fewer_heads(dsa):
     g = np.random.default_rng(203)
     n_q, n_kv = 40, 700
