@@ -266,3 +266,11 @@ def device_inputs(w: Workload, device, lay: Layout | None = None, mla: bool = Tr
         out["mla_q"] = device_normal(w, T_MLA_Q, (lay.n_q, w.mla_heads, w.d_qk), device, w.mla_scale)
         out["mla_kv"] = device_normal(w, T_MLA_KV, (lay.n_k, w.d_qk), device, w.mla_scale)
     return out
+
+
+def device_garbage(w: Workload, shape, device):
+    """+-1e4 with random sign (device tensor): what a score buffer holds outside
+    the rows' windows before the indexer writes the in-window entries."""
+    import torch
+    u = device_uniform(w, T_GARBAGE, shape, device)
+    return torch.where(u < 0.5, torch.tensor(1e4, device=device), torch.tensor(-1e4, device=device))

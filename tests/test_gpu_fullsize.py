@@ -1,0 +1,179 @@
+"""Full-size parity on the five workloads, in the launch configuration the
+benchmark times, compared with the oracle on sampled rows.
+
+Each workload runs the whole path on the GPU from the same seeded raw inputs the
+oracle reads: row windows -> indexer operand prep -> indexer scores (into a
+buffer that holds +-1e4 garbage outside the windows) -> top-k -> sparse MLA.
+The oracle runs its own prep, scores, top-k and attention on the sampled rows.
+
+Checks per sampled row:
+  * scores within the stated tolerance of the oracle's (T1);
+  * dsa_topk on the oracle's fp32 scores is bit-identical to the oracle's top-k;
+  * the GPU's end-to-end selection differs from the oracle's only in columns
+    whose score is within tolerance of the k-th (T3);
+  * the fused indexer + top-k call returns the unfused call's indices;
+  * sparse MLA over the oracle's selection matches the oracle (T4), and the
+    full-size MLA output matches it on rows whose selections are identical.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import indexer as o_idx
+from oracle import mla as o_mla
+from oracle import prep as o_prep
+from oracle import topk as o_topk
+from oracle import windows as o_win
+from parity import check_mla, check_scores, check_topk_e2e, dev, host, i32, say
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+
+
+def _rows_of(lay, w, n_random):
+    starts = lay.cu_q[:-1].tolist() if len(lay.q_lens) > 1 else [0]
+    rows = synth.sample_rows(lay.n_q, w.index_topk, seed=w.config_id, n_random=n_random,
+                             starts=starts)
+    return rows
+
+
+def _run_workload(dsa, name, n_random=96):
+    w = synth.WORKLOADS[name]
+    lay = synth.layout(w)
+    K = w.index_topk
+    say(f"[{name}] n_q={lay.n_q} n_k={lay.n_k} dtype={w.dtype} K={K}")
+    inp = synth.device_inputs(w, "cuda", lay, mla=True)
+    rs, re = dsa.dsa_row_windows(i32(lay.cu_q), i32(lay.cu_k), lay.n_q, True)
+    q, k, wt, ks = dsa.dsa_indexer_prep(inp["q_raw"], inp["k_raw"], inp["w"],
+                                        i32(lay.positions()), i32(lay.key_positions()),
+                                        out_dtype=TDT[w.dtype], rope_dim=w.rope_dim,
+                                        rope_main_dim=w.rope_main_dim, rope_theta=w.rope_theta)
+    scores = synth.device_garbage(w, (lay.n_q, lay.n_k), "cuda")
+    dsa.dsa_indexer_scores(q, k, wt, rs, re, k_scale=ks, scores=scores)
+    idx = dsa.dsa_topk(scores, rs, re, K)
+    idx_fused = dsa.dsa_indexer_topk(q, k, wt, rs, re, K, k_scale=ks)
+    mq = inp["mla_q"].to(torch.bfloat16)
+    mkv = inp["mla_kv"].to(torch.bfloat16)
+    out, lse = dsa.dsa_sparse_mla_fwd(mq, mkv, idx, w.sm_scale, w.d_v)
+    torch.cuda.synchronize()
+    say(f"[{name}] GPU path done")
+
+    rows = _rows_of(lay, w, n_random)
+    rt = torch.from_numpy(rows).cuda()
+    g_scores = {int(t): None for t in rows}
+    ors, ore = o_win.row_windows(lay.cu_q, lay.cu_k)
+    assert np.array_equal(host(rs), ors) and np.array_equal(host(re), ore)
+    g_idx = host(idx[rt])
+    assert np.array_equal(g_idx, host(idx_fused[rt])), "fused and unfused indices differ"
+    q_raw_s = host(inp["q_raw"][rt])
+    w_s = host(inp["w"][rt])
+    pos_q = lay.positions()
+    pos_k = lay.key_positions()
+    rtol = 2e-2
+    o_sel = np.full((len(rows), K), -1, np.int32)
+    S_or = np.full((len(rows), lay.n_k), -1e4, np.float32)   # oracle scores (fp32) + garbage
+    ndiff = 0
+    worst = 0.0
+    for i, t in enumerate(rows):
+        t = int(t)
+        a, b = int(ors[t]), int(ore[t])
+        k_raw_win = host(inp["k_raw"][a:b])
+        pk = o_prep.prepare_indexer_inputs(np.zeros((1, w.n_heads, w.head_dim)), k_raw_win,
+                                           np.zeros((1, w.n_heads)), np.zeros(1), pos_k[a:b],
+                                           w.dtype, w.rope_dim, w.rope_main_dim, w.rope_theta)
+        pq = o_prep.prepare_indexer_inputs(q_raw_s[i:i + 1], k_raw_win[:1], w_s[i:i + 1],
+                                           pos_q[t:t + 1], np.zeros(1), w.dtype, w.rope_dim,
+                                           w.rope_main_dim, w.rope_theta)
+        o, c = o_idx.score_row(pq["q"][0], pk["k"], pq["w"][0], pk["k_scale"], with_cond=True)
+        g_row = host(scores[t, a:b])
+        worst = max(worst, check_scores(g_row, o, c, rtol, f"[{name}] row {t}"))
+        full = np.full(lay.n_k, -np.inf)
+        full[a:b] = o
+        tau = np.zeros(lay.n_k)
+        tau[a:b] = rtol * np.maximum(np.abs(o), c / 128)
+        S_or[i, a:b] = o.astype(np.float32)
+        o_sel[i] = o_topk.topk_row(S_or[i], a, b, K)
+        ndiff += check_topk_e2e(g_idx[i], o_sel[i], full, tau, f"[{name}] row {t}")
+    say(f"[{name}] scores max rel err {worst:.2e}; end-to-end selection differs in {ndiff} columns")
+
+    # top-k bit-exact on the oracle's fp32 scores (same kernel, sampled rows)
+    g_or = host(dsa.dsa_topk(dev(S_or), i32(ors[rows]), i32(ore[rows]), K))
+    bad = np.nonzero((g_or != o_sel).any(axis=1))[0]
+    assert bad.size == 0, f"[{name}] dsa_topk differs from the oracle on rows {rows[bad[:5]]}"
+
+    # sparse MLA: kernel over the oracle's selection vs the oracle
+    kv_host = None
+    oq = o_prep.round_bf16(host(inp["mla_q"][rt]))
+    sel_rows = np.unique(o_sel[o_sel >= 0])
+    kv_sel = o_prep.round_bf16(host(inp["mla_kv"][torch.from_numpy(sel_rows).cuda()]))
+    remap = np.full(lay.n_k, -1, np.int64)
+    remap[sel_rows] = np.arange(len(sel_rows))
+    o_sel_local = np.where(o_sel >= 0, remap[np.maximum(o_sel, 0)], -1)
+    oo, ol = o_mla.sparse_mla(oq, kv_sel, o_sel_local, w.sm_scale, w.d_v)
+    g2, l2 = dsa.dsa_sparse_mla_fwd(mq[rt].contiguous(), mkv, i32(o_sel), w.sm_scale, w.d_v)
+    err = check_mla(host(g2), oo, host(l2), ol, True, f"[{name}] mla on oracle selection")
+    same = [i for i in range(len(rows)) if set(g_idx[i].tolist()) == set(o_sel[i].tolist())]
+    if same:
+        st = torch.from_numpy(rows[same]).cuda()
+        check_mla(host(out[st]), oo[same], host(lse[st]), ol[same], True, f"[{name}] mla end to end")
+    say(f"[{name}] mla max abs err {err:.2e}; {len(same)}/{len(rows)} rows with identical selection")
+    del inp, q, k, wt, ks, scores, idx, idx_fused, mq, mkv, out, lse, kv_host
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_prefill4k(dsa):
+    _run_workload(dsa, "prefill4k", n_random=160)
+
+
+def test_fullsize_thd(dsa):
+    _run_workload(dsa, "thd", n_random=96)
+
+
+def test_fullsize_decode(dsa):
+    _run_workload(dsa, "decode", n_random=64)
+
+
+def test_fullsize_fp8_64k(dsa):
+    _run_workload(dsa, "fp8_64k", n_random=48)
+
+
+def test_fullsize_tiny_fp32(dsa):
+    """The tiny fp32 workload end to end (every row, fp32 tolerances)."""
+    w = synth.WORKLOADS["tiny"]
+    lay = synth.layout(w)
+    K = w.index_topk
+    q_raw = synth.index_q_raw(w, 0, lay.n_q)
+    k_raw = synth.index_k_raw(w, 0, lay.n_k)
+    wt = synth.index_weights(w, 0, lay.n_q)
+    rs, re = dsa.dsa_row_windows(i32(lay.cu_q), i32(lay.cu_k), lay.n_q, True)
+    q, k, wd, _ = dsa.dsa_indexer_prep(dev(q_raw), dev(k_raw), dev(wt), i32(lay.positions()),
+                                       i32(lay.key_positions()), out_dtype=torch.float32)
+    scores = dsa.dsa_indexer_scores(q, k, wd, rs, re)
+    idx = host(dsa.dsa_topk(scores, rs, re, K))
+    p = o_prep.prepare_indexer_inputs(q_raw, k_raw, wt, lay.positions(), lay.key_positions(), "f32")
+    ors, ore = o_win.row_windows(lay.cu_q, lay.cu_k)
+    mq = o_prep.round_f32(synth.mla_q(w, 0, lay.n_q))
+    mkv = o_prep.round_f32(synth.mla_kv(w, 0, lay.n_k))
+    G = host(scores)
+    sel = np.full((lay.n_q, K), -1, np.int32)
+    for t in range(lay.n_q):
+        a, b = ors[t], ore[t]
+        o, c = o_idx.score_row(p["q"][t], p["k"][a:b], p["w"][t], with_cond=True)
+        check_scores(G[t, a:b], o, c, 1e-3, f"tiny row {t}")
+        full = np.full(lay.n_k, -np.inf)
+        full[a:b] = o
+        tau = np.zeros(lay.n_k)
+        tau[a:b] = 1e-3 * np.maximum(np.abs(o), c / 128)
+        sel[t] = o_topk.topk_row(full.astype(np.float32), a, b, K)
+        check_topk_e2e(idx[t], sel[t], full, tau, f"tiny row {t}")
+    # rows t < 15 see fewer than K keys: -1 padding; row 15 sees exactly K
+    assert all((idx[t] == -1).sum() == K - (t + 1) for t in range(15))
+    assert (idx[15] == -1).sum() == 0
+    out, lse = dsa.dsa_sparse_mla_fwd(dev(mq), dev(mkv), i32(sel), w.sm_scale, w.d_v)
+    oo, ol = o_mla.sparse_mla(mq, mkv, sel, w.sm_scale, w.d_v)
+    check_mla(host(out), oo, host(lse), ol, False, "tiny mla")
