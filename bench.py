@@ -33,10 +33,17 @@ FP8_PEAK_TFLOPS = 5000.0
 MLA_FLOP_PER_PAIR = 2 * 128 * (576 + 512)   # 278,528
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {                      # kernel -> the sources its code is built from
+    "mla_bf16_kernel": ["mla.hip", "dsa_device.h"],
+    "indexer_rows_kernel": ["indexer.hip", "dsa_device.h"],
+    "topk_rows_kernel": ["topk.hip", "dsa_device.h"],
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_attention_08_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -44,17 +51,17 @@ def kernel_source_hash() -> str:
 
 def traffic_from_profile(kernel: str):
     """HBM bytes per launch from the committed counter summary, or None when the
-    kernel sources changed since the counters were taken."""
+    kernel's sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "counters_prefill4k.json")
     try:
         with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != kernel_source_hash():
-        return None
     k = d.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None or k.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(host_inputs, seconds: float = 20.0):

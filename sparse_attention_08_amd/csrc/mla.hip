@@ -1,36 +1,43 @@
 // Sparse MLA attention over the top-k selected latent rows (gfx950).
 //
-// Absorbed MLA: every head of a query reads the same latent row per selected
-// key (512 latent dims followed by 64 rope dims, 1152 bytes in bf16); the value
-// is the latent part.  For each query t and head h:
+// Absorbed MLA (vLLM API page "vllm.models.kimi_k3.nvidia.dsa",
+// KimiK3DSAAttention: sparse FlashMLA over the indexer's top-k): every head of a
+// query reads the same latent row per selected key (512 latent dims followed by
+// 64 rope dims, 1152 bytes in bf16); the value is the latent part.  For each
+// query t and head h:
 //   out[t,h,:] = softmax_j(sm_scale * q[t,h,:] . kv[J_j,:]) @ kv[J, :512]
-// over J = the non -1 entries of topk_idx[t].
+//   lse[t,h]   = log sum_j exp(sm_scale * q[t,h,:] . kv[J_j,:])
+// over J = the entries of topk_idx[t] that are not -1.
 //
-// bf16 kernel: one workgroup = one query x 128 heads (4 waves x 32 heads), or a
-// slice of its selected keys when the key list is split (few queries: decode).
-// Per tile of 32 selected keys:
-//   gather    the 32 latent rows are read with 16-byte loads (a 1152-byte row is
-//             9 x 128-byte lines) into LDS twice: row-major (padded to 1168 bytes,
-//             conflict-free b128 fragment reads) for Q.K, and transposed
-//             (V^T [512 x 32], padded rows) for P.V;
+// bf16 kernel: one workgroup = one query x 128 heads, 8 waves = 4 head groups of
+// 32 heads x 2 halves; or a slice of the query's selected keys when the key list
+// is split (few queries: decode).  Per tile of 32 selected keys:
+//   gather    LDS-DMA (global_load_lds, 16 bytes per lane) of the 32 latent rows
+//             into a row-major LDS tile whose rows are padded to 1168 bytes
+//             (conflict-free 16-byte fragment reads); the next tile's gather is
+//             in flight while this one is computed (two LDS buffers);
 //   S^T=K.Q^T v_mfma_f32_32x32x16_bf16 with keys on M and the wave's 32 heads on
-//             N: lane l holds 16 keys of head l%32, so the softmax max/sum over
-//             keys is in-lane plus one exchange with lane l^32.  Q^T stays in
-//             registers for the whole query (36 K-steps of 16 dims);
-//   softmax   fp32, natural-exp; the running max is only moved (and the output
-//             rescaled) when a tile's max exceeds it by more than 8, so the
-//             probabilities stay <= e^8 and the rescale is rare;
-//   O += P.V  the S^T accumulator, rounded to bf16, IS the A operand of the next
-//             MFMA (heads on M, keys on K): the keys of a lane half are taken in
-//             the order the accumulator holds them, and V^T is stored with that
-//             key permutation, so no shuffle of P is needed.  O [32 heads x 512]
-//             stays in 256 accumulator registers per lane.
-// The row sum uses the bf16-rounded probabilities, so the output is an exact
+//             N; half h of a head group contracts dims [288h, 288h+288) with its
+//             Q^T half held in registers for the whole query, and the two fp32
+//             partials are added through LDS (both waves then hold the same S);
+//   softmax   fp32 in base-2 units (sm_scale * log2 e folded into one multiply);
+//             lane l holds 16 keys of head l%32, so the max over keys is in-lane
+//             plus one exchange with lane l^32; the running max only moves (and
+//             the output is rescaled) when a tile's max exceeds it by more than
+//             8, so the probabilities stay <= 2^8 and the rescale is rare;
+//   O += P.V  the probabilities, rounded to bf16, are the A operand of the next
+//             MFMA (heads on M, keys on K) in the order the S^T accumulator holds
+//             them; the B operand (keys x value columns) comes from the same
+//             row-major tile through ds_read_b64_tr_b16 (transposing LDS read);
+//             half h accumulates value columns [256h, 256h+256) of its 32 heads
+//             in 128 registers per lane.
+// The row sum adds the bf16-rounded probabilities, so the output is an exact
 // convex combination of value rows up to fp32 accumulation.
 //
 // Split mode writes per-split (normalised output, lse) in fp32 to the workspace;
 // a combine kernel merges them with the log-sum-exp weights.
 // The fp32 kernel (small head dims) is plain VALU code.
+#include <cfloat>
 #include <cmath>
 
 #include "dsa_device.h"
@@ -54,7 +61,9 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // 5
 constexpr int kHeadsPerBlock = 128;
 constexpr int kMaxIdx = 2048;                   // selected keys per workgroup (LDS-staged)
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kRescaleSlack = 8.0f;             // base-2 units: P <= 2^8
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -68,29 +77,48 @@ __device__ __forceinline__ int acc_row(int r, int half) {
 
 struct MlaShared {
   float sx[kWaves][16][kWave];    // partial S^T exchange between the two d_qk halves
-  int idx[kMaxIdx];               // this workgroup's slice of the top-k row
+  int idx[kMaxIdx];               // this workgroup's slice of the top-k row (-1 -> row 0)
+  uint32_t vmask[kMaxIdx / kKT];  // per tile: bit j set = selected key j is valid
   int last;
 };
 
-// Issue the LDS-DMA loads of one tile (local tile number lt): wave-load j copies
-// LDS chunks [64j, 64j+64) of the padded tile; chunk c is (key c/73, 16-byte
-// piece c%73 of that key's latent row; piece 72 is the row pad and repeats piece
-// 71).  A -1 index loads row 0 (its scores are masked).
+// Per-lane part of the LDS-DMA of a tile: wave-load j = wave + 8u copies LDS
+// chunks [64j, 64j+64) of the padded tile; chunk c is (key c/73, 16-byte piece
+// c%73 of that key's latent row; piece 72 is the row pad and repeats piece 71).
+static_assert(kTileChunks <= 2400, "the c / 73 multiply-shift holds for c < 2400");
+
+struct DmaLane {
+  // (byte offset of the chunk in the latent row) << 16 | 4 * (key of the chunk)
+  int pk[kDmaPerWave];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < kDmaPerWave; ++u) {
+      const int c = (wave + kWaves * u) * kWave + lane;
+      const int k = (c * 1796) >> 17;  // c / 73 for c < 2400
+      const int cc = c - k * kRowChunks;
+      pk[u] = ((cc < kRowChunks - 1 ? cc : kRowChunks - 2) * 16) << 16 | (k < kKT ? k : 0) * 4;
+    }
+  }
+};
+
+// Issue the LDS-DMA loads of local tile lt (rows staged in sidx, -1 already
+// replaced by row 0, whose scores are masked).
 __device__ __forceinline__ void dma_tile(uint8_t* buf, const int* sidx, int lt,
                                          const uint8_t* __restrict__ kv, int wave, int lane) {
-  // keep the per-lane address arithmetic inside the loop: hoisted, it would be
-  // spilled, and the scratch reloads would wait on the DMA counter
+  // the per-lane pieces are recomputed here: held across the tile loop they
+  // would be spilled, and the scratch reloads would wait on the DMA counter
   asm volatile("" : "+v"(lane));
+  DmaLane d2;
+  d2.init(wave, lane);
 #pragma unroll
   for (int u = 0; u < kDmaPerWave; ++u) {
     const int j = wave + kWaves * u;
-    const int c = j * kWave + lane;
-    if (j < kDmaPerTile && c < kTileChunks) {
-      const int key = c / kRowChunks;
-      int cc = c - key * kRowChunks;
-      cc = cc < kRowChunks - 1 ? cc : kRowChunks - 2;
-      const int r = sidx[lt * kKT + key];
-      const uint8_t* src = kv + int64_t(r < 0 ? 0 : r) * kRowBytes + cc * 16;
+    const bool last = j == kDmaPerTile - 1;   // the last wave-load covers 32 chunks
+    if (j < kDmaPerTile && (!last || lane < kTileChunks - (kDmaPerTile - 1) * kWave)) {
+      const int* ps = reinterpret_cast<const int*>(
+          reinterpret_cast<const uint8_t*>(sidx + lt * kKT) + (d2.pk[u] & 0xFFFF));
+      const uint32_t r = uint32_t(*ps);
+      const uint8_t* src = kv + (uint64_t(r) * kRowBytes + (uint32_t(d2.pk[u]) >> 16));
       __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(buf + j * kWave * 16), 16, 0, 0);
     }
   }
@@ -107,7 +135,7 @@ __shared__ __attribute__((aligned(16))) uint8_t g_kv1[kKT * kKvStride];
 template <int kBuf>
 __device__ __forceinline__ void mla_tile(MlaShared& sh, const bf16x8_t (&qf)[kQSteps],
                                          f32x16_t (&o)[kVTiles], float& m_run, float& l_run,
-                                         uint32_t vmask, float sm_scale, int wave, int lane) {
+                                         uint32_t vmask, float scale2, int wave, int lane) {
   const uint8_t* buf = kBuf == 0 ? g_kv0 : g_kv1;
   const int half = lane >> 5;
   const int hs = wave >> 2;
@@ -125,20 +153,30 @@ __device__ __forceinline__ void mla_tile(MlaShared& sh, const bf16x8_t (&qf)[kQS
   // full __syncthreads would also wait for the in-flight LDS-DMA of the next tile)
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
-  float mt = -INFINITY;
-  const uint32_t mv = vmask >> (4 * half);  // bit 8*(r/4) + r%4 = key of register r
+  // full S (both halves add the same two partials: IEEE addition commutes, so
+  // the two waves hold identical bits), in base-2 logit units
+  const float* other = &sh.sx[wave ^ 4][0][lane];
+  // key validity as per-register lane masks built on the scalar unit: register
+  // r holds key 8*(r/4) + r%4 in lanes 0..31 and that key + 4 in lanes 32..63
+  const float neg_inf = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float other = sh.sx[wave ^ 4][r][lane];
-    const float full = hs == 0 ? s[r] + other : other + s[r];  // same bits in both halves
-    s[r] = ((mv >> (8 * (r >> 2) + (r & 3))) & 1u) ? full * sm_scale : -INFINITY;
-    mt = fmaxf(mt, s[r]);
+    const int kr = 8 * (r >> 2) + (r & 3);
+    const uint64_t lm = (((vmask >> kr) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
+                        (((vmask >> (kr + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+    const float x = (s[r] + other[r * kWave]) * scale2;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(s[r]) : "v"(neg_inf), "v"(x), "s"(lm));
   }
+  float mt = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
   mt = fmaxf(mt, __shfl_xor(mt, 32));
+  // m_run starts at -FLT_MAX (finite), so exp2(s - m_run) is 0 for masked keys
+  // and the first tile with a finite logit always moves it (alpha = 0, O = 0)
   const bool grow = mt > m_run + kRescaleSlack;
   if (__ballot(grow) != 0ull) {
     const float m_new = grow ? mt : m_run;
-    const float alpha = grow ? (m_run == -INFINITY ? 0.0f : __expf(m_run - m_new)) : 1.0f;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
     m_run = m_new;
 #pragma unroll
@@ -148,16 +186,24 @@ __device__ __forceinline__ void mla_tile(MlaShared& sh, const bf16x8_t (&qf)[kQS
       for (int n = 0; n < kVTiles; ++n) o[n][r] *= ar;
     }
   }
+  // P = 2^(S - m) rounded to bf16 (v_cvt_pk_bf16_f32, round to nearest even); the
+  // row sum adds the rounded values (v_dot2 with ones), so the output is an exact
+  // convex combination of value rows up to fp32 accumulation
   bf16x8_t p0, p1;
   float ps = 0.0f;
+  const bf16x2_t ones = {__bf16(1.0f), __bf16(1.0f)};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = s[r] == -INFINITY ? 0.0f : __expf(s[r] - m_run);
-    const uint16_t pb = f32_to_bf16_bits(p);
-    ps += bf16_bits_to_f32(pb);
-    const __bf16 pv = __builtin_bit_cast(__bf16, pb);
-    if (r < 8) p0[r] = pv;
-    else p1[r - 8] = pv;
+  for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
+#pragma unroll
+  for (int r = 0; r < 8; r += 2) {
+    const bf16x2_t a = {__bf16(s[r]), __bf16(s[r + 1])};
+    const bf16x2_t b = {__bf16(s[r + 8]), __bf16(s[r + 9])};
+    ps = __builtin_amdgcn_fdot2_f32_bf16(a, ones, ps, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(b, ones, ps, false);
+    p0[r] = a[0];
+    p0[r + 1] = a[1];
+    p1[r] = b[0];
+    p1[r + 1] = b[1];
   }
   l_run += ps;
 
@@ -204,6 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   const bool hvalid = head < H;
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
 
+  const float scale2 = sm_scale * kLog2e;
   const int ntiles = (K + kKT - 1) / kKT;
   const int i0 = int(int64_t(ntiles) * blockIdx.z / nsplit);
   int i1 = int(int64_t(ntiles) * (blockIdx.z + 1) / nsplit);
@@ -220,7 +267,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     for (int x = tid; x < (i1 - i0) * kKT; x += kThreads) {
       const int j = jbase + x;
       const int r = j < K ? irow[j] : -1;
-      sh.idx[x] = r;
+      sh.idx[x] = r < 0 ? 0 : r;
+      const uint64_t b = __ballot(r >= 0);   // x advances by whole waves: 2 tiles per ballot
+      if (lane == 0) sh.vmask[x / kKT] = uint32_t(b);
+      if (lane == 32) sh.vmask[x / kKT] = uint32_t(b >> 32);
       if (r >= 0) last = x;
     }
     if (last >= 0) atomicMax(&sh.last, last);
@@ -246,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   f32x16_t o[kVTiles];
 #pragma unroll
   for (int n = 0; n < kVTiles; ++n) o[n] = f32x16_t{};
-  float m_run = -INFINITY;  // per head (lane column), same in both lane halves
+  float m_run = -FLT_MAX;   // per head (lane column, base-2 units), same in both lane halves
   float l_run = 0.0f;       // per head, partial over this lane half's keys
 
   for (int lt = 0; lt < nt; lt += 2) {
@@ -254,21 +304,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (lt + 1 < nt) dma_tile(g_kv1, sh.idx, lt + 1, kvb, wave, lane);
-    mla_tile<0>(sh, qf, o, m_run, l_run, uint32_t(__ballot(sh.idx[lt * kKT + (lane & 31)] >= 0)),
-                sm_scale, wave, lane);
+    mla_tile<0>(sh, qf, o, m_run, l_run, sh.vmask[lt],
+                scale2, wave, lane);
     if (lt + 1 >= nt) break;
     // tile lt+1 (buffer 1)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (lt + 2 < nt) dma_tile(g_kv0, sh.idx, lt + 2, kvb, wave, lane);
     mla_tile<1>(sh, qf, o, m_run, l_run,
-                uint32_t(__ballot(sh.idx[(lt + 1) * kKT + (lane & 31)] >= 0)), sm_scale, wave, lane);
+                sh.vmask[lt + 1], scale2, wave, lane);
   }
 
   // epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_h = l_tot > 0.0f ? m_run + __logf(l_tot) : -INFINITY;
+  const float lse_h = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   const int col0 = hs * kVTiles * 32 + (lane & 31);
   if (nsplit == 1) {
     if (lse && half == 0 && hs == 0 && hvalid) lse[t * H + head] = lse_h;
