@@ -9,30 +9,32 @@
 //   lse[t,h]   = log sum_j exp(sm_scale * q[t,h,:] . kv[J_j,:])
 // over J = the entries of topk_idx[t] that are not -1.
 //
-// bf16 kernel: one workgroup = one query x 128 heads, 8 waves = 4 head groups of
-// 32 heads x 2 halves; or a slice of the query's selected keys when the key list
-// is split (few queries: decode).  Per tile of 32 selected keys:
+// bf16 kernel: one workgroup = one query x 128 heads, 4 waves (one per SIMD)
+// of 32 heads each; or a slice of the query's selected keys when the key list
+// is split (few queries: decode).  A wave keeps its Q^T [576 x 32 heads] in 144
+// VGPRs and its O [32 heads x 512] in the 256 accumulation registers for the
+// whole query, so no partial result crosses waves.  Per tile of 32 selected
+// keys:
 //   gather    LDS-DMA (global_load_lds, 16 bytes per lane) of the 32 latent rows
 //             into a row-major LDS tile whose rows are padded to 1168 bytes
-//             (conflict-free 16-byte fragment reads); the next tile's gather is
-//             in flight while this one is computed (two LDS buffers);
+//             (conflict-free 16-byte fragment reads); four tile buffers, the
+//             gather of tile i+2 is issued while tile i is computed;
 //   S^T=K.Q^T v_mfma_f32_32x32x16_bf16 with keys on M and the wave's 32 heads on
-//             N; half h of a head group contracts dims [288h, 288h+288) with its
-//             Q^T half held in registers for the whole query, and the two fp32
-//             partials are added through LDS (both waves then hold the same S);
-//   softmax   fp32 in base-2 units (sm_scale * log2 e folded into one multiply);
-//             lane l holds 16 keys of head l%32, so the max over keys is in-lane
-//             plus one exchange with lane l^32; the running max only moves (and
-//             the output is rescaled) when a tile's max exceeds it by more than
-//             8, so the probabilities stay <= 2^8 and the rescale is rare;
-//   O += P.V  the probabilities, rounded to bf16, are the A operand of the next
-//             MFMA (heads on M, keys on K) in the order the S^T accumulator holds
-//             them; the B operand (keys x value columns) comes from the same
-//             row-major tile through ds_read_b64_tr_b16 (transposing LDS read);
-//             half h accumulates value columns [256h, 256h+256) of its 32 heads
-//             in 128 registers per lane.
-// The row sum adds the bf16-rounded probabilities, so the output is an exact
-// convex combination of value rows up to fp32 accumulation.
+//             N, 36 K-steps; lane l then holds 16 keys of head l%32;
+//   softmax   fp32 in base-2 units (sm_scale * log2 e folded into one multiply)
+//             against a fixed per-head reference: the max of the head's first
+//             tile with a finite logit.  P = 2^(S - m_ref) <= 2^32 unless a later
+//             tile exceeds m_ref + 32, in which case the workgroup runs the
+//             query a second time with m_ref = the true max (known by then), so
+//             O is never rescaled inside the loop;
+//   O += P.V  the probabilities, rounded to bf16, are the A operand (heads on M,
+//             keys on K) in the order the S^T accumulator holds them; the B
+//             operand (keys x value columns) comes from the same row-major tile
+//             through ds_read_b64_tr_b16 (transposing LDS read).
+// The P.V of tile i-1 runs while the softmax of tile i is computed (its VALU
+// work sits between those MFMAs), and the gather of tile i+2 is issued between
+// the MFMAs of S(i).  The row sum adds the bf16-rounded probabilities, so the
+// output is an exact convex combination of value rows up to fp32 accumulation.
 //
 // Split mode writes per-split (normalised output, lse) in fp32 to the workspace;
 // a combine kernel merges them with the log-sum-exp weights.
@@ -54,14 +56,16 @@ constexpr int kRowChunks = kRowBytes / 16 + 1;  // 73: one pad chunk per LDS row
 constexpr int kKvStride = kRowChunks * 16;      // 1168: padded LDS row
 constexpr int kTileChunks = kKT * kRowChunks;   // 2336
 constexpr int kDmaPerTile = (kTileChunks + kWave - 1) / kWave;  // 37 wave loads of 1 KB
-constexpr int kQSteps = kDqk / 16 / 2;          // 18 K-steps per wave (half of d_qk)
-constexpr int kVTiles = kDv / 32 / 2;           // 8 value tiles per wave (half of d_v)
-constexpr int kThreads = 512;                   // 8 waves: 4 head groups x 2 halves
+constexpr int kQSteps = kDqk / 16;              // 36 K-steps of 16 dims
+constexpr int kVTiles = kDv / 32;               // 16 value tiles of 32 columns
+constexpr int kThreads = 256;                   // 4 waves x 32 heads
 constexpr int kWaves = kThreads / kWave;
-constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // 5
-constexpr int kHeadsPerBlock = 128;
+constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // 10 (wave 0), else 9
+constexpr int kHeadsPerBlock = kWaves * 32;     // 128
 constexpr int kMaxIdx = 2048;                   // selected keys per workgroup (LDS-staged)
-constexpr float kRescaleSlack = 8.0f;             // base-2 units: P <= 2^8
+constexpr int kMaxTiles = kMaxIdx / kKT;
+constexpr int kRing = 3;                      // LDS fragment reads in flight ahead of the MFMAs
+constexpr float kSpan = 32.0f;                 // base-2 units: P <= 2^32 before a second pass
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -76,161 +80,324 @@ __device__ __forceinline__ int acc_row(int r, int half) {
 }
 
 struct MlaShared {
-  float sx[kWaves][16][kWave];    // partial S^T exchange between the two d_qk halves
-  int idx[kMaxIdx];               // this workgroup's slice of the top-k row (-1 -> row 0)
-  uint32_t vmask[kMaxIdx / kKT];  // per tile: bit j set = selected key j is valid
+  int idx[kMaxIdx + 3 * kKT];     // this workgroup's slice of the top-k row (-1 -> row 0),
+                                  // plus up to 3 padding tiles
+  uint32_t vmask[kMaxTiles + 3];  // per tile: bit j set = selected key j is valid
   int last;
+  int redo[2];                    // per pass: some head needs the second pass
 };
 
-// Per-lane part of the LDS-DMA of a tile: wave-load j = wave + 8u copies LDS
-// chunks [64j, 64j+64) of the padded tile; chunk c is (key c/73, 16-byte piece
-// c%73 of that key's latent row; piece 72 is the row pad and repeats piece 71).
-static_assert(kTileChunks <= 2400, "the c / 73 multiply-shift holds for c < 2400");
-
-struct DmaLane {
-  // (byte offset of the chunk in the latent row) << 16 | 4 * (key of the chunk)
-  int pk[kDmaPerWave];
-  __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) {
-      const int c = (wave + kWaves * u) * kWave + lane;
-      const int k = (c * 1796) >> 17;  // c / 73 for c < 2400
-      const int cc = c - k * kRowChunks;
-      pk[u] = ((cc < kRowChunks - 1 ? cc : kRowChunks - 2) * 16) << 16 | (k < kKT ? k : 0) * 4;
-    }
-  }
-};
-
-// Issue the LDS-DMA loads of local tile lt (rows staged in sidx, -1 already
-// replaced by row 0, whose scores are masked).
-__device__ __forceinline__ void dma_tile(uint8_t* buf, const int* sidx, int lt,
-                                         const uint8_t* __restrict__ kv, int wave, int lane) {
-  // the per-lane pieces are recomputed here: held across the tile loop they
-  // would be spilled, and the scratch reloads would wait on the DMA counter
-  asm volatile("" : "+v"(lane));
-  DmaLane d2;
-  d2.init(wave, lane);
-#pragma unroll
-  for (int u = 0; u < kDmaPerWave; ++u) {
-    const int j = wave + kWaves * u;
-    const bool last = j == kDmaPerTile - 1;   // the last wave-load covers 32 chunks
-    if (j < kDmaPerTile && (!last || lane < kTileChunks - (kDmaPerTile - 1) * kWave)) {
-      const int* ps = reinterpret_cast<const int*>(
-          reinterpret_cast<const uint8_t*>(sidx + lt * kKT) + (d2.pk[u] & 0xFFFF));
-      const uint32_t r = uint32_t(*ps);
-      const uint8_t* src = kv + (uint64_t(r) * kRowBytes + (uint32_t(d2.pk[u]) >> 16));
-      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(buf + j * kWave * 16), 16, 0, 0);
-    }
-  }
-}
-
-// One workgroup: one query, 128 heads.  Wave w: head group g = w & 3 (32 heads),
-// half h = w >> 2.  Half h computes the partial S^T over dims [288h, 288h+288),
-// the two partials are added through LDS (both waves then hold the same S and run
-// the same softmax), and half h accumulates output columns [256h, 256h+256).
-// Everything lives in VGPRs (Q^T half: 72, O half: 128 per lane).
+// Four KV tile buffers, separate LDS objects so that every access names its
+// buffer statically: the compiler then knows that reads of one buffer do not
+// wait for the LDS-DMA still writing another.  Tile i lives in buffer i % 4;
+// while tile i is computed, tile i-1 is still read (P.V) and tiles i+1, i+2
+// are in flight.
 __shared__ __attribute__((aligned(16))) uint8_t g_kv0[kKT * kKvStride];
 __shared__ __attribute__((aligned(16))) uint8_t g_kv1[kKT * kKvStride];
+__shared__ __attribute__((aligned(16))) uint8_t g_kv2[kKT * kKvStride];
+__shared__ __attribute__((aligned(16))) uint8_t g_kv3[kKT * kKvStride];
 
-template <int kBuf>
-__device__ __forceinline__ void mla_tile(MlaShared& sh, const bf16x8_t (&qf)[kQSteps],
-                                         f32x16_t (&o)[kVTiles], float& m_run, float& l_run,
-                                         uint32_t vmask, float scale2, int wave, int lane) {
-  const uint8_t* buf = kBuf == 0 ? g_kv0 : g_kv1;
-  const int half = lane >> 5;
-  const int hs = wave >> 2;
+template <int B>
+__device__ __forceinline__ uint8_t* kvbuf() {
+  return B == 0 ? g_kv0 : B == 1 ? g_kv1 : B == 2 ? g_kv2 : g_kv3;
+}
 
-  // partial S^T = K . Q^T over this wave's half of d_qk (keys on M, heads on N)
-  f32x16_t s = f32x16_t{};
-  const uint8_t* ka = buf + (lane & 31) * kKvStride + hs * kDqk + half * 16;
+
+// MFMA issued through inline asm, so that each accumulator gets the register
+// file it needs: S (16 per lane) in arch VGPRs, O (256 per lane) in the
+// accumulation registers.  (With the builtin every MFMA of a kernel takes the
+// same form, and S + O do not fit in the 256 accumulation registers.)  The
+// compiler does not see into the asm, so the MFMA data hazards it would
+// otherwise cover are covered here, with the counts it emits for the builtin on
+// gfx950: a VALU write feeding an MFMA operand needs 1 wait state, an MFMA
+// result read by a VALU (or accumulation-register move) needs 12, and chained
+// accumulation (srcC = previous dst) needs none.
+__device__ __forceinline__ void mfma_v0(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// last MFMA of a chain whose result the VALU reads next
+__device__ __forceinline__ void mfma_v_last(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3"
+      : "+v"(d) : "v"(a), "v"(b));
+}
+// accumulation into O; the leading nops cover a VALU-written operand
+// (P, a repacked V fragment, or a rescaled O)
+__device__ __forceinline__ void mfma_a(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// before the VALU touches O after MFMAs into it
+__device__ __forceinline__ void o_fence(f32x16_t (&o)[kVTiles]) {
+  asm volatile("s_nop 7\n\ts_nop 3"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                 "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                 "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+}
+
+static_assert(kTileChunks <= 2400, "the c / 73 multiply-shift holds for c < 2400");
+
+// LDS-DMA of a tile: wave-load j = wave + 4u copies LDS chunks [64j, 64j+64) of
+// the padded tile; chunk c is (key c/73, 16-byte piece c%73 of that key's latent
+// row; piece 72 is the row pad and repeats piece 71).  sidx holds the staged rows
+// with -1 replaced by row 0 (masked later).  Wave 0 issues 10 loads per tile
+// (the 37th covers 32 chunks), the other waves 9.
+__device__ __forceinline__ int dma_key(int c) {
+  const int k = (c * 1796) >> 17;  // c / 73
+  return k < kKT ? k : kKT - 1;
+}
+
+// rows of this lane's chunks for tile lt (read from the staged slice)
+__device__ __forceinline__ void dma_rows(const int* sidx, int lt, int wave, int lane,
+                                         uint32_t (&row)[kDmaPerWave]) {
+  // the per-lane pieces are recomputed for every tile: held across the tile
+  // loop they would take registers the loop needs
+  asm volatile("" : "+v"(lane));
 #pragma unroll
-  for (int st = 0; st < kQSteps; ++st)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(ka + st * 32),
-                                                qf[st], s, 0, 0, 0);
+  for (int u = 0; u < kDmaPerWave; ++u)
+    row[u] = uint32_t(sidx[lt * kKT + dma_key((wave + kWaves * u) * kWave + lane)]);
+}
+
+// issue wave-load u of the tile into buffer B
+template <int B>
+__device__ __forceinline__ void dma_issue(int u, uint32_t row, const uint8_t* __restrict__ kv,
+                                          int wave, int lane) {
+  static_assert(kDmaPerTile == kWaves * (kDmaPerWave - 1) + 1, "load split");
+  // loads u < 9 are full for every wave; load 9 is wave 0's 37th (32 chunks)
+  if (u == kDmaPerWave - 1 && !(wave == 0 && lane < kTileChunks - (kDmaPerTile - 1) * kWave))
+    return;
+  asm volatile("" : "+v"(lane));  // recomputed here, not held in registers
+  const int j = wave + kWaves * u;
+  const int c = j * kWave + lane;
+  int cc = c - dma_key(c) * kRowChunks;
+  cc = cc < kRowChunks - 1 ? cc : kRowChunks - 2;
+  const uint8_t* src = kv + (uint64_t(row) * kRowBytes + uint32_t(cc * 16));
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(kvbuf<B>() + j * kWave * 16), 16, 0, 0);
+}
+
+template <int B>
+__device__ __forceinline__ void dma_tile(const int* sidx, int lt, const uint8_t* __restrict__ kv,
+                                         int wave, int lane) {
+  uint32_t row[kDmaPerWave];
+  dma_rows(sidx, lt, wave, lane, row);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sh.sx[wave][r][lane] = s[r];
-  // LDS-only exchange: wait for this wave's LDS writes, then a plain barrier (a
-  // full __syncthreads would also wait for the in-flight LDS-DMA of the next tile)
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  // full S (both halves add the same two partials: IEEE addition commutes, so
-  // the two waves hold identical bits), in base-2 logit units
-  const float* other = &sh.sx[wave ^ 4][0][lane];
-  // key validity as per-register lane masks built on the scalar unit: register
-  // r holds key 8*(r/4) + r%4 in lanes 0..31 and that key + 4 in lanes 32..63
-  const float neg_inf = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kr = 8 * (r >> 2) + (r & 3);
-    const uint64_t lm = (((vmask >> kr) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
-                        (((vmask >> (kr + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
-    const float x = (s[r] + other[r * kWave]) * scale2;
-    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(s[r]) : "v"(neg_inf), "v"(x), "s"(lm));
+  for (int u = 0; u < kDmaPerWave; ++u) dma_issue<B>(u, row[u], kv, wave, lane);
+}
+
+// Wait until this wave's LDS-DMA of the current tile has landed.  The next
+// tile's loads (issued one tile later, vector-memory counters retire in order)
+// may stay in flight: wave 0 issues 10 loads per tile, the others 9.
+__device__ __forceinline__ void wait_tile(bool next_in_flight, int wave) {
+  if (!next_in_flight) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  } else if (wave == 0) {
+    __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
   }
-  float mt = s[0];
+  static_assert(kDmaPerWave == 10 && (kDmaPerTile - 1) % kWaves == 0, "vmcnt immediates");
+}
+
+// S^T = K . Q^T for the tile in buffer B: keys on M, the wave's 32 heads on N,
+// 36 K-steps of 16 dims.  Lane l reads key l%32, dims 16*st + 8*(l/32) .. +8;
+// the fragment reads run kRing steps ahead of their MFMA.  With kDma, the
+// LDS-DMA loads of a later tile (into buffer BD) are issued between the MFMAs
+// (the wave can issue them while the matrix core works).
+template <int B, int BD, bool kDma>
+__device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], int lane,
+                                            const uint32_t (&row)[kDmaPerWave],
+                                            const uint8_t* __restrict__ kv, int wave) {
+  const uint8_t* ka = kvbuf<B>() + (lane & 31) * kKvStride + (lane >> 5) * 16;
+  bf16x8_t fr[kRing];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  // m_run starts at -FLT_MAX (finite), so exp2(s - m_run) is 0 for masked keys
-  // and the first tile with a finite logit always moves it (alpha = 0, O = 0)
-  const bool grow = mt > m_run + kRescaleSlack;
-  if (__ballot(grow) != 0ull) {
-    const float m_new = grow ? mt : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-    m_run = m_new;
+  for (int st = 0; st < kRing; ++st) fr[st] = *reinterpret_cast<const bf16x8_t*>(ka + st * 32);
+  f32x16_t s;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float ar = __shfl(alpha, acc_row(r, half));
+  for (int st = 0; st < kQSteps; ++st) {
+    const bf16x8_t a = fr[st % kRing];
+    if (st + kRing < kQSteps)
+      fr[st % kRing] = *reinterpret_cast<const bf16x8_t*>(ka + (st + kRing) * 32);
+    if (st == 0) mfma_v0(s, a, qf[st]);
+    else if (st + 1 < kQSteps) mfma_v(s, a, qf[st]);
+    else mfma_v_last(s, a, qf[st]);
+    if constexpr (kDma) {
+      if (st % 3 == 1 && st / 3 < kDmaPerWave) dma_issue<BD>(st / 3, row[st / 3], kv, wave, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep this order
+  }
+  return s;
+}
+
+// Softmax of one tile against a fixed per-head reference m_ref (base-2 units,
+// same in both lane halves): P = 2^(S - m_ref).  m_ref is the max of the first
+// tile that has a finite logit for the head, so P <= 2^kSpan unless a later
+// tile's max exceeds m_ref + kSpan; that sets `over` and the query is computed
+// again with m_ref = the true max (m_max tracks it).  O is never rescaled
+// inside the loop.  The work is cut into kSmStages stages that the P.V of the
+// previous tile interleaves with its MFMAs.
+struct Softmax {
+  f32x16_t s;      // S^T of the tile: lane = head l%32, 16 keys
+  uint32_t vmask;  // valid keys of the tile
+  float mt;
+  float ps;
+  bf16x8_t p0, p1;
+
+  template <int K>
+  __device__ __forceinline__ void stage(float scale2, float& m_ref, float& m_max, bool& over,
+                                        float& l_run) {
+    if constexpr (K < 4) {
+      // key validity as per-register lane masks built on the scalar unit:
+      // register r holds key 8*(r/4) + r%4 in lanes 0..31 and that key + 4 in
+      // lanes 32..63
+      const float neg_inf = -INFINITY;
 #pragma unroll
-      for (int n = 0; n < kVTiles; ++n) o[n][r] *= ar;
+      for (int r = 4 * K; r < 4 * K + 4; ++r) {
+        const int kr = 8 * (r >> 2) + (r & 3);
+        const uint64_t lm = (((vmask >> kr) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
+                            (((vmask >> (kr + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+        const float x = s[r] * scale2;
+        asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(s[r]) : "v"(neg_inf), "v"(x), "s"(lm));
+      }
+    } else if constexpr (K == 4) {
+      mt = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    } else if constexpr (K == 5) {
+      // lanes l and l^32 hold the two key halves of head l%32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      // -FLT_MAX = no finite logit yet (an all-masked tile keeps it)
+      m_ref = m_ref == -FLT_MAX ? fmaxf(mt, -FLT_MAX) : m_ref;
+      m_max = fmaxf(m_max, mt);
+      over = over || mt > m_ref + kSpan;
+    } else if constexpr (K < 10) {
+#pragma unroll
+      for (int r = 4 * (K - 6); r < 4 * (K - 6) + 4; ++r)
+        s[r] = __builtin_amdgcn_exp2f(s[r] - m_ref);
+    } else {
+      // P rounded to bf16 (v_cvt_pk_bf16_f32, round to nearest even); the row
+      // sum adds the rounded values (v_dot2 with ones), so the output is an
+      // exact convex combination of value rows up to fp32 accumulation
+      const bf16x2_t ones = {__bf16(1.0f), __bf16(1.0f)};
+      if constexpr (K == 10) ps = 0.0f;
+#pragma unroll
+      for (int r = 4 * (K - 10); r < 4 * (K - 10) + 4; r += 2) {
+        const bf16x2_t a = {__bf16(s[r]), __bf16(s[r + 1])};
+        const bf16x2_t b = {__bf16(s[r + 8]), __bf16(s[r + 9])};
+        ps = __builtin_amdgcn_fdot2_f32_bf16(a, ones, ps, false);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(b, ones, ps, false);
+        p0[r] = a[0];
+        p0[r + 1] = a[1];
+        p1[r] = b[0];
+        p1[r + 1] = b[1];
+      }
+      if constexpr (K == 11) l_run += ps;
     }
   }
-  // P = 2^(S - m) rounded to bf16 (v_cvt_pk_bf16_f32, round to nearest even); the
-  // row sum adds the rounded values (v_dot2 with ones), so the output is an exact
-  // convex combination of value rows up to fp32 accumulation
-  bf16x8_t p0, p1;
-  float ps = 0.0f;
-  const bf16x2_t ones = {__bf16(1.0f), __bf16(1.0f)};
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
-#pragma unroll
-  for (int r = 0; r < 8; r += 2) {
-    const bf16x2_t a = {__bf16(s[r]), __bf16(s[r + 1])};
-    const bf16x2_t b = {__bf16(s[r + 8]), __bf16(s[r + 9])};
-    ps = __builtin_amdgcn_fdot2_f32_bf16(a, ones, ps, false);
-    ps = __builtin_amdgcn_fdot2_f32_bf16(b, ones, ps, false);
-    p0[r] = a[0];
-    p0[r + 1] = a[1];
-    p1[r] = b[0];
-    p1[r + 1] = b[1];
-  }
-  l_run += ps;
+};
+constexpr int kSmStages = 12;
 
-  // O[:, 256*hs .. +256] += P . V.  The B operand (8 keys x 1 value column per
-  // lane) is read from the row-major tile with ds_read_b64_tr_b16: in each group
-  // of 16 lanes, lane 4m+q reads 4 value columns of key row k0+m and the
-  // transpose hands lane i the 4 keys k0..k0+3 of column n0+i.  Lane half h
-  // needs keys {4h..4h+3} (first read) and {8+4h..8+4h+3} (second read) of each
-  // 16-key step, the order in which P sits in the S^T accumulator.
+template <int K>
+__device__ __forceinline__ void sm_stage_if(int k, Softmax& sm, float scale2, float& m_ref,
+                                            float& m_max, bool& over, float& l_run) {
+  if (k == K) sm.template stage<K>(scale2, m_ref, m_max, over, l_run);
+}
+
+__device__ __forceinline__ void sm_stage(int k, Softmax& sm, float scale2, float& m_ref,
+                                         float& m_max, bool& over, float& l_run) {
+  sm_stage_if<0>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<1>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<2>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<3>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<4>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<5>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<6>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<7>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<8>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<9>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<10>(k, sm, scale2, m_ref, m_max, over, l_run);
+  sm_stage_if<11>(k, sm, scale2, m_ref, m_max, over, l_run);
+}
+
+__device__ __forceinline__ void softmax_all(Softmax& sm, float scale2, float& m_ref,
+                                            float& m_max, bool& over, float& l_run) {
+#pragma unroll
+  for (int k = 0; k < kSmStages; ++k) sm_stage(k, sm, scale2, m_ref, m_max, over, l_run);
+}
+
+// O += P . V for the tile in buffer B (B < 0: the buffer `buf` chosen at run
+// time).  The B operand (8 keys x 1 value column per lane) is read from the
+// row-major tile with ds_read_b64_tr_b16: in each group of 16 lanes, lane 4m+q
+// reads 4 value columns of key row k0+m and the transpose hands lane i the 4
+// keys k0..k0+3 of column n0+i.  Lane half h needs keys {4h..4h+3} (first read)
+// and {8+4h..8+4h+3} (second read) of each 16-key step: the order in which P
+// sits in the S^T accumulator.  With sm, the softmax stages of the current tile
+// are interleaved with the MFMAs.
+template <int B, bool kSm>
+__device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_t p1,
+                                        f32x16_t (&o)[kVTiles], int lane, Softmax& sm,
+                                        float scale2, float& m_ref, float& m_max, bool& over,
+                                        float& l_run) {
+  const int half = lane >> 5;
   const int grp = lane >> 4;      // 16-lane group
   const int li = lane & 15;
   const int n0 = 16 * (grp & 1);  // value column offset of the group inside a 32-wide tile
-  const uint8_t* vb = buf + (li >> 2) * kKvStride + (hs * kVTiles * 32 + n0 + 4 * (li & 3)) * 2;
+  const uint8_t* vb = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) + (li >> 2) * kKvStride +
+                      (n0 + 4 * (li & 3)) * 2 + 4 * half * kKvStride;
+  // step m = 2n + ks: value tile n, key step ks; reads run kRing steps ahead
+  auto rd = [&](int m) {
+    const uint8_t* base = vb + 16 * (m & 1) * kKvStride + (m >> 1) * 64;
+    const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
+    const v4i16_t b =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kKvStride));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8_t fr[kRing];
 #pragma unroll
-  for (int n = 0; n < kVTiles; ++n) {
+  for (int m = 0; m < kRing; ++m) fr[m] = rd(m);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint8_t* base = vb + (16 * ks + 4 * half) * kKvStride + n * 64;
-      const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
-      const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kKvStride));
-      const bf16x8_t v = __builtin_bit_cast(
-          bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ks == 0 ? p0 : p1, v, o[n], 0, 0, 0);
+  for (int m = 0; m < 2 * kVTiles; ++m) {
+    const bf16x8_t v = fr[m % kRing];
+    if (m + kRing < 2 * kVTiles) fr[m % kRing] = rd(m + kRing);
+    mfma_a(o[m >> 1], (m & 1) == 0 ? p0 : p1, v);
+    if constexpr (kSm) {
+      if (m % 2 == 1 && m / 2 < kSmStages) sm_stage(m / 2, sm, scale2, m_ref, m_max, over, l_run);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep this order
   }
 }
 
+// One tile step i (buffer B = i % 4): wait for tile i, S(i) = K(i).Q^T with
+// the gather of tile i+2 issued between its MFMAs, then O += P(i-1).V(i-1) with
+// the softmax of S(i) issued between those MFMAs.
+template <int B>
+__device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const uint8_t* kvb,
+                                          const bf16x8_t (&qf)[kQSteps], f32x16_t (&o)[kVTiles],
+                                          bf16x8_t& p0, bf16x8_t& p1, float& m_ref,
+                                          float& m_max, bool& over, float& l_run, float scale2,
+                                          int wave, int lane) {
+  wait_tile(i + 1 < nt, wave);
+  __builtin_amdgcn_s_barrier();
+  Softmax sm;
+  sm.vmask = sh.vmask[i];
+  uint32_t row[kDmaPerWave];
+  if (i + 2 < nt) {
+    dma_rows(sh.idx, i + 2, wave, lane, row);
+    sm.s = qk_tile<B, (B + 2) & 3, true>(qf, lane, row, kvb, wave);
+  } else {
+    sm.s = qk_tile<B, 0, false>(qf, lane, row, kvb, wave);
+  }
+  pv_tile<(B + 3) & 3, true>(nullptr, p0, p1, o, lane, sm, scale2, m_ref, m_max, over, l_run);
+  p0 = sm.p0;
+  p1 = sm.p1;
+}
+
+// One workgroup: one query x 128 heads (wave w: heads 32w .. 32w+31 of the
+// block's head range), or one key slice of it in split mode.  The query's Q^T
+// stays in registers (144 per lane), O [32 heads x 512] in 256 accumulation
+// registers per lane.
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ idx, int H, int K, float sm_scale,
@@ -238,27 +405,27 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     float* __restrict__ part_lse, int nsplit) {
   __shared__ __attribute__((aligned(16))) MlaShared sh;
 
-  const int64_t t = blockIdx.x;
+  // longest rows first: in causal prefill the last queries select the most keys
+  const int64_t t = int64_t(gridDim.x) - 1 - blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int half = lane >> 5;
-  const int grp = wave & 3;
-  const int hs = wave >> 2;  // which half of d_qk (Q.K) and of d_v (P.V)
-  const int h0 = int(blockIdx.y) * kHeadsPerBlock + grp * 32;
+  const int h0 = int(blockIdx.y) * kHeadsPerBlock + wave * 32;
   const int head = h0 + (lane & 31);
   const bool hvalid = head < H;
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
-
   const float scale2 = sm_scale * kLog2e;
+
   const int ntiles = (K + kKT - 1) / kKT;
   const int i0 = int(int64_t(ntiles) * blockIdx.z / nsplit);
   int i1 = int(int64_t(ntiles) * (blockIdx.z + 1) / nsplit);
   const int32_t* irow = idx + t * K;
 
-  // Stage this workgroup's index slice in LDS (padded with -1 to whole tiles) and
-  // drop trailing tiles that hold only -1 padding (top-k rows are -1 padded at
-  // the end); padding elsewhere is masked per key.
+  // Stage this workgroup's index slice in LDS (padded with -1 to whole tiles,
+  // -1 stored as row 0) with per-tile validity masks, and drop trailing tiles
+  // that hold only -1 padding (top-k rows are -1 padded at the end); padding
+  // elsewhere is masked per key.
   {
     if (tid == 0) sh.last = -1;
     __syncthreads();
@@ -279,13 +446,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     i1 = last < 0 ? i0 : i0 + last / kKT + 1;
   }
   const int nt = i1 - i0;
-  if (nt > 0) dma_tile(g_kv0, sh.idx, 0, kvb, wave, lane);
+  // tiles are run in groups of four after tile 0: pad with masked tiles that
+  // gather row 0 (finite values: a masked key's P is 0, and 0 * V must stay 0)
+  const int nt4 = nt > 0 ? 1 + 4 * ((nt + 2) / 4) : 0;
+  for (int x = nt * kKT + tid; x < nt4 * kKT; x += kThreads) {
+    sh.idx[x] = 0;
+    if ((x & (kKT - 1)) == 0) sh.vmask[x / kKT] = 0u;
+  }
+  if (tid < 2) sh.redo[tid] = 0;
+  __syncthreads();
 
-  // Q^T fragments: lane holds q[t, head, 288*hs + 16*st + 8*half .. +8]
+  // Q^T fragments: lane holds q[t, head, 16*st + 8*half .. +8]
   bf16x8_t qf[kQSteps];
   {
-    const __bf16* qr =
-        q + (t * H + (hvalid ? head : 0)) * int64_t(kDqk) + (kDqk / 2) * hs + 8 * half;
+    const __bf16* qr = q + (t * H + (hvalid ? head : 0)) * int64_t(kDqk) + 8 * half;
 #pragma unroll
     for (int st = 0; st < kQSteps; ++st) {
       bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qr + 16 * st);
@@ -294,34 +468,64 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   }
 
   f32x16_t o[kVTiles];
+  float m_ref = -FLT_MAX;  // per head (lane column, base-2 units), same in both lane halves
+  float m_max = -FLT_MAX;
+  float l_run = 0.0f;      // per head, partial over this lane half's keys
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int n = 0; n < kVTiles; ++n) o[n] = f32x16_t{};
-  float m_run = -FLT_MAX;   // per head (lane column, base-2 units), same in both lane halves
-  float l_run = 0.0f;       // per head, partial over this lane half's keys
-
-  for (int lt = 0; lt < nt; lt += 2) {
-    // tile lt (buffer 0); the DMA of tile lt+1 into buffer 1 overlaps it
-    __builtin_amdgcn_s_waitcnt(0);
+    for (int n = 0; n < kVTiles; ++n) o[n] = f32x16_t{};
+    l_run = 0.0f;
+    bool over = false;
+    bf16x8_t p0 = bf16x8_t{}, p1 = bf16x8_t{};
+    if (nt4 > 0) dma_tile<0>(sh.idx, 0, kvb, wave, lane);
+    if (nt4 > 1) dma_tile<1>(sh.idx, 1, kvb, wave, lane);
+    if (nt4 > 0) {
+      // tile 0: no P.V yet
+      wait_tile(nt4 > 1, wave);
+      __builtin_amdgcn_s_barrier();
+      if (nt4 > 2) dma_tile<2>(sh.idx, 2, kvb, wave, lane);
+      {
+        Softmax sm;
+        sm.vmask = sh.vmask[0];
+        uint32_t row[kDmaPerWave];
+        sm.s = qk_tile<0, 0, false>(qf, lane, row, kvb, wave);
+        softmax_all(sm, scale2, m_ref, m_max, over, l_run);
+        p0 = sm.p0;
+        p1 = sm.p1;
+      }
+      // tiles 1 .. nt4-1 in groups of four (one exit: a loop left in the middle
+      // makes the register allocator copy O out of the accumulation registers)
+      for (int i = 1; i < nt4; i += 4) {
+        tile_step<1>(sh, i, nt4, kvb, qf, o, p0, p1, m_ref, m_max, over, l_run, scale2, wave, lane);
+        tile_step<2>(sh, i + 1, nt4, kvb, qf, o, p0, p1, m_ref, m_max, over, l_run, scale2, wave,
+                     lane);
+        tile_step<3>(sh, i + 2, nt4, kvb, qf, o, p0, p1, m_ref, m_max, over, l_run, scale2, wave,
+                     lane);
+        tile_step<0>(sh, i + 3, nt4, kvb, qf, o, p0, p1, m_ref, m_max, over, l_run, scale2, wave,
+                     lane);
+      }
+      // P.V of the last tile: no gather is in flight any more, so its buffer can
+      // be chosen at run time
+      const int lb = (nt4 - 1) & 3;
+      const uint8_t* buf = lb == 0 ? g_kv0 : lb == 1 ? g_kv1 : lb == 2 ? g_kv2 : g_kv3;
+      Softmax none;
+      pv_tile<-1, false>(buf, p0, p1, o, lane, none, scale2, m_ref, m_max, over, l_run);
+    }
+    o_fence(o);  // the last MFMAs into O finish before O is read or cleared
+    // the whole workgroup agrees on a second pass (its waves share barriers)
+    if (__ballot(over) != 0ull && lane == 0) sh.redo[pass] = 1;
     __syncthreads();
-    if (lt + 1 < nt) dma_tile(g_kv1, sh.idx, lt + 1, kvb, wave, lane);
-    mla_tile<0>(sh, qf, o, m_run, l_run, sh.vmask[lt],
-                scale2, wave, lane);
-    if (lt + 1 >= nt) break;
-    // tile lt+1 (buffer 1)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (lt + 2 < nt) dma_tile(g_kv0, sh.idx, lt + 2, kvb, wave, lane);
-    mla_tile<1>(sh, qf, o, m_run, l_run,
-                sh.vmask[lt + 1], scale2, wave, lane);
+    if (sh.redo[pass] == 0) break;
+    m_ref = fmaxf(m_max, -FLT_MAX);
   }
 
   // epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_h = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  const int col0 = hs * kVTiles * 32 + (lane & 31);
+  const float lse_h = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+  const int col0 = lane & 31;
   if (nsplit == 1) {
-    if (lse && half == 0 && hs == 0 && hvalid) lse[t * H + head] = lse_h;
+    if (lse && half == 0 && hvalid) lse[t * H + head] = lse_h;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hr = h0 + acc_row(r, half);
@@ -334,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     }
   } else {
     const int64_t slot = t * nsplit + blockIdx.z;
-    if (half == 0 && hs == 0 && hvalid) part_lse[slot * H + head] = lse_h;
+    if (half == 0 && hvalid) part_lse[slot * H + head] = lse_h;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hr = h0 + acc_row(r, half);
