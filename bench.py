@@ -110,11 +110,126 @@ def cpu_baseline(host_inputs, seconds: float = 20.0):
                       f"MLA in float64: {pairs} indexer pairs in {dt:.1f} s"}
 
 
+def stage_bench(args, dsa, synth, np, torch):
+    """Each stage of the path timed on its own on one of the other workloads (THD
+    varlen prefill, decode, fp8 64K prefill).  HBM-bound stages (all of decode,
+    and every standalone top-k) get a 1 GiB write between repetitions so that
+    their inputs are not served from the 256 MB last-level cache."""
+    dev = "cuda"
+    w = synth.WORKLOADS[args.workload]
+    lay = synth.layout(w)
+    i32 = lambda x: torch.from_numpy(np.asarray(x, np.int32)).to(dev)
+    inp = synth.device_inputs(w, dev, lay)
+    tdt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
+    rs, re = dsa.dsa_row_windows(i32(lay.cu_q), i32(lay.cu_k), lay.n_q)
+    q, k, wt, ks = dsa.dsa_indexer_prep(inp["q_raw"], inp["k_raw"], inp["w"], i32(lay.positions()),
+                                        i32(lay.key_positions()), tdt, w.rope_dim, w.rope_main_dim,
+                                        w.rope_theta)
+    mq = inp["mla_q"].to(torch.bfloat16)
+    mkv = inp["mla_kv"].to(torch.bfloat16)
+    del inp
+    K = w.index_topk
+    scores = torch.full((lay.n_q, lay.n_k), float("-inf"), dtype=torch.float32, device=dev)
+    idx = torch.empty((lay.n_q, K), dtype=torch.int32, device=dev)
+    out = torch.empty((lay.n_q, w.mla_heads, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((lay.n_q, w.mla_heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(dsa.sparse_mla_workspace(lay.n_q, w.mla_heads, w.d_qk, w.d_v, K, 1), 1),
+                     dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    hbm_bound = {"indexer": w.decode, "topk": True, "mla": w.decode}
+    fns = {
+        "indexer": lambda: dsa.dsa_indexer_scores(q, k, wt, rs, re, k_scale=ks, scores=scores),
+        "topk": lambda: dsa.dsa_topk(scores, rs, re, K, out=idx),
+        "mla": lambda: dsa.dsa_sparse_mla_fwd(mq, mkv, idx, w.sm_scale, w.d_v, out=out, lse=lse,
+                                              workspace=ws),
+    }
+    ms = {}
+    for name in ("indexer", "topk", "mla"):
+        f = fns[name]
+        for _ in range(args.warmup):
+            f()
+        times = []
+        for _ in range(args.steps):
+            if hbm_bound[name]:
+                flush.fill_(float(len(times)))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms[name] = float(np.median([a.elapsed_time(b) for a, b in times]))
+    rs_h, re_h = rs.cpu().numpy().astype(np.int64), re.cpu().numpy().astype(np.int64)
+    pairs = int((re_h - rs_h).sum())
+    sel = int((idx >= 0).sum().item())
+    hd = w.n_heads * w.head_dim
+    elt = 1 if w.dtype == "fp8" else 2
+    idx_flop = pairs * 2 * hd
+    idx_bytes = lay.n_q * hd * elt + lay.n_k * w.head_dim * elt + lay.n_q * w.n_heads * 4 + pairs * 4
+    topk_bytes = pairs * 4 + lay.n_q * K * 4
+    mla_flop = sel * MLA_FLOP_PER_PAIR
+    gather = sel * w.d_qk * 2
+    mla_compulsory = mq.numel() * 2 + out.numel() * 2 + lse.numel() * 4 + idx.numel() * 4
+    mfma_peak = FP8_PEAK_TFLOPS if w.dtype == "fp8" else BF16_PEAK_TFLOPS
+    t = {n: v * 1e-3 for n, v in ms.items()}
+    comp = {
+        "indexer": {"ms": ms["indexer"], "pairs_per_s": pairs / t["indexer"],
+                    "tflops": idx_flop / t["indexer"] / 1e12,
+                    "frac_mfma_peak": idx_flop / t["indexer"] / 1e12 / mfma_peak,
+                    "gbs": idx_bytes / t["indexer"] / 1e9,
+                    "frac_hbm": idx_bytes / t["indexer"] / 1e9 / HBM_PEAK_GBS},
+        "topk": {"ms": ms["topk"], "rows_per_s": lay.n_q / t["topk"],
+                 "gbs": topk_bytes / t["topk"] / 1e9,
+                 "frac_hbm": topk_bytes / t["topk"] / 1e9 / HBM_PEAK_GBS},
+        "mla": {"ms": ms["mla"], "tflops": mla_flop / t["mla"] / 1e12,
+                "frac_bf16_peak": mla_flop / t["mla"] / 1e12 / BF16_PEAK_TFLOPS,
+                "gather_gbs": (gather + mla_compulsory) / t["mla"] / 1e9,
+                "frac_hbm": (gather + mla_compulsory) / t["mla"] / 1e9 / HBM_PEAK_GBS},
+    }
+    dom = max(ms, key=ms.get)
+    if dom == "indexer" and not w.decode:
+        ach = comp["indexer"]["tflops"]
+        roof = {"kernel": "indexer_rows_kernel", "bound": "mfma", "achieved": ach, "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": ach / mfma_peak, "traffic": None}
+    elif dom == "indexer":
+        ach = comp["indexer"]["gbs"]
+        roof = {"kernel": "indexer_rowsplit_kernel", "bound": "hbm", "achieved": ach,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    elif dom == "mla" and not w.decode:
+        ach = comp["mla"]["tflops"]
+        roof = {"kernel": "mla_bf16_kernel", "bound": "mfma", "achieved": ach,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                "traffic": None}
+    elif dom == "mla":
+        ach = comp["mla"]["gather_gbs"]
+        roof = {"kernel": "mla_bf16_kernel", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    else:
+        ach = comp["topk"]["gbs"]
+        roof = {"kernel": "topk_rows_kernel", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    total = sum(ms.values())
+    return {
+        "metric": "indexer q·k pairs/s + top-k rows/s + sparse-MLA TFLOP/s (per stage)",
+        "value": pairs / (total * 1e-3), "unit": "indexer pairs/s (sum of the stage medians)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": total,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: n_q={lay.n_q} n_k={lay.n_k} index {w.n_heads}x{w.head_dim} "
+                               f"{w.dtype}, index_topk {K}, sparse MLA {w.mla_heads} heads "
+                               f"{w.d_qk}/{w.d_v} bf16", "valid_pairs": pairs, "selected_pairs": sel,
+                   "parallelism": "none (1 GPU)"},
+        "components": comp, "roofline": roof,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill4k", choices=["prefill4k", "thd", "decode", "fp8_64k"],
+                    help="prefill4k: the benchmark step; the others time each stage on its own")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -139,6 +254,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload != "prefill4k":
+        print(json.dumps(stage_bench(args, dsa, synth, np, torch)), flush=True)
+        return
     w = synth.WORKLOADS["prefill4k"]
     lay = synth.layout(w)
     i32 = lambda x: torch.from_numpy(np.asarray(x, np.int32)).to(dev)
