@@ -158,7 +158,12 @@ int dsa_indexer_scores(const void* q, const void* k, const float* k_scale,
  *
  *   scores    f32 [n_q, ld_scores]; only in-window entries are read.
  *   topk_idx  int32 [n_q, index_topk], every entry written (global columns).
- *   workspace may be NULL when dsa_topk_workspace_size(...) returns 0.
+ *   workspace at least dsa_topk_workspace_size(...) bytes, 256-byte aligned, or
+ *             NULL when that size is 0.  It is nonzero for few rows over many
+ *             columns (n_q <= 1024, n_cols > 8192, index_topk <= 2048), where
+ *             each row's window is selected in up to 16 chunks whose candidates
+ *             (key, column) are merged: n_q * 16 * index_topk * 8 + n_q * 64
+ *             bytes.  Its contents on entry do not matter.
  * Bit-exact: the result is a function of the fp32 score bits only.
  * Supported: 1 <= index_topk <= 65536; windows within [0, n_cols].
  */

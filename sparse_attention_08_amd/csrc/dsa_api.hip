@@ -48,7 +48,7 @@ int check_topk(const float* scores, int64_t ld, const int32_t* rs, const int32_t
   if (K < 1) return DSA_ERR_INVALID_ARG;
   if (ld < n_cols) return DSA_ERR_INVALID_ARG;
   if (n_q > 0 && (!scores || !rs || !re || !out)) return DSA_ERR_INVALID_ARG;
-  if (K > (1 << 20)) return DSA_ERR_UNSUPPORTED;
+  if (K > 65536) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
@@ -117,21 +117,20 @@ int dsa_indexer_scores(const void* q, const void* k, const float* k_scale, const
 }
 
 size_t dsa_topk_workspace_size(int64_t n_q, int64_t n_cols, int32_t index_topk) {
-  (void)n_q;
-  (void)n_cols;
-  (void)index_topk;
-  return 0;
+  if (n_q <= 0 || n_cols < 0 || index_topk < 1) return 0;
+  return dsa::topk_workspace_bytes(n_q, n_cols, index_topk);
 }
 
 int dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_starts,
              const int32_t* row_ends, int64_t n_q, int64_t n_cols, int32_t index_topk,
              int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int st = check_topk(scores, ld_scores, row_starts, row_ends, n_q, n_cols, index_topk, topk_idx);
   if (st != DSA_OK) return st;
-  return launch_status(dsa::launch_topk(scores, ld_scores, row_starts, row_ends, n_q, index_topk,
-                                        topk_idx, as_stream(stream)));
+  const size_t need = dsa_topk_workspace_size(n_q, n_cols, index_topk);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return DSA_ERR_WORKSPACE;
+  return launch_status(dsa::launch_topk(scores, ld_scores, row_starts, row_ends, n_q, n_cols,
+                                        index_topk, topk_idx, workspace, as_stream(stream)));
 }
 
 size_t dsa_indexer_topk_workspace_size(int64_t n_q, int64_t n_k, int32_t n_heads,
@@ -139,9 +138,10 @@ size_t dsa_indexer_topk_workspace_size(int64_t n_q, int64_t n_k, int32_t n_heads
   (void)n_heads;
   (void)head_dim;
   (void)dtype;
-  (void)index_topk;
-  if (n_q <= 0 || n_k <= 0) return 0;
-  return size_t(n_q) * size_t(n_k) * sizeof(float);
+  if (n_q <= 0 || n_k <= 0 || index_topk < 1) return 0;
+  // the score matrix, then the top-k's own workspace (256-byte aligned)
+  const size_t scores = (size_t(n_q) * size_t(n_k) * sizeof(float) + 255) & ~size_t(255);
+  return scores + dsa::topk_workspace_bytes(n_q, n_k, index_topk);
 }
 
 int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const float* w,
@@ -153,7 +153,7 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const f
                          dtype);
   if (st != DSA_OK) return st;
   if (index_topk < 1 || (n_q > 0 && !topk_idx)) return DSA_ERR_INVALID_ARG;
-  if (index_topk > (1 << 20)) return DSA_ERR_UNSUPPORTED;
+  if (index_topk > 65536) return DSA_ERR_UNSUPPORTED;
   const size_t need =
       dsa_indexer_topk_workspace_size(n_q, n_k, n_heads, head_dim, dtype, index_topk);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
@@ -164,8 +164,10 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const f
   hipError_t e = dsa::launch_indexer_scores(q, k, k_scale, w, row_starts, row_ends, n_q, n_k,
                                             n_heads, head_dim, dtype, scores, n_k, s);
   if (e != hipSuccess) return DSA_ERR_LAUNCH;
-  return launch_status(
-      dsa::launch_topk(scores, n_k, row_starts, row_ends, n_q, index_topk, topk_idx, s));
+  void* topk_ws = static_cast<uint8_t*>(workspace) +
+                  ((size_t(n_q) * size_t(n_k) * sizeof(float) + 255) & ~size_t(255));
+  return launch_status(dsa::launch_topk(scores, n_k, row_starts, row_ends, n_q, n_k, index_topk,
+                                        topk_idx, topk_ws, s));
 }
 
 size_t dsa_sparse_mla_workspace_size(int64_t n_q, int32_t n_heads, int32_t d_qk, int32_t d_v,

@@ -19,9 +19,11 @@ hipError_t launch_indexer_prep(const float* q_raw, const float* k_raw, const flo
                                float eps, int32_t dtype, void* q_out, void* k_out,
                                float* w_out, float* k_scale_out, hipStream_t stream);
 
+size_t topk_workspace_bytes(int64_t n_q, int64_t n_cols, int32_t K);
+
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_starts,
-                       const int32_t* row_ends, int64_t n_q, int32_t K, int32_t* out,
-                       hipStream_t stream);
+                       const int32_t* row_ends, int64_t n_q, int64_t n_cols, int32_t K,
+                       int32_t* out, void* workspace, hipStream_t stream);
 
 hipError_t launch_indexer_scores(const void* q, const void* k, const float* k_scale,
                                  const float* w, const int32_t* row_starts,

@@ -108,15 +108,58 @@ def test_topk_garbage_outside_windows(dsa):
     _topk_case(dsa, S, rs, re, 1024, "thd garbage")
 
 
-def test_topk_long_rows_global_path(dsa):
-    # windows longer than the LDS-resident limit (8192) use the global passes
+def test_topk_long_rows_split_path(dsa):
+    # few rows over many columns: windows above the LDS-resident limit (8192) are
+    # selected in up to 16 chunks and merged; shorter ones by one workgroup
     g = np.random.default_rng(103)
     n_q, n = 24, 70000
     S = g.standard_normal((n_q, n)).astype(np.float32)
     S[::3] = np.round(S[::3] * 4) / 4                       # heavy ties on some rows
+    S[1, 100:40000:7] = -np.inf                             # -inf inside a split window
     rs = np.zeros(n_q, np.int32)
+    rs[5::6] = 777                                          # windows not starting at 0
     re = np.array([n, 8192, 8193, 9000, 30000, 65536] * 4, np.int32)
-    _topk_case(dsa, S, rs, re, 2048, "long rows")
+    assert dsa._lib_or_load().dsa_topk_workspace_size(n_q, n, 2048) > 0
+    for K in (2048, 100, 1):
+        _topk_case(dsa, S, rs, re, K, f"split K={K}")
+
+
+def test_topk_split_few_candidates(dsa):
+    # split-path windows where most keys are -inf: chunks emit fewer than K
+    # candidates, the merged row is -1 padded
+    g = np.random.default_rng(107)
+    n_q, n = 6, 50000
+    S = np.full((n_q, n), -np.inf, np.float32)
+    for t in range(n_q):
+        cols = g.choice(n, size=[10, 1500, 2047, 2048, 2049, 5000][t], replace=False)
+        S[t, cols] = np.round(g.standard_normal(cols.size) * 2).astype(np.float32)
+    rs = np.zeros(n_q, np.int32)
+    re = np.full(n_q, n, np.int32)
+    _topk_case(dsa, S, rs, re, 2048, "split sparse")
+
+
+def test_topk_rows_longer_than_split(dsa):
+    # windows above 16 * 8192 keys: one workgroup re-reads the row from memory
+    g = np.random.default_rng(104)
+    n_q, n = 3, 140000
+    S = g.standard_normal((n_q, n)).astype(np.float32)
+    S[2] = np.round(S[2] * 3) / 3
+    rs = np.array([0, 5, 1000], np.int32)
+    re = np.array([n, 131073, 140000], np.int32)
+    _topk_case(dsa, S, rs, re, 2048, "longer than split")
+
+
+def test_topk_many_long_rows_global_path(dsa):
+    # more than 1024 rows over more than 8192 columns: one workgroup per row,
+    # re-reading windows longer than 8192 from memory
+    g = np.random.default_rng(105)
+    n_q, n = 1100, 9000
+    S = g.standard_normal((n_q, n)).astype(np.float32)
+    S[::4] = np.round(S[::4] * 2) / 2
+    rs = g.integers(0, 500, n_q).astype(np.int32)
+    re = np.minimum(n, rs + g.integers(7000, 9000, n_q)).astype(np.int32)
+    assert dsa._lib_or_load().dsa_topk_workspace_size(n_q, n, 2048) == 0
+    _topk_case(dsa, S, rs, re, 2048, "many long rows")
 
 
 def test_topk_prefill4k_oracle_scores(dsa):
