@@ -35,8 +35,8 @@ MLA_FLOP_PER_PAIR = 2 * 128 * (576 + 512)   # 278,528
 
 KERNEL_SOURCES = {                      # kernel -> the sources its code is built from
     "mla_bf16_kernel": ["mla.hip", "dsa_device.h"],
-    "indexer_rows_kernel": ["indexer.hip", "dsa_device.h"],
-    "topk_rows_kernel": ["topk.hip", "dsa_device.h"],
+    "indexer_rows_kernel": ["indexer.hip", "indexer_core.h", "dsa_device.h"],
+    "topk_rows_kernel": ["topk.hip", "topk_select.h", "dsa_device.h"],
 }
 
 
@@ -143,8 +143,17 @@ def stage_bench(args, dsa, synth, np, torch):
         "mla": lambda: dsa.dsa_sparse_mla_fwd(mq, mkv, idx, w.sm_scale, w.d_v, out=out, lse=lse,
                                               workspace=ws),
     }
+    fused = lay.n_q <= 1024          # decode shape: the fused indexer + top-k applies
+    if fused:
+        idx2 = torch.empty_like(idx)
+        code = 1 if w.dtype == "bf16" else 2
+        fws = torch.empty(max(dsa.indexer_topk_workspace(lay.n_q, lay.n_k, w.n_heads, w.head_dim,
+                                                         code, K), 1), dtype=torch.uint8, device=dev)
+        fns["indexer_topk"] = lambda: dsa.dsa_indexer_topk(q, k, wt, rs, re, K, k_scale=ks, out=idx2,
+                                                           workspace=fws)
+        hbm_bound["indexer_topk"] = True
     ms = {}
-    for name in ("indexer", "topk", "mla"):
+    for name in fns:
         f = fns[name]
         for _ in range(args.warmup):
             f()
@@ -172,6 +181,8 @@ def stage_bench(args, dsa, synth, np, torch):
     mla_compulsory = mq.numel() * 2 + out.numel() * 2 + lse.numel() * 4 + idx.numel() * 4
     mfma_peak = FP8_PEAK_TFLOPS if w.dtype == "fp8" else BF16_PEAK_TFLOPS
     t = {n: v * 1e-3 for n, v in ms.items()}
+    if fused:
+        assert torch.equal(idx, idx2), "fused and unfused indexer + top-k disagree"
     comp = {
         "indexer": {"ms": ms["indexer"], "pairs_per_s": pairs / t["indexer"],
                     "tflops": idx_flop / t["indexer"] / 1e12,
@@ -186,8 +197,21 @@ def stage_bench(args, dsa, synth, np, torch):
                 "gather_gbs": (gather + mla_compulsory) / t["mla"] / 1e9,
                 "frac_hbm": (gather + mla_compulsory) / t["mla"] / 1e9 / HBM_PEAK_GBS},
     }
-    dom = max(ms, key=ms.get)
-    if dom == "indexer" and not w.decode:
+    if fused:
+        fb = idx_bytes - pairs * 4 + lay.n_q * K * 4       # q + k + w read, indices written
+        comp["indexer_topk_fused"] = {"ms": ms["indexer_topk"],
+                                      "pairs_per_s": pairs / t["indexer_topk"],
+                                      "gbs": fb / t["indexer_topk"] / 1e9,
+                                      "frac_hbm": fb / t["indexer_topk"] / 1e9 / HBM_PEAK_GBS}
+        ms_path = {"indexer_topk": ms["indexer_topk"], "mla": ms["mla"]}
+    else:
+        ms_path = {"indexer": ms["indexer"], "topk": ms["topk"], "mla": ms["mla"]}
+    dom = max(ms_path, key=ms_path.get)
+    if dom == "indexer_topk":
+        ach = comp["indexer_topk_fused"]["gbs"]
+        roof = {"kernel": "indexer_topk_chunk_kernel", "bound": "hbm", "achieved": ach,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    elif dom == "indexer" and not w.decode:
         ach = comp["indexer"]["tflops"]
         roof = {"kernel": "indexer_rows_kernel", "bound": "mfma", "achieved": ach, "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": ach / mfma_peak, "traffic": None}
@@ -208,7 +232,7 @@ def stage_bench(args, dsa, synth, np, torch):
         ach = comp["topk"]["gbs"]
         roof = {"kernel": "topk_rows_kernel", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
-    total = sum(ms.values())
+    total = sum(ms_path.values())
     return {
         "metric": "indexer q·k pairs/s + top-k rows/s + sparse-MLA TFLOP/s (per stage)",
         "value": pairs / (total * 1e-3), "unit": "indexer pairs/s (sum of the stage medians)",

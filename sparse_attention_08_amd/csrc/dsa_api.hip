@@ -137,8 +137,9 @@ size_t dsa_indexer_topk_workspace_size(int64_t n_q, int64_t n_k, int32_t n_heads
                                        int32_t head_dim, int32_t dtype, int32_t index_topk) {
   (void)n_heads;
   (void)head_dim;
-  (void)dtype;
   if (n_q <= 0 || n_k <= 0 || index_topk < 1) return 0;
+  if (dsa::indexer_topk_fused(n_q, dtype, index_topk))
+    return n_k > 8192 ? dsa::indexer_topk_fused_workspace_bytes(n_q, index_topk) : 0;
   // the score matrix, then the top-k's own workspace (256-byte aligned)
   const size_t scores = (size_t(n_q) * size_t(n_k) * sizeof(float) + 255) & ~size_t(255);
   return scores + dsa::topk_workspace_bytes(n_q, n_k, index_topk);
@@ -159,8 +160,12 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const f
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return DSA_ERR_WORKSPACE;
   if (n_q == 0) return DSA_OK;
-  float* scores = static_cast<float*>(workspace);
   hipStream_t s = as_stream(stream);
+  if (dsa::indexer_topk_fused(n_q, dtype, index_topk))
+    return launch_status(dsa::launch_indexer_topk_fused(q, k, k_scale, w, row_starts, row_ends,
+                                                        n_q, n_heads, dtype, index_topk,
+                                                        topk_idx, workspace, s));
+  float* scores = static_cast<float*>(workspace);
   hipError_t e = dsa::launch_indexer_scores(q, k, k_scale, w, row_starts, row_ends, n_q, n_k,
                                             n_heads, head_dim, dtype, scores, n_k, s);
   if (e != hipSuccess) return DSA_ERR_LAUNCH;

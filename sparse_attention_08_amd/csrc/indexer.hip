@@ -26,98 +26,15 @@
 
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "indexer_core.h"
 
 namespace dsa {
 namespace {
 
-struct OpBf16 {
-  typedef bf16x8_t frag_t;
-  static constexpr int kRowBytes = 256;  // 128 bf16
-  static constexpr int kFragBytes = 16;  // 8 bf16 per lane per K-step of 16
-  static constexpr int kSteps = 8;
-  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-struct OpFp8 {
-  typedef i32x8_t frag_t;
-  static constexpr int kRowBytes = 128;  // 128 e4m3
-  static constexpr int kFragBytes = 32;  // 32 e4m3 per lane per K-step of 64
-  static constexpr int kSteps = 2;
-  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c) {
-    // format 0 = e4m3 for both operands; block scales 127 = 2^0 (no scaling)
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-  }
-};
-
-constexpr int kKeyTile = 32;
-
-// q[t] fragments and the matching head weights of one query row, per lane.
-template <class Op, int MT>
-struct QueryRow {
-  typename Op::frag_t qa[MT][Op::kSteps];
-  float wv[MT][16];
-
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ q,
-                                       const float* __restrict__ w, int64_t t, int H,
-                                       int lane) {
-    const int half = lane >> 5;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int h = mt * 32 + (lane & 31);
-      const bool ok = h < H;
-      const uint8_t* base =
-          q + (t * H + (ok ? h : 0)) * int64_t(Op::kRowBytes) + half * Op::kFragBytes;
-#pragma unroll
-      for (int st = 0; st < Op::kSteps; ++st) {
-        typename Op::frag_t v = *reinterpret_cast<const typename Op::frag_t*>(
-            base + st * 2 * Op::kFragBytes);
-        qa[mt][st] = ok ? v : typename Op::frag_t{};
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int hh = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        wv[mt][r] = hh < H ? w[t * H + hh] : 0.0f;
-      }
-    }
-  }
-
-  // Logits of the 32 keys whose fragments are in kb (heads on M, keys on N).
-  __device__ __forceinline__ void mma(const typename Op::frag_t (&kb)[Op::kSteps],
-                                      f32x16_t (&acc)[MT]) const {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
-#pragma unroll
-    for (int st = 0; st < Op::kSteps; ++st)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mfma(qa[mt][st], kb[st], acc[mt]);
-  }
-
-  // ReLU, head weights and the head sum; lanes l and l^32 both end with the
-  // score of key l%32.  ReLU is a signed-integer max on the float bits:
-  // non-negative floats keep their bits, every negative float (and -0.0) has
-  // negative bits and becomes +0.0 -- one v_max_i32 instead of the two VALU ops
-  // of an IEEE fmaxf.
-  __device__ __forceinline__ float epilogue(const f32x16_t (&acc)[MT]) const {
-    float p = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        p = fmaf(wv[mt][r], __int_as_float(max(__float_as_int(acc[mt][r]), 0)), p);
-    // v_permlane32_swap: lanes 0-31 and 32-63 exchange this value
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p),
-                                                     false, false);
-    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
-
-  __device__ __forceinline__ float score(const typename Op::frag_t (&kb)[Op::kSteps]) const {
-    f32x16_t acc[MT];
-    mma(kb, acc);
-    return epilogue(acc);
-  }
-};
+using ixcore::OpBf16;
+using ixcore::OpFp8;
+using ixcore::QueryRow;
+using ixcore::kKeyTile;
 
 // ---------------------------------------------------------------------------
 // prefill: 8 query rows per workgroup (one per wave), keys staged through LDS in
@@ -311,24 +228,15 @@ __global__ __launch_bounds__(kSplitThreads) void indexer_rowsplit_kernel(
 
   QueryRow<Op, MT> qr;
   qr.load(q, w, t, H, lane);
-  const int half = lane >> 5;
-  for (int i = i0 + wave; i < i1; i += kWaves) {
+  constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
+  auto put = [&](int i, float p, float ks) {
     const int s = a + i * kKeyTile + (lane & 31);
-    const bool ok = s < b;
-    const uint8_t* src = k + int64_t(ok ? s : a) * Op::kRowBytes + half * Op::kFragBytes;
-    typename Op::frag_t kb[Op::kSteps];
-#pragma unroll
-    for (int st = 0; st < Op::kSteps; ++st) {
-      typename Op::frag_t v =
-          *reinterpret_cast<const typename Op::frag_t*>(src + st * 2 * Op::kFragBytes);
-      kb[st] = ok ? v : typename Op::frag_t{};
-    }
-    float p = qr.score(kb);
-    if (lane < 32 && ok) {
-      if (k_scale) p *= k_scale[s];
+    if (lane < 32 && s < b && i < i1) {
+      if constexpr (kScaled) p *= ks;
       scores[t * ld + s] = p;
     }
-  }
+  };
+  ixcore::stream_tiles<Op, MT, kScaled>(qr, k, k_scale, a, b, i0 + wave, kWaves, i1, lane, put);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,173 @@
+// Indexer building blocks shared by the score kernels and the fused indexer +
+// top-k kernel (gfx950): operand traits of the bf16 and fp8 matrix-core paths
+// and the per-row query state.
+//
+//   score[t, s] = k_scale[s] * sum_h w[t, h] * max(0, q[t, h, :] . k[s, :])
+//
+// For one query row the q[t] block [H x 128] is the MFMA A operand (heads on M,
+// in MT tiles of 32) and a tile of 32 keys [128 x 32] is the B operand (keys on
+// N), so the 32x32 output of v_mfma_f32_32x32x16_bf16 (or
+// v_mfma_scale_f32_32x32x64_f8f6f4) holds, in lane l, 16 heads of key column
+// l%32.  The ReLU and the weighted head sum happen in those registers; one
+// cross-lane add (lane l + lane l^32) finishes the head sum.
+#pragma once
+
+#include "dsa_device.h"
+
+namespace dsa {
+namespace ixcore {
+
+struct OpBf16 {
+  typedef bf16x8_t frag_t;
+  static constexpr int kRowBytes = 256;  // 128 bf16
+  static constexpr int kFragBytes = 16;  // 8 bf16 per lane per K-step of 16
+  static constexpr int kSteps = 8;
+  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct OpFp8 {
+  typedef i32x8_t frag_t;
+  static constexpr int kRowBytes = 128;  // 128 e4m3
+  static constexpr int kFragBytes = 32;  // 32 e4m3 per lane per K-step of 64
+  static constexpr int kSteps = 2;
+  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c) {
+    // format 0 = e4m3 for both operands; block scales 127 = 2^0 (no scaling)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+constexpr int kKeyTile = 32;
+
+// q[t] fragments and the matching head weights of one query row, per lane.
+template <class Op, int MT>
+struct QueryRow {
+  typename Op::frag_t qa[MT][Op::kSteps];
+  float wv[MT][16];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ q,
+                                       const float* __restrict__ w, int64_t t, int H,
+                                       int lane) {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = mt * 32 + (lane & 31);
+      const bool ok = h < H;
+      const uint8_t* base =
+          q + (t * H + (ok ? h : 0)) * int64_t(Op::kRowBytes) + half * Op::kFragBytes;
+#pragma unroll
+      for (int st = 0; st < Op::kSteps; ++st) {
+        typename Op::frag_t v = *reinterpret_cast<const typename Op::frag_t*>(
+            base + st * 2 * Op::kFragBytes);
+        qa[mt][st] = ok ? v : typename Op::frag_t{};
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int hh = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        wv[mt][r] = hh < H ? w[t * H + hh] : 0.0f;
+      }
+    }
+  }
+
+  // Logits of the 32 keys whose fragments are in kb (heads on M, keys on N).
+  __device__ __forceinline__ void mma(const typename Op::frag_t (&kb)[Op::kSteps],
+                                      f32x16_t (&acc)[MT]) const {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < Op::kSteps; ++st)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mfma(qa[mt][st], kb[st], acc[mt]);
+  }
+
+  // ReLU, head weights and the head sum; lanes l and l^32 both end with the
+  // score of key l%32.  ReLU is a signed-integer max on the float bits:
+  // non-negative floats keep their bits, every negative float (and -0.0) has
+  // negative bits and becomes +0.0 -- one v_max_i32 instead of the two VALU ops
+  // of an IEEE fmaxf.
+  __device__ __forceinline__ float epilogue(const f32x16_t (&acc)[MT]) const {
+    float p = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p = fmaf(wv[mt][r], __int_as_float(max(__float_as_int(acc[mt][r]), 0)), p);
+    // v_permlane32_swap: lanes 0-31 and 32-63 exchange this value
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p),
+                                                     false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+
+  __device__ __forceinline__ float score(const typename Op::frag_t (&kb)[Op::kSteps]) const {
+    f32x16_t acc[MT];
+    mma(kb, acc);
+    return epilogue(acc);
+  }
+};
+
+
+// Fragments of the 32-key tile starting at key s0, straight from global memory:
+// lane l reads key s0 + l%32.  Lanes past the last key b-1 read key s0 instead
+// (their score columns are discarded; a column of the MFMA output depends only
+// on that column's key).
+template <class Op>
+__device__ __forceinline__ void load_key_tile(const uint8_t* __restrict__ k, int s0, int b,
+                                              int lane, typename Op::frag_t (&kb)[Op::kSteps]) {
+  const int s = s0 + (lane & 31);
+  const uint8_t* src = k + int64_t(s < b ? s : s0) * Op::kRowBytes + (lane >> 5) * Op::kFragBytes;
+#pragma unroll
+  for (int st = 0; st < Op::kSteps; ++st)
+    kb[st] = *reinterpret_cast<const typename Op::frag_t*>(src + st * 2 * Op::kFragBytes);
+}
+
+// A 32-key tile and, for fp8 keys, the scale of the lane's key.
+template <class Op, bool kScaled>
+struct KeyTile {
+  typename Op::frag_t kb[Op::kSteps];
+  float ks;
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ k,
+                                       const float* __restrict__ k_scale, int s0, int b,
+                                       int lane) {
+    load_key_tile<Op>(k, s0, b, lane, kb);
+    if constexpr (kScaled) {
+      const int s = s0 + (lane & 31);
+      ks = k_scale[s < b ? s : s0];
+    }
+  }
+};
+
+// Scores of the tiles i = first, first + step, ... < nt of one query row, with
+// the next tile's loads in flight while a tile is on the matrix core.  Two
+// tiles alternate between two register sets, and every load is issued
+// unconditionally (past the last tile the last tile is reloaded and its score
+// dropped), so each loop iteration has the same loads in the same order and
+// the compiler's memory-counter waits stay exact instead of draining the
+// prefetch.  put(i, score, scale) receives each tile's scores (lanes l and l^32
+// both hold key l%32).
+template <class Op, int MT, bool kScaled, class Put>
+__device__ __forceinline__ void stream_tiles(const QueryRow<Op, MT>& qr,
+                                             const uint8_t* __restrict__ k,
+                                             const float* __restrict__ k_scale, int base, int b,
+                                             int first, int step, int nt, int lane, Put put) {
+  if (first >= nt) return;
+  auto key0 = [&](int i) { return base + (i < nt ? i : nt - 1) * 32; };
+  KeyTile<Op, kScaled> ta, tb;
+  ta.load(k, k_scale, key0(first), b, lane);
+  tb.load(k, k_scale, key0(first + step), b, lane);
+  for (int i = first;; i += 2 * step) {
+    const float pa = qr.score(ta.kb);
+    const float ka = ta.ks;
+    ta.load(k, k_scale, key0(i + 2 * step), b, lane);
+    put(i, pa, ka);
+    if (i + step >= nt) break;
+    const float pb = qr.score(tb.kb);
+    const float kbs = tb.ks;
+    tb.load(k, k_scale, key0(i + 3 * step), b, lane);
+    put(i + step, pb, kbs);
+    if (i + 2 * step >= nt) break;
+  }
+}
+
+}  // namespace ixcore
+}  // namespace dsa

@@ -64,7 +64,8 @@ constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // 10 (wave 0)
 constexpr int kHeadsPerBlock = kWaves * 32;     // 128
 constexpr int kMaxIdx = 2048;                   // selected keys per workgroup (LDS-staged)
 constexpr int kMaxTiles = kMaxIdx / kKT;
-constexpr int kRing = 3;                      // LDS fragment reads in flight ahead of the MFMAs
+constexpr int kRingQ = 3;                     // LDS fragment reads in flight ahead of the MFMAs
+constexpr int kRingV = 3;
 constexpr float kSpan = 32.0f;                 // base-2 units: P <= 2^32 before a second pass
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -159,6 +160,12 @@ __device__ __forceinline__ void dma_rows(const int* sidx, int lt, int wave, int 
     row[u] = uint32_t(sidx[lt * kKT + dma_key((wave + kWaves * u) * kWave + lane)]);
 }
 
+// row of this lane's chunk of wave-load u of tile lt
+__device__ __forceinline__ uint32_t dma_row(const int* sidx, int lt, int u, int wave, int lane) {
+  asm volatile("" : "+v"(lane));  // recomputed here, not held in registers
+  return uint32_t(sidx[lt * kKT + dma_key((wave + kWaves * u) * kWave + lane)]);
+}
+
 // issue wave-load u of the tile into buffer B
 template <int B>
 __device__ __forceinline__ void dma_issue(int u, uint32_t row, const uint8_t* __restrict__ kv,
@@ -201,28 +208,31 @@ __device__ __forceinline__ void wait_tile(bool next_in_flight, int wave) {
 
 // S^T = K . Q^T for the tile in buffer B: keys on M, the wave's 32 heads on N,
 // 36 K-steps of 16 dims.  Lane l reads key l%32, dims 16*st + 8*(l/32) .. +8;
-// the fragment reads run kRing steps ahead of their MFMA.  With kDma, the
+// the fragment reads run kRingQ steps ahead of their MFMA.  With kDma, the
 // LDS-DMA loads of a later tile (into buffer BD) are issued between the MFMAs
 // (the wave can issue them while the matrix core works).
 template <int B, int BD, bool kDma>
 __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], int lane,
-                                            const uint32_t (&row)[kDmaPerWave],
+                                            const int* sidx, int lt_dma,
                                             const uint8_t* __restrict__ kv, int wave) {
   const uint8_t* ka = kvbuf<B>() + (lane & 31) * kKvStride + (lane >> 5) * 16;
-  bf16x8_t fr[kRing];
+  bf16x8_t fr[kRingQ];
 #pragma unroll
-  for (int st = 0; st < kRing; ++st) fr[st] = *reinterpret_cast<const bf16x8_t*>(ka + st * 32);
+  for (int st = 0; st < kRingQ; ++st) fr[st] = *reinterpret_cast<const bf16x8_t*>(ka + st * 32);
   f32x16_t s;
+  uint32_t row = 0u;
 #pragma unroll
   for (int st = 0; st < kQSteps; ++st) {
-    const bf16x8_t a = fr[st % kRing];
-    if (st + kRing < kQSteps)
-      fr[st % kRing] = *reinterpret_cast<const bf16x8_t*>(ka + (st + kRing) * 32);
+    const bf16x8_t a = fr[st % kRingQ];
+    if (st + kRingQ < kQSteps)
+      fr[st % kRingQ] = *reinterpret_cast<const bf16x8_t*>(ka + (st + kRingQ) * 32);
     if (st == 0) mfma_v0(s, a, qf[st]);
     else if (st + 1 < kQSteps) mfma_v(s, a, qf[st]);
     else mfma_v_last(s, a, qf[st]);
     if constexpr (kDma) {
-      if (st % 3 == 1 && st / 3 < kDmaPerWave) dma_issue<BD>(st / 3, row[st / 3], kv, wave, lane);
+      // the row of load u is read one MFMA before the load is issued
+      if (st % 3 == 0 && st / 3 < kDmaPerWave) row = dma_row(sidx, lt_dma, st / 3, wave, lane);
+      if (st % 3 == 1 && st / 3 < kDmaPerWave) dma_issue<BD>(st / 3, row, kv, wave, lane);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep this order
   }
@@ -346,7 +356,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
   const int n0 = 16 * (grp & 1);  // value column offset of the group inside a 32-wide tile
   const uint8_t* vb = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) + (li >> 2) * kKvStride +
                       (n0 + 4 * (li & 3)) * 2 + 4 * half * kKvStride;
-  // step m = 2n + ks: value tile n, key step ks; reads run kRing steps ahead
+  // step m = 2n + ks: value tile n, key step ks; reads run kRingV steps ahead
   auto rd = [&](int m) {
     const uint8_t* base = vb + 16 * (m & 1) * kKvStride + (m >> 1) * 64;
     const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
@@ -354,13 +364,13 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kKvStride));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  bf16x8_t fr[kRing];
+  bf16x8_t fr[kRingV];
 #pragma unroll
-  for (int m = 0; m < kRing; ++m) fr[m] = rd(m);
+  for (int m = 0; m < kRingV; ++m) fr[m] = rd(m);
 #pragma unroll
   for (int m = 0; m < 2 * kVTiles; ++m) {
-    const bf16x8_t v = fr[m % kRing];
-    if (m + kRing < 2 * kVTiles) fr[m % kRing] = rd(m + kRing);
+    const bf16x8_t v = fr[m % kRingV];
+    if (m + kRingV < 2 * kVTiles) fr[m % kRingV] = rd(m + kRingV);
     mfma_a(o[m >> 1], (m & 1) == 0 ? p0 : p1, v);
     if constexpr (kSm) {
       if (m % 2 == 1 && m / 2 < kSmStages) sm_stage(m / 2, sm, scale2, m_ref, m_max, over, l_run);
@@ -382,12 +392,10 @@ __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const ui
   __builtin_amdgcn_s_barrier();
   Softmax sm;
   sm.vmask = sh.vmask[i];
-  uint32_t row[kDmaPerWave];
   if (i + 2 < nt) {
-    dma_rows(sh.idx, i + 2, wave, lane, row);
-    sm.s = qk_tile<B, (B + 2) & 3, true>(qf, lane, row, kvb, wave);
+    sm.s = qk_tile<B, (B + 2) & 3, true>(qf, lane, sh.idx, i + 2, kvb, wave);
   } else {
-    sm.s = qk_tile<B, 0, false>(qf, lane, row, kvb, wave);
+    sm.s = qk_tile<B, 0, false>(qf, lane, sh.idx, 0, kvb, wave);
   }
   pv_tile<(B + 3) & 3, true>(nullptr, p0, p1, o, lane, sm, scale2, m_ref, m_max, over, l_run);
   p0 = sm.p0;
@@ -487,8 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       {
         Softmax sm;
         sm.vmask = sh.vmask[0];
-        uint32_t row[kDmaPerWave];
-        sm.s = qk_tile<0, 0, false>(qf, lane, row, kvb, wave);
+        sm.s = qk_tile<0, 0, false>(qf, lane, sh.idx, 0, kvb, wave);
         softmax_all(sm, scale2, m_ref, m_max, over, l_run);
         p0 = sm.p0;
         p1 = sm.p1;

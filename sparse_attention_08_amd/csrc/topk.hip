@@ -29,179 +29,12 @@
 //            c precede those of chunk c+1, so the merged output stays ascending.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "topk_select.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kCap = 8192;        // keys held in LDS by one workgroup
-constexpr int kBins = 2048;       // 11-bit digit
-constexpr int kMaxChunks = 16;    // chunks per row on the split path
-constexpr int kMaxSplitK = 2048;  // largest k on the split path
-constexpr int kMergeCap = kMaxChunks * kMaxSplitK;  // candidates merged in LDS
-constexpr int64_t kMaxSplitRows = 1024;
-constexpr int kMergeThreads = 1024;
-
-template <int NT>
-struct SelectShared {
-  static constexpr int kNW = NT / kWave;
-  uint32_t hist[kBins];
-  uint32_t tmp[2 * kNW];
-  uint32_t seg_cnt[2 * kNW];
-  uint32_t pick[2];
-};
-
-// Keys of a row held in LDS, or read (and mapped) from the fp32 scores.
-struct LdsKeys {
-  const uint32_t* keys;
-  __device__ __forceinline__ uint32_t operator()(int i) const { return keys[i]; }
-};
-struct GlobalKeys {
-  const float* src;
-  __device__ __forceinline__ uint32_t operator()(int i) const { return score_key(src[i]); }
-};
-
-// Workgroup-wide min and max of u32 values.
-template <int NT>
-__device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32_t* tmp) {
-  constexpr int NW = NT / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) {
-    lo = min(lo, uint32_t(__shfl_xor(int(lo), o)));
-    hi = max(hi, uint32_t(__shfl_xor(int(hi), o)));
-  }
-  if (lane == 0) {
-    tmp[wave] = lo;
-    tmp[NW + wave] = hi;
-  }
-  __syncthreads();
-  lo = tmp[0];
-  hi = tmp[NW];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    lo = min(lo, tmp[w]);
-    hi = max(hi, tmp[NW + w]);
-  }
-  __syncthreads();
-}
-
-// Select the K largest of the n keys key(0..n-1) (n_sel of them are nonzero),
-// ties to the lowest index, and call emit(p, i, key) for each selected index i
-// in ascending order, p = its output slot in [0, min(K, n_sel)).  All NT threads
-// of the workgroup call it.
-//
-// The radix passes start at the highest bit in which the row's selectable keys
-// differ (the bits above are common to all of them), in digits of at most 11
-// bits: close scores then spread over the histogram instead of piling into a
-// few bins, and narrow ranges need fewer passes.
-template <int NT, class Keys, class Emit>
-__device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_sel, int K,
-                                            SelectShared<NT>& sh, Emit emit) {
-  constexpr int NW = NT / kWave;
-  constexpr int kBPT = kBins / NT;  // histogram bins owned per thread in the scan
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-
-  uint32_t thr = 0u, need_eq = 0u;
-  if (n_sel > uint32_t(K)) {
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t k = key(i);
-      if (k != 0u) {
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
-      }
-    }
-    block_min_max<NT>(kmin, kmax, sh.tmp);
-    const uint32_t diff = kmin ^ kmax;
-    int shift = diff == 0u ? 0 : 32 - __builtin_clz(diff);  // varying bits [0, shift)
-    uint32_t pmask = shift >= 32 ? 0u : ~((1u << shift) - 1u);
-    uint32_t prefix = kmax & pmask;
-    uint32_t remaining = uint32_t(K);
-#pragma unroll 1
-    while (shift > 0) {
-      const int nb = shift < 11 ? shift : 11;
-      shift -= nb;
-      const uint32_t dmask = (1u << nb) - 1u;
-      for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
-      __syncthreads();
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t k = key(i);
-        if (k != 0u && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      // thread j owns the bins of slot (NT-1-j), so an exclusive prefix over
-      // threads is the count of keys in higher bins
-      const int base = (NT - 1 - tid) * kBPT;
-      uint32_t local = 0u;
-#pragma unroll
-      for (int j = 0; j < kBPT; ++j) local += sh.hist[base + j];
-      uint32_t total;
-      const uint32_t above = block_exclusive_sum<NT>(local, sh.tmp, total);
-      if (above < remaining && above + local >= remaining) {
-        uint32_t c = above;
-        for (int j = kBPT - 1; j >= 0; --j) {
-          const uint32_t h = sh.hist[base + j];
-          if (c + h >= remaining) {
-            sh.pick[0] = uint32_t(base + j);
-            sh.pick[1] = remaining - c;
-            break;
-          }
-          c += h;
-        }
-      }
-      __syncthreads();
-      prefix |= sh.pick[0] << shift;
-      pmask |= dmask << shift;
-      remaining = sh.pick[1];
-      __syncthreads();
-    }
-    thr = prefix;
-    need_eq = remaining;
-  }
-
-  // ordered compaction
-  const int seg = ((n + NW - 1) / NW + kWave - 1) & ~(kWave - 1);
-  const int s_lo = wave * seg;
-  const int s_hi = min(n, s_lo + seg);
-  uint32_t gt = 0u, eq = 0u;
-  for (int base = s_lo; base < s_hi; base += kWave) {
-    const int i = base + lane;
-    const uint32_t k = i < s_hi ? key(i) : 0u;
-    gt += __popcll(__ballot(k > thr));
-    eq += __popcll(__ballot(i < s_hi && k == thr));
-  }
-  if (lane == 0) {
-    sh.seg_cnt[wave] = gt;
-    sh.seg_cnt[NW + wave] = eq;
-  }
-  __syncthreads();
-  uint32_t gt_before = 0u, eq_before = 0u;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += sh.seg_cnt[w];
-    eq_before += sh.seg_cnt[NW + w];
-  }
-  const uint64_t lt = lanemask_lt();
-  for (int base = s_lo; base < s_hi; base += kWave) {
-    const int i = base + lane;
-    const uint32_t k = i < s_hi ? key(i) : 0u;
-    const bool is_gt = k > thr;
-    const bool is_eq = i < s_hi && k == thr;
-    const uint64_t mgt = __ballot(is_gt);
-    const uint64_t meq = __ballot(is_eq);
-    const uint32_t eq_rank = eq_before + uint32_t(__popcll(meq & lt));
-    if (is_gt || (is_eq && eq_rank < need_eq)) {
-      const uint32_t pos = gt_before + uint32_t(__popcll(mgt & lt)) + min(eq_rank, need_eq);
-      if (pos < uint32_t(K)) emit(pos, i, k);
-    }
-    gt_before += uint32_t(__popcll(mgt));
-    eq_before += uint32_t(__popcll(meq));
-  }
-}
+using namespace topksel;
 
 // Keys of scores[a .. a+n) into LDS (n <= kCap); returns the selectable count.
 __device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t* keys,
@@ -245,15 +78,6 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
   __shared__ SelectShared<kThreads> sh;
   const int64_t row = blockIdx.x;
   row_topk(scores, ld, row, row_starts[row], row_ends[row], K, out, keys, sh);
-}
-
-// Chunk length of a window on the split path (multiple of 64), or 0 when the
-// row is handled whole by chunk 0 (short windows, and windows too long for 16
-// LDS-resident chunks).
-__device__ __forceinline__ int split_chunk_len(int n) {
-  if (n <= kCap || n > kMaxChunks * kCap) return 0;
-  const int c = (n + kMaxChunks - 1) / kMaxChunks;
-  return (c + kWave - 1) & ~(kWave - 1);
 }
 
 // Split path, phase 1: workgroup (row, c) selects the top-k of chunk c.
@@ -309,10 +133,30 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   }
   __syncthreads();
   const int n = off[kMaxChunks];
-  for (int c = 0; c < kMaxChunks; ++c) {
-    const uint32_t* ck = cand_key + (row * kMaxChunks + c) * int64_t(K);
-    for (int i = threadIdx.x; i < off[c + 1] - off[c]; i += kMergeThreads)
-      keys[off[c] + i] = ck[i];
+  // every thread issues all its candidate loads before storing any of them:
+  // slot s of chunk c for s = tid, tid + kMergeThreads (k <= 2048)
+  {
+    constexpr int kPer = kMaxSplitK / kMergeThreads;
+    uint32_t v[kMaxChunks][kPer];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const uint32_t* ck = cand_key + (row * kMaxChunks + c) * int64_t(K);
+      const int cnt = off[c + 1] - off[c];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int sl = int(threadIdx.x) + j * kMergeThreads;
+        v[c][j] = sl < cnt ? ck[sl] : 0u;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int cnt = off[c + 1] - off[c];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int sl = int(threadIdx.x) + j * kMergeThreads;
+        if (sl < cnt) keys[off[c] + sl] = v[c][j];
+      }
+    }
   }
   __syncthreads();
   int32_t* dst = out + row * int64_t(K);
@@ -334,8 +178,7 @@ bool use_split(int64_t n_q, int64_t n_cols, int32_t K) {
 
 size_t topk_workspace_bytes(int64_t n_q, int64_t n_cols, int32_t K) {
   if (n_q <= 0 || !use_split(n_q, n_cols, K)) return 0;
-  const size_t slots = size_t(n_q) * kMaxChunks;
-  return slots * size_t(K) * (sizeof(uint32_t) + sizeof(int32_t)) + slots * sizeof(int32_t);
+  return Candidates::bytes(n_q, K);
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_starts,
@@ -347,17 +190,19 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
                        ld, row_starts, row_ends, K, out);
     return hipGetLastError();
   }
-  const size_t slots = size_t(n_q) * kMaxChunks;
-  uint32_t* cand_key = static_cast<uint32_t*>(workspace);
-  int32_t* cand_col = reinterpret_cast<int32_t*>(cand_key + slots * K);
-  int32_t* cand_cnt = cand_col + slots * K;
+  const Candidates cd = Candidates::at(workspace, n_q, K);
   hipLaunchKernelGGL(topk_chunk_kernel, dim3(unsigned(n_q), kMaxChunks), dim3(kThreads), 0,
-                     stream, scores, ld, row_starts, row_ends, K, out, cand_key, cand_col,
-                     cand_cnt);
+                     stream, scores, ld, row_starts, row_ends, K, out, cd.key, cd.col, cd.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_topk_merge(row_starts, row_ends, n_q, K, out, workspace, stream);
+}
+
+hipError_t launch_topk_merge(const int32_t* row_starts, const int32_t* row_ends, int64_t n_q,
+                             int32_t K, int32_t* out, void* workspace, hipStream_t stream) {
+  const Candidates cd = Candidates::at(workspace, n_q, K);
   hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(n_q)), dim3(kMergeThreads), 0, stream,
-                     row_starts, row_ends, K, out, cand_key, cand_col, cand_cnt);
+                     row_starts, row_ends, K, out, cd.key, cd.col, cd.cnt);
   return hipGetLastError();
 }
 

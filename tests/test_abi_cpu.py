@@ -84,13 +84,27 @@ def test_indexer_rejects_bad_arguments(lib):
 
 
 def test_indexer_topk_workspace_is_checked(lib):
-    need = lib.dsa_indexer_topk_workspace_size(4, 8, 64, 128, 1, 4)
-    assert need > 0
-    st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, 4, 8, 64, 128, 1, 4, FAKE,
-                              None, 0, None)
-    assert st == WORKSPACE
-    st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, 4, 8, 64, 128, 1, 4, FAKE,
-                              FAKE32, need - 1, None)
+    # few rows over more than 8192 keys (fused: candidate workspace) and many
+    # rows (scores go through the workspace)
+    for n_q, n_k in ((4, 10000), (2000, 8)):
+        need = lib.dsa_indexer_topk_workspace_size(n_q, n_k, 64, 128, 1, 4)
+        assert need > 0
+        st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, n_q, n_k, 64, 128, 1, 4,
+                                  FAKE, None, 0, None)
+        assert st == WORKSPACE
+        st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, n_q, n_k, 64, 128, 1, 4,
+                                  FAKE, FAKE32, need - 1, None)
+        assert st == WORKSPACE
+    # fused with every window inside 8192 keys needs none
+    assert lib.dsa_indexer_topk_workspace_size(4, 8192, 64, 128, 1, 4) == 0
+
+
+def test_topk_workspace_is_checked(lib):
+    need = lib.dsa_topk_workspace_size(4, 10000, 2048)
+    assert need == 4 * 16 * 2048 * 8 + 4 * 16 * 4
+    assert lib.dsa_topk_workspace_size(4, 8192, 2048) == 0       # windows fit one workgroup
+    assert lib.dsa_topk_workspace_size(2000, 10000, 2048) == 0   # many rows: one per workgroup
+    st = lib.dsa_topk(FAKE32, 10000, FAKE, FAKE, 4, 10000, 2048, FAKE, None, 0, None)
     assert st == WORKSPACE
 
 

@@ -173,6 +173,28 @@ def test_topk_prefill4k_oracle_scores(dsa):
     _topk_case(dsa, S, rs, re, P4K.index_topk, "prefill4k")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_topk_fused_matches_unfused(dsa, dtype):
+    # few rows (decode shape): the fused call keeps the scores in LDS and must
+    # return exactly the indices of dsa_indexer_scores + dsa_topk on the same
+    # operands; windows cover the whole-row (<= 8192 keys), split (8193 ..
+    # 131072) and streamed (> 131072) cases
+    w = synth.WORKLOADS["decode" if dtype == "bf16" else "fp8_64k"]
+    lay = synth.layout_from_lengths([5000, 33, 12000, 140000, 70000, 8192, 8193], decode=True)
+    p, rs, re = canonical_indexer(w, lay, dtype, rope=False)
+    q, k, wt, ks = to_device_indexer(p, dtype)
+    say(f"indexer_topk fused vs unfused {dtype}: n_k={lay.n_k}")
+    for K in (2048, 300):
+        S = dsa.dsa_indexer_scores(q, k, wt, i32(rs), i32(re), k_scale=ks)
+        ref = host(dsa.dsa_topk(S, i32(rs), i32(re), K))
+        got = host(dsa.dsa_indexer_topk(q, k, wt, i32(rs), i32(re), K, k_scale=ks))
+        bad = np.nonzero((got != ref).any(axis=1))[0]
+        assert bad.size == 0, f"fused differs on rows {bad}"
+        # and the unfused selection is the oracle's on the GPU's fp32 scores
+        o = o_topk.topk(host(S), rs, re, K)
+        assert np.array_equal(ref, o)
+
+
 # ---------------------------------------------------------------------------
 # indexer scores
 # ---------------------------------------------------------------------------
