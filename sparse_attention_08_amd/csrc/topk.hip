@@ -20,6 +20,8 @@
 // Work layouts:
 //   rows     one workgroup per row; windows of at most 8192 keys are held in
 //            LDS, longer ones are re-read from global memory by each pass;
+//   stream   many rows over more than 8192 columns: one workgroup per row
+//            streams the window through LDS with its running top-k;
 //   split    for few rows with long windows (decode): a row's window is cut into
 //            up to 16 chunks of at most 8192 keys, each workgroup selects its
 //            chunk's top-k into a candidate list (key, column) in the workspace,
@@ -170,6 +172,107 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   for (int p = (n < K ? n : K) + threadIdx.x; p < K; p += kMergeThreads) dst[p] = -1;
 }
 
+// Many rows over more than 8192 columns (k <= 2048): a row is streamed through
+// LDS in pieces of kPiece keys.  The keys that can still be in the top-k are
+// held in LDS with their columns, in column order; a new key enters only if it
+// is above the floor (the k-th key of everything seen at the last shrink: a key
+// not above it can no longer be selected, as on a tie the older, lower column
+// wins).  When a piece's survivors do not fit, the held keys are first shrunk
+// to their top k and the floor raised.  The scores are read once.
+constexpr int kPiece = 4096;
+
+struct StreamShared {
+  uint32_t keys[kMaxSplitK + kPiece];
+  int32_t cols[kMaxSplitK + kPiece];
+  uint32_t tkey[kMaxSplitK];
+  int32_t tcol[kMaxSplitK];
+  uint32_t wcnt[kWaves];
+  SelectShared<kThreads> sel;
+};
+
+__global__ __launch_bounds__(kThreads) void topk_stream_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
+    const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out) {
+  __shared__ StreamShared sh;
+  constexpr int kPer = kPiece / kThreads;  // keys per thread per piece
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int a = row_starts[row];
+  const int b = row_ends[row];
+  const int n = b > a ? b - a : 0;
+  const float* src = scores + row * ld + a;
+  int32_t* dst = out + row * int64_t(K);
+  const uint64_t lt = lanemask_lt();
+
+  int ncand = 0;           // keys held in LDS (the running set, then survivors)
+  uint32_t floor_key = 0;  // keys <= floor_key cannot enter (0: not selectable)
+  for (int lo = 0;; lo += kPiece) {
+    const int m = lo < n ? min(kPiece, n - lo) : 0;
+    // load: wave w owns keys [w*kPiece/4, (w+1)*kPiece/4) of the piece, lane-strided
+    uint32_t v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = wave * (kPiece / kWaves) + j * kWave + lane;
+      v[j] = i < m ? score_key(src[lo + i]) : 0u;
+    }
+    auto survivors = [&]() {  // survivors of this wave's part (uniform per wave)
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) c += __popcll(__ballot(v[j] > floor_key));
+      if (lane == 0) sh.wcnt[wave] = c;
+      __syncthreads();
+      int tot = 0;
+      for (int w = 0; w < kWaves; ++w) tot += int(sh.wcnt[w]);
+      return tot;
+    };
+    int s_all = survivors();
+    if (ncand + s_all > kMaxSplitK + kPiece) {
+      // no room: shrink the held keys to their top k and raise the floor
+      select_topk<kThreads>(LdsKeys{sh.keys}, ncand, uint32_t(ncand), K, sh.sel,
+                            [&](uint32_t p, int i, uint32_t key) {
+                              sh.tkey[p] = key;
+                              sh.tcol[p] = sh.cols[i];
+                            });
+      __syncthreads();
+      uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+      for (int p = tid; p < K; p += kThreads) {
+        sh.keys[p] = sh.tkey[p];
+        sh.cols[p] = sh.tcol[p];
+        kmin = min(kmin, sh.tkey[p]);
+        kmax = max(kmax, sh.tkey[p]);
+      }
+      block_min_max<kThreads>(kmin, kmax, sh.sel.tmp);  // also orders the copies
+      ncand = K;
+      floor_key = kmin;  // the k-th key of everything seen so far
+      s_all = survivors();
+    }
+    // ordered compaction of the survivors behind the held keys
+    int base = ncand;
+    for (int w = 0; w < wave; ++w) base += int(sh.wcnt[w]);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const bool keep = v[j] > floor_key;
+      const uint64_t bal = __ballot(keep);
+      if (keep) {
+        const int at = base + __popcll(bal & lt);
+        sh.keys[at] = v[j];
+        sh.cols[at] = a + lo + wave * (kPiece / kWaves) + j * kWave + lane;
+      }
+      base += __popcll(bal);
+    }
+    ncand += s_all;
+    __syncthreads();
+    if (lo + m >= n) {
+      select_topk<kThreads>(LdsKeys{sh.keys}, ncand, uint32_t(ncand), K, sh.sel,
+                            [&](uint32_t p, int i, uint32_t) { dst[p] = sh.cols[i]; });
+      for (int p = (ncand < K ? ncand : K) + tid; p < K; p += kThreads) dst[p] = -1;
+      return;
+    }
+  }
+}
+
 bool use_split(int64_t n_q, int64_t n_cols, int32_t K) {
   return n_cols > kCap && K <= kMaxSplitK && n_q <= kMaxSplitRows;
 }
@@ -185,6 +288,11 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
                        const int32_t* row_ends, int64_t n_q, int64_t n_cols, int32_t K,
                        int32_t* out, void* workspace, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
+  if (!use_split(n_q, n_cols, K) && n_cols > kCap && K <= kMaxSplitK) {
+    hipLaunchKernelGGL(topk_stream_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
+                       ld, row_starts, row_ends, K, out);
+    return hipGetLastError();
+  }
   if (!use_split(n_q, n_cols, K)) {
     hipLaunchKernelGGL(topk_rows_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
                        ld, row_starts, row_ends, K, out);

@@ -149,17 +149,33 @@ def test_topk_rows_longer_than_split(dsa):
     _topk_case(dsa, S, rs, re, 2048, "longer than split")
 
 
-def test_topk_many_long_rows_global_path(dsa):
-    # more than 1024 rows over more than 8192 columns: one workgroup per row,
-    # re-reading windows longer than 8192 from memory
+def test_topk_many_long_rows_stream_path(dsa):
+    # more than 1024 rows over more than 8192 columns: one workgroup per row
+    # streams the window through LDS with its running top-k
     g = np.random.default_rng(105)
     n_q, n = 1100, 9000
     S = g.standard_normal((n_q, n)).astype(np.float32)
-    S[::4] = np.round(S[::4] * 2) / 2
+    S[::4] = np.round(S[::4] * 2) / 2                       # ties across pieces
+    S[1::4, ::3] = -np.inf                                  # unselectable keys
+    S[2::8] = -np.inf
+    S[2::8, 4000:4100] = 1.0                                # fewer selectable keys than k
     rs = g.integers(0, 500, n_q).astype(np.int32)
     re = np.minimum(n, rs + g.integers(7000, 9000, n_q)).astype(np.int32)
+    re[:5] = rs[:5] + np.array([0, 1, 4096, 4097, 8192])    # empty and piece-boundary windows
     assert dsa._lib_or_load().dsa_topk_workspace_size(n_q, n, 2048) == 0
-    _topk_case(dsa, S, rs, re, 2048, "many long rows")
+    for K in (2048, 333, 1):
+        _topk_case(dsa, S, rs, re, K, f"stream K={K}")
+
+
+def test_topk_many_rows_large_k_global_path(dsa):
+    # k above 2048 over long windows: one workgroup per row re-reads from memory
+    g = np.random.default_rng(106)
+    n_q, n = 40, 12000
+    S = g.standard_normal((n_q, n)).astype(np.float32)
+    S[::3] = np.round(S[::3] * 3) / 3
+    rs = np.zeros(n_q, np.int32)
+    re = g.integers(9000, n, n_q).astype(np.int32)
+    _topk_case(dsa, S, rs, re, 3000, "large k")
 
 
 def test_topk_prefill4k_oracle_scores(dsa):
