@@ -52,15 +52,20 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kKT = 32;                         // selected keys per tile
 constexpr int kRowBytes = kDqk * 2;             // 1152 bytes = 72 chunks of 16
-constexpr int kRowChunks = kRowBytes / 16 + 1;  // 73: one pad chunk per LDS row
-constexpr int kKvStride = kRowChunks * 16;      // 1168: padded LDS row
-constexpr int kTileChunks = kKT * kRowChunks;   // 2336
-constexpr int kDmaPerTile = (kTileChunks + kWave - 1) / kWave;  // 37 wave loads of 1 KB
+// LDS tile of 32 latent rows: region A holds each key's 512 latent dims (1024
+// bytes, the value and the first 512 dims of the key) in rows 1040 bytes apart
+// (16-byte fragment reads of 16 consecutive keys hit 16 different bank groups);
+// region B holds the 64 rope dims (128 bytes) of every key, its 16-byte pieces
+// XOR-swizzled by the key so that those reads are conflict-free too.
+constexpr int kRowA = 1072;                     // region A row stride
+constexpr int kRegionA = kKT * kRowA;           // 33280
+constexpr int kRegionB = kKT * 128;             // 4096
+constexpr int kTileBytes = kRegionA + kRegionB;  // 37376
 constexpr int kQSteps = kDqk / 16;              // 36 K-steps of 16 dims
 constexpr int kVTiles = kDv / 32;               // 16 value tiles of 32 columns
 constexpr int kThreads = 256;                   // 4 waves x 32 heads
 constexpr int kWaves = kThreads / kWave;
-constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // 10 (wave 0), else 9
+constexpr int kDmaPerWave = kKT / kWaves + 1;  // 8 latent rows + 1 rope load: 9
 constexpr int kHeadsPerBlock = kWaves * 32;     // 128
 constexpr int kMaxIdx = 2048;                   // selected keys per workgroup (LDS-staged)
 constexpr int kMaxTiles = kMaxIdx / kKT;
@@ -93,10 +98,10 @@ struct MlaShared {
 // wait for the LDS-DMA still writing another.  Tile i lives in buffer i % 4;
 // while tile i is computed, tile i-1 is still read (P.V) and tiles i+1, i+2
 // are in flight.
-__shared__ __attribute__((aligned(16))) uint8_t g_kv0[kKT * kKvStride];
-__shared__ __attribute__((aligned(16))) uint8_t g_kv1[kKT * kKvStride];
-__shared__ __attribute__((aligned(16))) uint8_t g_kv2[kKT * kKvStride];
-__shared__ __attribute__((aligned(16))) uint8_t g_kv3[kKT * kKvStride];
+__shared__ __attribute__((aligned(16))) uint8_t g_kv0[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_kv1[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_kv2[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_kv3[kTileBytes];
 
 template <int B>
 __device__ __forceinline__ uint8_t* kvbuf() {
@@ -137,73 +142,82 @@ __device__ __forceinline__ void o_fence(f32x16_t (&o)[kVTiles]) {
                  "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
 }
 
-static_assert(kTileChunks <= 2400, "the c / 73 multiply-shift holds for c < 2400");
-
-// LDS-DMA of a tile: wave-load j = wave + 4u copies LDS chunks [64j, 64j+64) of
-// the padded tile; chunk c is (key c/73, 16-byte piece c%73 of that key's latent
-// row; piece 72 is the row pad and repeats piece 71).  sidx holds the staged rows
-// with -1 replaced by row 0 (masked later).  Wave 0 issues 10 loads per tile
-// (the 37th covers 32 chunks), the other waves 9.
-__device__ __forceinline__ int dma_key(int c) {
-  const int k = (c * 1796) >> 17;  // c / 73
-  return k < kKT ? k : kKT - 1;
+// LDS-DMA of local tile lt into buffer B by one wave: the latent rows of keys
+// wave, wave+4, ..., wave+28 (one 1 KB load each: the row index is the same for
+// the whole wave, so the address is a scalar base plus lane * 16), then the rope
+// dims of keys 8*wave .. 8*wave+7 (lane = 8 * key + slot, slot holding rope piece
+// slot ^ ((key >> 1) & 7)).  sidx holds the staged rows with -1 replaced by row
+// 0 (masked later).
+//
+// The loads are issued through inline asm.  The compiler counts an LDS-DMA it
+// issues itself on both the vector-memory and the LDS counters, and with one in
+// flight it can only wait for LDS reads with a full drain (lgkmcnt(0)), which
+// would empty the fragment rings of both MFMA phases.  The asm loads are
+// invisible to its counting: their only wait is the explicit one in wait_tile
+// (vector-memory count), and the DMA writes no registers.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((lds_void_ptr)p));
 }
 
-// rows of this lane's chunks for tile lt (read from the staged slice)
-__device__ __forceinline__ void dma_rows(const int* sidx, int lt, int wave, int lane,
-                                         uint32_t (&row)[kDmaPerWave]) {
-  // the per-lane pieces are recomputed for every tile: held across the tile
-  // loop they would take registers the loop needs
-  asm volatile("" : "+v"(lane));
-#pragma unroll
-  for (int u = 0; u < kDmaPerWave; ++u)
-    row[u] = uint32_t(sidx[lt * kKT + dma_key((wave + kWaves * u) * kWave + lane)]);
+// The rows one wave's loads of tile lt need, read from the staged slice ahead
+// of the loads: lane l holds the row of key l % 32 (the latent loads take theirs
+// with readlane) and the row of its rope key 8 * wave + l / 8.
+struct DmaRows {
+  int key;
+  int rope;
+};
+__device__ __forceinline__ DmaRows dma_rows(const int* sidx, int lt, int wave, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));  // recomputed here, not held in registers
+  return {sidx[lt * kKT + (l & 31)], sidx[lt * kKT + 8 * wave + (l >> 3)]};
 }
 
-// row of this lane's chunk of wave-load u of tile lt
-__device__ __forceinline__ uint32_t dma_row(const int* sidx, int lt, int u, int wave, int lane) {
-  asm volatile("" : "+v"(lane));  // recomputed here, not held in registers
-  return uint32_t(sidx[lt * kKT + dma_key((wave + kWaves * u) * kWave + lane)]);
-}
-
-// issue wave-load u of the tile into buffer B
 template <int B>
-__device__ __forceinline__ void dma_issue(int u, uint32_t row, const uint8_t* __restrict__ kv,
-                                          int wave, int lane) {
-  static_assert(kDmaPerTile == kWaves * (kDmaPerWave - 1) + 1, "load split");
-  // loads u < 9 are full for every wave; load 9 is wave 0's 37th (32 chunks)
-  if (u == kDmaPerWave - 1 && !(wave == 0 && lane < kTileChunks - (kDmaPerTile - 1) * kWave))
-    return;
-  asm volatile("" : "+v"(lane));  // recomputed here, not held in registers
-  const int j = wave + kWaves * u;
-  const int c = j * kWave + lane;
-  int cc = c - dma_key(c) * kRowChunks;
-  cc = cc < kRowChunks - 1 ? cc : kRowChunks - 2;
-  const uint8_t* src = kv + (uint64_t(row) * kRowBytes + uint32_t(cc * 16));
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(kvbuf<B>() + j * kWave * 16), 16, 0, 0);
+__device__ __forceinline__ void dma_latent(const DmaRows& rows, int u,
+                                           const uint8_t* __restrict__ kv, int wave, int lane) {
+  const int r = wave + kWaves * u;
+  const uint32_t row = uint32_t(__builtin_amdgcn_readlane(rows.key, r));
+  const uint64_t base = reinterpret_cast<uint64_t>(kv) + uint64_t(row) * kRowBytes;
+  const uint32_t vofs = uint32_t(lane) * 16u;
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(vofs), "s"(base), "{m0}"(lds_addr(kvbuf<B>() + r * kRowA))
+               : "memory");
+}
+
+template <int B>
+__device__ __forceinline__ void dma_rope(const DmaRows& rows, const uint8_t* __restrict__ kv,
+                                         int wave, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));  // recomputed here, not held in registers
+  const int key = 8 * wave + (l >> 3);
+  const int piece = (l & 7) ^ ((key >> 1) & 7);
+  const uint8_t* src = kv + uint64_t(uint32_t(rows.rope)) * kRowBytes + 1024 + piece * 16;
+  asm volatile("global_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(lds_addr(kvbuf<B>() + kRegionA + wave * 1024))
+               : "memory");
 }
 
 template <int B>
 __device__ __forceinline__ void dma_tile(const int* sidx, int lt, const uint8_t* __restrict__ kv,
                                          int wave, int lane) {
-  uint32_t row[kDmaPerWave];
-  dma_rows(sidx, lt, wave, lane, row);
+  const DmaRows rows = dma_rows(sidx, lt, wave, lane);
 #pragma unroll
-  for (int u = 0; u < kDmaPerWave; ++u) dma_issue<B>(u, row[u], kv, wave, lane);
+  for (int u = 0; u < kKT / kWaves; ++u) dma_latent<B>(rows, u, kv, wave, lane);
+  dma_rope<B>(rows, kv, wave, lane);
 }
 
 // Wait until this wave's LDS-DMA of the current tile has landed.  The next
-// tile's loads (issued one tile later, vector-memory counters retire in order)
-// may stay in flight: wave 0 issues 10 loads per tile, the others 9.
-__device__ __forceinline__ void wait_tile(bool next_in_flight, int wave) {
-  if (!next_in_flight) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  } else if (wave == 0) {
-    __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
-  } else {
+// tile's 9 loads (issued one tile later, vector-memory counters retire in
+// order) may stay in flight.
+__device__ __forceinline__ void wait_tile(bool next_in_flight) {
+  if (next_in_flight) {
     __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
-  static_assert(kDmaPerWave == 10 && (kDmaPerTile - 1) % kWaves == 0, "vmcnt immediates");
+  static_assert(kDmaPerWave == 9, "vmcnt immediate");
 }
 
 // S^T = K . Q^T for the tile in buffer B: keys on M, the wave's 32 heads on N,
@@ -215,24 +229,36 @@ template <int B, int BD, bool kDma>
 __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], int lane,
                                             const int* sidx, int lt_dma,
                                             const uint8_t* __restrict__ kv, int wave) {
-  const uint8_t* ka = kvbuf<B>() + (lane & 31) * kKvStride + (lane >> 5) * 16;
+  const int kk = lane & 31;
+  const int h = lane >> 5;
+  const uint8_t* ka = kvbuf<B>() + kk * kRowA + h * 16;        // latent K-steps 0..31
+  auto frag = [&](int st) {
+    if (st < 32) return *reinterpret_cast<const bf16x8_t*>(ka + st * 32);
+    // rope K-steps 32..35: the swizzled address is recomputed for each read,
+    // not held in registers across the tile loop
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    const int r = l & 31;
+    const int piece = (2 * (st - 32) + (l >> 5)) ^ ((r >> 1) & 7);
+    return *reinterpret_cast<const bf16x8_t*>(kvbuf<B>() + kRegionA + r * 128 + piece * 16);
+  };
+  DmaRows rows{};
+  if constexpr (kDma) rows = dma_rows(sidx, lt_dma, wave, lane);  // ahead of the ring reads
   bf16x8_t fr[kRingQ];
 #pragma unroll
-  for (int st = 0; st < kRingQ; ++st) fr[st] = *reinterpret_cast<const bf16x8_t*>(ka + st * 32);
+  for (int st = 0; st < kRingQ; ++st) fr[st] = frag(st);
   f32x16_t s;
-  uint32_t row = 0u;
 #pragma unroll
   for (int st = 0; st < kQSteps; ++st) {
     const bf16x8_t a = fr[st % kRingQ];
-    if (st + kRingQ < kQSteps)
-      fr[st % kRingQ] = *reinterpret_cast<const bf16x8_t*>(ka + (st + kRingQ) * 32);
+    if (st + kRingQ < kQSteps) fr[st % kRingQ] = frag(st + kRingQ);
     if (st == 0) mfma_v0(s, a, qf[st]);
     else if (st + 1 < kQSteps) mfma_v(s, a, qf[st]);
     else mfma_v_last(s, a, qf[st]);
     if constexpr (kDma) {
-      // the row of load u is read one MFMA before the load is issued
-      if (st % 3 == 0 && st / 3 < kDmaPerWave) row = dma_row(sidx, lt_dma, st / 3, wave, lane);
-      if (st % 3 == 1 && st / 3 < kDmaPerWave) dma_issue<BD>(st / 3, row, kv, wave, lane);
+      // the gather of a later tile, spread between the MFMAs
+      if (st % 4 == 1 && st / 4 < kKT / kWaves) dma_latent<BD>(rows, st / 4, kv, wave, lane);
+      if (st == 33) dma_rope<BD>(rows, kv, wave, lane);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep this order
   }
@@ -354,14 +380,14 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
   const int grp = lane >> 4;      // 16-lane group
   const int li = lane & 15;
   const int n0 = 16 * (grp & 1);  // value column offset of the group inside a 32-wide tile
-  const uint8_t* vb = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) + (li >> 2) * kKvStride +
-                      (n0 + 4 * (li & 3)) * 2 + 4 * half * kKvStride;
+  const uint8_t* vb = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) + (li >> 2) * kRowA +
+                      (n0 + 4 * (li & 3)) * 2 + 4 * half * kRowA;
   // step m = 2n + ks: value tile n, key step ks; reads run kRingV steps ahead
   auto rd = [&](int m) {
-    const uint8_t* base = vb + 16 * (m & 1) * kKvStride + (m >> 1) * 64;
+    const uint8_t* base = vb + 16 * (m & 1) * kRowA + (m >> 1) * 64;
     const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
     const v4i16_t b =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kKvStride));
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kRowA));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   bf16x8_t fr[kRingV];
@@ -385,13 +411,13 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
 template <int B>
 __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const uint8_t* kvb,
                                           const bf16x8_t (&qf)[kQSteps], f32x16_t (&o)[kVTiles],
-                                          bf16x8_t& p0, bf16x8_t& p1, float& m_ref,
-                                          float& m_max, bool& over, float& l_run, float scale2,
-                                          int wave, int lane) {
-  wait_tile(i + 1 < nt, wave);
+                                          bf16x8_t& p0, bf16x8_t& p1, uint32_t& vm,
+                                          float& m_ref, float& m_max, bool& over, float& l_run,
+                                          float scale2, int wave, int lane) {
+  wait_tile(i + 1 < nt);
   __builtin_amdgcn_s_barrier();
   Softmax sm;
-  sm.vmask = sh.vmask[i];
+  sm.vmask = vm;
   if (i + 2 < nt) {
     sm.s = qk_tile<B, (B + 2) & 3, true>(qf, lane, sh.idx, i + 2, kvb, wave);
   } else {
@@ -400,6 +426,7 @@ __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const ui
   pv_tile<(B + 3) & 3, true>(nullptr, p0, p1, o, lane, sm, scale2, m_ref, m_max, over, l_run);
   p0 = sm.p0;
   p1 = sm.p1;
+  vm = sh.vmask[i + 1];  // the next tile's mask, read well before it is needed
 }
 
 // One workgroup: one query x 128 heads (wave w: heads 32w .. 32w+31 of the
@@ -489,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     if (nt4 > 1) dma_tile<1>(sh.idx, 1, kvb, wave, lane);
     if (nt4 > 0) {
       // tile 0: no P.V yet
-      wait_tile(nt4 > 1, wave);
+      wait_tile(nt4 > 1);
       __builtin_amdgcn_s_barrier();
       if (nt4 > 2) dma_tile<2>(sh.idx, 2, kvb, wave, lane);
       {
@@ -500,15 +527,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
         p0 = sm.p0;
         p1 = sm.p1;
       }
+      uint32_t vm = sh.vmask[1];
       // tiles 1 .. nt4-1 in groups of four (one exit: a loop left in the middle
       // makes the register allocator copy O out of the accumulation registers)
       for (int i = 1; i < nt4; i += 4) {
-        tile_step<1>(sh, i, nt4, kvb, qf, o, p0, p1, m_ref, m_max, over, l_run, scale2, wave, lane);
-        tile_step<2>(sh, i + 1, nt4, kvb, qf, o, p0, p1, m_ref, m_max, over, l_run, scale2, wave,
+        tile_step<1>(sh, i, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave, lane);
+        tile_step<2>(sh, i + 1, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
                      lane);
-        tile_step<3>(sh, i + 2, nt4, kvb, qf, o, p0, p1, m_ref, m_max, over, l_run, scale2, wave,
+        tile_step<3>(sh, i + 2, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
                      lane);
-        tile_step<0>(sh, i + 3, nt4, kvb, qf, o, p0, p1, m_ref, m_max, over, l_run, scale2, wave,
+        tile_step<0>(sh, i + 3, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
                      lane);
       }
       // P.V of the last tile: no gather is in flight any more, so its buffer can
