@@ -52,13 +52,26 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kKT = 32;                         // selected keys per tile
 constexpr int kRowBytes = kDqk * 2;             // 1152 bytes = 72 chunks of 16
-// LDS tile of 32 latent rows: region A holds each key's 512 latent dims (1024
-// bytes, the value and the first 512 dims of the key) in rows 1040 bytes apart
-// (16-byte fragment reads of 16 consecutive keys hit 16 different bank groups);
-// region B holds the 64 rope dims (128 bytes) of every key, its 16-byte pieces
-// XOR-swizzled by the key so that those reads are conflict-free too.
-constexpr int kRowA = 1072;                     // region A row stride
+// LDS tile of 32 latent rows.  Region A holds each key's 512 latent dims (1024
+// bytes: the value and the first 512 dims of the key) in 32 slots 1040 bytes
+// apart; key j of the tile sits in slot kslot(j), which swaps the two 2-bit
+// digits of j % 16.  Slot starts fall 16 bytes apart modulo 256, so
+//   * a 16-byte K-fragment read of 16 consecutive keys touches 16 different
+//     16-byte bank groups, and
+//   * a transposed V read (keys 4g .. 4g+3, 64 bytes of each) touches four
+//     disjoint 64-byte bank windows;
+// both are free of bank conflicts.  Region B holds the 64 rope dims (128 bytes)
+// of every key, its 16-byte pieces XOR-swizzled by the key so that those reads
+// are conflict-free too.
+constexpr int kRowA = 1040;                     // region A slot stride
+__host__ __device__ constexpr int kslot(int j) { return 4 * (j & 3) + ((j >> 2) & 3) + (j & 16); }
 constexpr int kRegionA = kKT * kRowA;           // 33280
+constexpr bool kslot_is_permutation() {
+  uint32_t seen = 0;
+  for (int j = 0; j < kKT; ++j) seen |= 1u << kslot(j);
+  return seen == 0xFFFFFFFFu;
+}
+static_assert(kslot_is_permutation(), "slots are a permutation of 0 .. 31");
 constexpr int kRegionB = kKT * 128;             // 4096
 constexpr int kTileBytes = kRegionA + kRegionB;  // 37376
 constexpr int kQSteps = kDqk / 16;              // 36 K-steps of 16 dims
@@ -132,7 +145,7 @@ __device__ __forceinline__ void mfma_v_last(f32x16_t& d, bf16x8_t a, bf16x8_t b)
 // accumulation into O; the leading nops cover a VALU-written operand
 // (P, a repacked V fragment, or a rescaled O)
 __device__ __forceinline__ void mfma_a(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 // before the VALU touches O after MFMAs into it
 __device__ __forceinline__ void o_fence(f32x16_t (&o)[kVTiles]) {
@@ -181,7 +194,7 @@ __device__ __forceinline__ void dma_latent(const DmaRows& rows, int u,
   const uint32_t vofs = uint32_t(lane) * 16u;
   asm volatile("global_load_lds_dwordx4 %0, %1"
                :
-               : "v"(vofs), "s"(base), "{m0}"(lds_addr(kvbuf<B>() + r * kRowA))
+               : "v"(vofs), "s"(base), "{m0}"(lds_addr(kvbuf<B>() + kslot(r) * kRowA))
                : "memory");
 }
 
@@ -226,12 +239,12 @@ __device__ __forceinline__ void wait_tile(bool next_in_flight) {
 // LDS-DMA loads of a later tile (into buffer BD) are issued between the MFMAs
 // (the wave can issue them while the matrix core works).
 template <int B, int BD, bool kDma>
-__device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], int lane,
-                                            const int* sidx, int lt_dma,
+__device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint32_t vmask,
+                                            int lane, const int* sidx, int lt_dma,
                                             const uint8_t* __restrict__ kv, int wave) {
   const int kk = lane & 31;
   const int h = lane >> 5;
-  const uint8_t* ka = kvbuf<B>() + kk * kRowA + h * 16;        // latent K-steps 0..31
+  const uint8_t* ka = kvbuf<B>() + kslot(kk) * kRowA + h * 16;  // latent K-steps 0..31
   auto frag = [&](int st) {
     if (st < 32) return *reinterpret_cast<const bf16x8_t*>(ka + st * 32);
     // rope K-steps 32..35: the swizzled address is recomputed for each read,
@@ -253,8 +266,7 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], int l
     const bf16x8_t a = fr[st % kRingQ];
     if (st + kRingQ < kQSteps) fr[st % kRingQ] = frag(st + kRingQ);
     if (st == 0) mfma_v0(s, a, qf[st]);
-    else if (st + 1 < kQSteps) mfma_v(s, a, qf[st]);
-    else mfma_v_last(s, a, qf[st]);
+    else mfma_v(s, a, qf[st]);
     if constexpr (kDma) {
       // the gather of a later tile, spread between the MFMAs
       if (st % 4 == 1 && st / 4 < kKT / kWaves) dma_latent<BD>(rows, st / 4, kv, wave, lane);
@@ -262,64 +274,91 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], int l
     }
     __builtin_amdgcn_sched_barrier(0);  // keep this order
   }
+  // The key mask as one more K-step: dim 0 of the step is -inf for a masked key
+  // (lanes 0..31 of the K side) against 1 on the Q side, every other product is
+  // 0 * 0, so S = -inf exactly for masked keys and unchanged for the others.
+  // Lanes 32..63 carry dims 8..15 of the step: zero on both sides.
+  {
+    const uint64_t keep =
+        uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(vmask)))) | 0xFFFFFFFF00000000ull;
+    // operands are rebuilt for every tile, not held in registers across the loop
+    int l = lane, ninf = 0xFF80;
+    asm volatile("" : "+v"(l), "+v"(ninf));
+    i32x4_t ka = {0, 0, 0, 0};
+    asm("v_cndmask_b32_e64 %0, %1, 0, %2" : "=v"(ka[0]) : "v"(ninf), "s"(keep));
+    const i32x4_t qa = {l < 32 ? 0x3F80 : 0, 0, 0, 0};
+    mfma_v_last(s, __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qa));
+  }
   return s;
 }
 
 // Softmax of one tile against a fixed per-head reference m_ref (base-2 units,
-// same in both lane halves): P = 2^(S - m_ref).  m_ref is the max of the first
-// tile that has a finite logit for the head, so P <= 2^kSpan unless a later
-// tile's max exceeds m_ref + kSpan; that sets `over` and the query is computed
-// again with m_ref = the true max (m_max tracks it).  O is never rescaled
-// inside the loop.  The work is cut into kSmStages stages that the P.V of the
-// previous tile interleaves with its MFMAs.
+// same in both lane halves): P = 2^(S * scale2 - m_ref).  Masked keys already
+// hold S = -inf (the bias step of the QK chain), so P = 0 for them.  m_ref is
+// the max of the first tile that has a finite logit for the head, so
+// P <= 2^kSpan unless a later tile's max exceeds m_ref + kSpan; that sets
+// `over` and the query is computed again with m_ref = the true max (m_max
+// tracks it).  O is never rescaled inside the loop.  The work is cut into
+// kSmStages stages that the P.V of the previous tile interleaves with its
+// MFMAs.
 struct Softmax {
   f32x16_t s;      // S^T of the tile: lane = head l%32, 16 keys
-  uint32_t vmask;  // valid keys of the tile
   float mt;
   float ps;
   bf16x8_t p0, p1;
 
+  // The stage's inputs pass through an empty volatile asm first: the stage
+  // is pure arithmetic, which the instruction selector would otherwise place
+  // anywhere (in practice all of it ahead of the P.V MFMAs it is meant to hide
+  // behind).
+  template <int K>
+  __device__ __forceinline__ void pin() {
+    if constexpr (K == 0) {
+      asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]), "+v"(s[4]), "+v"(s[5]),
+                   "+v"(s[6]), "+v"(s[7]));
+      asm volatile("" : "+v"(s[8]), "+v"(s[9]), "+v"(s[10]), "+v"(s[11]), "+v"(s[12]),
+                   "+v"(s[13]), "+v"(s[14]), "+v"(s[15]));
+    } else if constexpr (K == 1) {
+      asm volatile("" : "+v"(mt));
+    } else if constexpr (K < 6) {
+      const int r0 = 4 * (K - 2);
+      asm volatile("" : "+v"(s[r0]), "+v"(s[r0 + 1]), "+v"(s[r0 + 2]), "+v"(s[r0 + 3]));
+    } else {
+      const int r0 = 4 * (K - 6);
+      asm volatile("" : "+v"(s[r0]), "+v"(s[r0 + 1]), "+v"(s[r0 + 2]), "+v"(s[r0 + 3]),
+                   "+v"(s[r0 + 8]), "+v"(s[r0 + 9]), "+v"(s[r0 + 10]), "+v"(s[r0 + 11]));
+    }
+  }
+
   template <int K>
   __device__ __forceinline__ void stage(float scale2, float& m_ref, float& m_max, bool& over,
                                         float& l_run) {
-    if constexpr (K < 4) {
-      // key validity as per-register lane masks built on the scalar unit:
-      // register r holds key 8*(r/4) + r%4 in lanes 0..31 and that key + 4 in
-      // lanes 32..63
-      const float neg_inf = -INFINITY;
-#pragma unroll
-      for (int r = 4 * K; r < 4 * K + 4; ++r) {
-        const int kr = 8 * (r >> 2) + (r & 3);
-        const uint64_t lm = (((vmask >> kr) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
-                            (((vmask >> (kr + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
-        const float x = s[r] * scale2;
-        asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(s[r]) : "v"(neg_inf), "v"(x), "s"(lm));
-      }
-    } else if constexpr (K == 4) {
+    pin<K>();
+    if constexpr (K == 0) {
       mt = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-    } else if constexpr (K == 5) {
+    } else if constexpr (K == 1) {
       // lanes l and l^32 hold the two key halves of head l%32
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                        false, false);
-      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
       // -FLT_MAX = no finite logit yet (an all-masked tile keeps it)
       m_ref = m_ref == -FLT_MAX ? fmaxf(mt, -FLT_MAX) : m_ref;
       m_max = fmaxf(m_max, mt);
       over = over || mt > m_ref + kSpan;
-    } else if constexpr (K < 10) {
+    } else if constexpr (K < 6) {
 #pragma unroll
-      for (int r = 4 * (K - 6); r < 4 * (K - 6) + 4; ++r)
-        s[r] = __builtin_amdgcn_exp2f(s[r] - m_ref);
+      for (int r = 4 * (K - 2); r < 4 * (K - 2) + 4; ++r)
+        s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale2, -m_ref));
     } else {
       // P rounded to bf16 (v_cvt_pk_bf16_f32, round to nearest even); the row
       // sum adds the rounded values (v_dot2 with ones), so the output is an
       // exact convex combination of value rows up to fp32 accumulation
       const bf16x2_t ones = {__bf16(1.0f), __bf16(1.0f)};
-      if constexpr (K == 10) ps = 0.0f;
+      if constexpr (K == 6) ps = 0.0f;
 #pragma unroll
-      for (int r = 4 * (K - 10); r < 4 * (K - 10) + 4; r += 2) {
+      for (int r = 4 * (K - 6); r < 4 * (K - 6) + 4; r += 2) {
         const bf16x2_t a = {__bf16(s[r]), __bf16(s[r + 1])};
         const bf16x2_t b = {__bf16(s[r + 8]), __bf16(s[r + 9])};
         ps = __builtin_amdgcn_fdot2_f32_bf16(a, ones, ps, false);
@@ -329,11 +368,11 @@ struct Softmax {
         p1[r] = b[0];
         p1[r + 1] = b[1];
       }
-      if constexpr (K == 11) l_run += ps;
+      if constexpr (K == 7) l_run += ps;
     }
   }
 };
-constexpr int kSmStages = 12;
+constexpr int kSmStages = 8;
 
 template <int K>
 __device__ __forceinline__ void sm_stage_if(int k, Softmax& sm, float scale2, float& m_ref,
@@ -351,10 +390,6 @@ __device__ __forceinline__ void sm_stage(int k, Softmax& sm, float scale2, float
   sm_stage_if<5>(k, sm, scale2, m_ref, m_max, over, l_run);
   sm_stage_if<6>(k, sm, scale2, m_ref, m_max, over, l_run);
   sm_stage_if<7>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<8>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<9>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<10>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<11>(k, sm, scale2, m_ref, m_max, over, l_run);
 }
 
 __device__ __forceinline__ void softmax_all(Softmax& sm, float scale2, float& m_ref,
@@ -380,14 +415,16 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
   const int grp = lane >> 4;      // 16-lane group
   const int li = lane & 15;
   const int n0 = 16 * (grp & 1);  // value column offset of the group inside a 32-wide tile
-  const uint8_t* vb = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) + (li >> 2) * kRowA +
-                      (n0 + 4 * (li & 3)) * 2 + 4 * half * kRowA;
+  // key (li >> 2) + 4 * half (+ 8, + 16 per read and step) is in slot
+  // 4 * (li >> 2) + half (+ 2, + 16)
+  const uint8_t* vb = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) +
+                      (4 * (li >> 2) + half) * kRowA + (n0 + 4 * (li & 3)) * 2;
   // step m = 2n + ks: value tile n, key step ks; reads run kRingV steps ahead
   auto rd = [&](int m) {
     const uint8_t* base = vb + 16 * (m & 1) * kRowA + (m >> 1) * 64;
     const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
     const v4i16_t b =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kRowA));
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 2 * kRowA));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   bf16x8_t fr[kRingV];
@@ -417,11 +454,10 @@ __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const ui
   wait_tile(i + 1 < nt);
   __builtin_amdgcn_s_barrier();
   Softmax sm;
-  sm.vmask = vm;
   if (i + 2 < nt) {
-    sm.s = qk_tile<B, (B + 2) & 3, true>(qf, lane, sh.idx, i + 2, kvb, wave);
+    sm.s = qk_tile<B, (B + 2) & 3, true>(qf, vm, lane, sh.idx, i + 2, kvb, wave);
   } else {
-    sm.s = qk_tile<B, 0, false>(qf, lane, sh.idx, 0, kvb, wave);
+    sm.s = qk_tile<B, 0, false>(qf, vm, lane, sh.idx, 0, kvb, wave);
   }
   pv_tile<(B + 3) & 3, true>(nullptr, p0, p1, o, lane, sm, scale2, m_ref, m_max, over, l_run);
   p0 = sm.p0;
@@ -521,8 +557,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       if (nt4 > 2) dma_tile<2>(sh.idx, 2, kvb, wave, lane);
       {
         Softmax sm;
-        sm.vmask = sh.vmask[0];
-        sm.s = qk_tile<0, 0, false>(qf, lane, sh.idx, 0, kvb, wave);
+        sm.s = qk_tile<0, 0, false>(qf, sh.vmask[0], lane, sh.idx, 0, kvb, wave);
         softmax_all(sm, scale2, m_ref, m_max, over, l_run);
         p0 = sm.p0;
         p1 = sm.p1;
