@@ -61,8 +61,8 @@ constexpr int kRowBytes = kDqk * 2;             // 1152 bytes = 72 chunks of 16
 //   * a transposed V read (keys 4g .. 4g+3, 64 bytes of each) touches four
 //     disjoint 64-byte bank windows;
 // both are free of bank conflicts.  Region B holds the 64 rope dims (128 bytes)
-// of every key, its 16-byte pieces XOR-swizzled by the key so that those reads
-// are conflict-free too.
+// of every key piece-major: 16-byte piece p of key j at p * 512 + j * 16, so a
+// rope fragment read of 16 consecutive keys is 256 contiguous bytes.
 constexpr int kRowA = 1040;                     // region A slot stride
 __host__ __device__ constexpr int kslot(int j) { return 4 * (j & 3) + ((j >> 2) & 3) + (j & 16); }
 constexpr int kRegionA = kKT * kRowA;           // 33280
@@ -137,9 +137,10 @@ __device__ __forceinline__ void mfma_v0(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
 __device__ __forceinline__ void mfma_v(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-// last MFMA of a chain whose result the VALU reads next
+// last MFMA of a chain whose result the VALU reads next; its operands are
+// VALU-written just before (the leading nop)
 __device__ __forceinline__ void mfma_v_last(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3"
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3"
       : "+v"(d) : "v"(a), "v"(b));
 }
 // accumulation into O; the leading nops cover a VALU-written operand
@@ -157,10 +158,10 @@ __device__ __forceinline__ void o_fence(f32x16_t (&o)[kVTiles]) {
 
 // LDS-DMA of local tile lt into buffer B by one wave: the latent rows of keys
 // wave, wave+4, ..., wave+28 (one 1 KB load each: the row index is the same for
-// the whole wave, so the address is a scalar base plus lane * 16), then the rope
-// dims of keys 8*wave .. 8*wave+7 (lane = 8 * key + slot, slot holding rope piece
-// slot ^ ((key >> 1) & 7)).  sidx holds the staged rows with -1 replaced by row
-// 0 (masked later).
+// the whole wave, so the address is a scalar base plus lane * 16), then rope
+// pieces 2*wave and 2*wave+1 of all 32 keys (lane l: key l % 32, piece
+// 2*wave + l / 32).  sidx holds the staged rows with -1 replaced by row 0
+// (masked later).
 //
 // The loads are issued through inline asm.  The compiler counts an LDS-DMA it
 // issues itself on both the vector-memory and the LDS counters, and with one in
@@ -174,15 +175,14 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 
 // The rows one wave's loads of tile lt need, read from the staged slice ahead
 // of the loads: lane l holds the row of key l % 32 (the latent loads take theirs
-// with readlane) and the row of its rope key 8 * wave + l / 8.
+// with readlane).
 struct DmaRows {
   int key;
-  int rope;
 };
-__device__ __forceinline__ DmaRows dma_rows(const int* sidx, int lt, int wave, int lane) {
+__device__ __forceinline__ DmaRows dma_rows(const int* sidx, int lt, int lane) {
   int l = lane;
   asm volatile("" : "+v"(l));  // recomputed here, not held in registers
-  return {sidx[lt * kKT + (l & 31)], sidx[lt * kKT + 8 * wave + (l >> 3)]};
+  return {sidx[lt * kKT + (l & 31)]};
 }
 
 template <int B>
@@ -203,9 +203,8 @@ __device__ __forceinline__ void dma_rope(const DmaRows& rows, const uint8_t* __r
                                          int wave, int lane) {
   int l = lane;
   asm volatile("" : "+v"(l));  // recomputed here, not held in registers
-  const int key = 8 * wave + (l >> 3);
-  const int piece = (l & 7) ^ ((key >> 1) & 7);
-  const uint8_t* src = kv + uint64_t(uint32_t(rows.rope)) * kRowBytes + 1024 + piece * 16;
+  const int piece = 2 * wave + (l >> 5);
+  const uint8_t* src = kv + uint64_t(uint32_t(rows.key)) * kRowBytes + 1024 + piece * 16;
   asm volatile("global_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "{m0}"(lds_addr(kvbuf<B>() + kRegionA + wave * 1024))
@@ -215,7 +214,7 @@ __device__ __forceinline__ void dma_rope(const DmaRows& rows, const uint8_t* __r
 template <int B>
 __device__ __forceinline__ void dma_tile(const int* sidx, int lt, const uint8_t* __restrict__ kv,
                                          int wave, int lane) {
-  const DmaRows rows = dma_rows(sidx, lt, wave, lane);
+  const DmaRows rows = dma_rows(sidx, lt, lane);
 #pragma unroll
   for (int u = 0; u < kKT / kWaves; ++u) dma_latent<B>(rows, u, kv, wave, lane);
   dma_rope<B>(rows, kv, wave, lane);
@@ -245,18 +244,14 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint3
   const int kk = lane & 31;
   const int h = lane >> 5;
   const uint8_t* ka = kvbuf<B>() + kslot(kk) * kRowA + h * 16;  // latent K-steps 0..31
+  int l = lane;
+  asm volatile("" : "+v"(l));  // the rope base is rebuilt per tile, not held in registers
+  const uint8_t* kr = kvbuf<B>() + kRegionA + (l >> 5) * 512 + (l & 31) * 16;  // K-steps 32..35
   auto frag = [&](int st) {
-    if (st < 32) return *reinterpret_cast<const bf16x8_t*>(ka + st * 32);
-    // rope K-steps 32..35: the swizzled address is recomputed for each read,
-    // not held in registers across the tile loop
-    int l = lane;
-    asm volatile("" : "+v"(l));
-    const int r = l & 31;
-    const int piece = (2 * (st - 32) + (l >> 5)) ^ ((r >> 1) & 7);
-    return *reinterpret_cast<const bf16x8_t*>(kvbuf<B>() + kRegionA + r * 128 + piece * 16);
+    return *reinterpret_cast<const bf16x8_t*>(st < 32 ? ka + st * 32 : kr + (st - 32) * 1024);
   };
   DmaRows rows{};
-  if constexpr (kDma) rows = dma_rows(sidx, lt_dma, wave, lane);  // ahead of the ring reads
+  if constexpr (kDma) rows = dma_rows(sidx, lt_dma, lane);  // ahead of the ring reads
   bf16x8_t fr[kRingQ];
 #pragma unroll
   for (int st = 0; st < kRingQ; ++st) fr[st] = frag(st);
@@ -279,13 +274,16 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint3
   // 0 * 0, so S = -inf exactly for masked keys and unchanged for the others.
   // Lanes 32..63 carry dims 8..15 of the step: zero on both sides.
   {
+    // operands are rebuilt for every tile, not held in registers across the loop
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    int ninf = 0xFF80;
+    asm volatile("" : "+v"(ninf));
     const uint64_t keep =
         uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(vmask)))) | 0xFFFFFFFF00000000ull;
-    // operands are rebuilt for every tile, not held in registers across the loop
-    int l = lane, ninf = 0xFF80;
-    asm volatile("" : "+v"(l), "+v"(ninf));
     i32x4_t ka = {0, 0, 0, 0};
-    asm("v_cndmask_b32_e64 %0, %1, 0, %2" : "=v"(ka[0]) : "v"(ninf), "s"(keep));
+    // the nop: the lane mask may have just been written by the VALU (readfirstlane)
+    asm("s_nop 3\n\tv_cndmask_b32_e64 %0, %1, 0, %2" : "=v"(ka[0]) : "v"(ninf), "s"(keep));
     const i32x4_t qa = {l < 32 ? 0x3F80 : 0, 0, 0, 0};
     mfma_v_last(s, __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qa));
   }
@@ -589,13 +587,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     m_ref = fmaxf(m_max, -FLT_MAX);
   }
 
-  // epilogue
+  // epilogue (the head index is rebuilt here rather than kept live across the loop)
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));
+  const int head_e = h0 + (lane_e & 31);
+  const bool hvalid_e = head_e < H;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_h = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
   const int col0 = lane & 31;
   if (nsplit == 1) {
-    if (lse && half == 0 && hvalid) lse[t * H + head] = lse_h;
+    if (lse && half == 0 && hvalid_e) lse[t * H + head_e] = lse_h;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hr = h0 + acc_row(r, half);
@@ -608,7 +610,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     }
   } else {
     const int64_t slot = t * nsplit + blockIdx.z;
-    if (half == 0 && hvalid) part_lse[slot * H + head] = lse_h;
+    if (half == 0 && hvalid_e) part_lse[slot * H + head_e] = lse_h;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hr = h0 + acc_row(r, half);
