@@ -20,8 +20,9 @@
 // Work layouts:
 //   rows     one workgroup per row; windows of at most 8192 keys are held in
 //            LDS, longer ones are re-read from global memory by each pass;
-//   stream   many rows over more than 8192 columns: one workgroup per row
-//            streams the window through LDS with its running top-k;
+//   stream   many rows over more than 8192 columns: the rows kernel takes the
+//            windows of at most 8192 keys, and a second kernel streams each
+//            longer window through LDS with its running top-k;
 //   split    for few rows with long windows (decode): a row's window is cut into
 //            up to 16 chunks of at most 8192 keys, each workgroup selects its
 //            chunk's top-k into a candidate list (key, column) in the workspace,
@@ -73,13 +74,17 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64
   for (uint32_t p = k_eff + threadIdx.x; p < uint32_t(K); p += kThreads) dst[p] = -1;
 }
 
+// skip_long: rows whose window exceeds kCap are left to the stream kernel
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
-    const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out) {
+    const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out, int skip_long) {
   __shared__ uint32_t keys[kCap];
   __shared__ SelectShared<kThreads> sh;
   const int64_t row = blockIdx.x;
-  row_topk(scores, ld, row, row_starts[row], row_ends[row], K, out, keys, sh);
+  const int a = row_starts[row];
+  const int b = row_ends[row];
+  if (skip_long && b - a > kCap) return;
+  row_topk(scores, ld, row, a, b, K, out, keys, sh);
 }
 
 // Split path, phase 1: workgroup (row, c) selects the top-k of chunk c.
@@ -204,6 +209,7 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
   const int n = b > a ? b - a : 0;
   const float* src = scores + row * ld + a;
   int32_t* dst = out + row * int64_t(K);
+  if (n <= kCap) return;  // held whole by the rows kernel of the same launch
   const uint64_t lt = lanemask_lt();
 
   int ncand = 0;           // keys held in LDS (the running set, then survivors)
@@ -288,13 +294,15 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
                        const int32_t* row_ends, int64_t n_q, int64_t n_cols, int32_t K,
                        int32_t* out, void* workspace, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
-  if (!use_split(n_q, n_cols, K) && n_cols > kCap && K <= kMaxSplitK) {
-    hipLaunchKernelGGL(topk_stream_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
-                       ld, row_starts, row_ends, K, out);
-    return hipGetLastError();
-  }
   if (!use_split(n_q, n_cols, K)) {
+    // windows of at most kCap keys: held whole in LDS by the rows kernel; longer
+    // ones (only possible when n_cols > kCap) streamed by the stream kernel
+    const bool stream_long = n_cols > kCap && K <= kMaxSplitK;
     hipLaunchKernelGGL(topk_rows_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
+                       ld, row_starts, row_ends, K, out, int(stream_long));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !stream_long) return e;
+    hipLaunchKernelGGL(topk_stream_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
                        ld, row_starts, row_ends, K, out);
     return hipGetLastError();
   }

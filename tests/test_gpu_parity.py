@@ -151,7 +151,8 @@ def test_topk_rows_longer_than_split(dsa):
 
 def test_topk_many_long_rows_stream_path(dsa):
     # more than 1024 rows over more than 8192 columns: one workgroup per row
-    # streams the window through LDS with its running top-k
+    # streams a window of more than 8192 keys through LDS with its running
+    # top-k and holds a shorter one whole
     g = np.random.default_rng(105)
     n_q, n = 1100, 9000
     S = g.standard_normal((n_q, n)).astype(np.float32)
@@ -161,7 +162,7 @@ def test_topk_many_long_rows_stream_path(dsa):
     S[2::8, 4000:4100] = 1.0                                # fewer selectable keys than k
     rs = g.integers(0, 500, n_q).astype(np.int32)
     re = np.minimum(n, rs + g.integers(7000, 9000, n_q)).astype(np.int32)
-    re[:5] = rs[:5] + np.array([0, 1, 4096, 4097, 8192])    # empty and piece-boundary windows
+    re[:6] = rs[:6] + np.array([0, 1, 4096, 4097, 8192, 8193])  # empty and boundary windows
     assert dsa._lib_or_load().dsa_topk_workspace_size(n_q, n, 2048) == 0
     for K in (2048, 333, 1):
         _topk_case(dsa, S, rs, re, K, f"stream K={K}")
