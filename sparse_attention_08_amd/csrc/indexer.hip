@@ -19,8 +19,9 @@
 //                          are issued latest-first so the longest causal rows
 //                          start first.
 //   rowsplit kernel (decode) one long row per workgroup slice: each wave streams
-//                          its own 32-key tiles straight from global memory (the
-//                          keys are read once, so there is nothing to share).
+//                          its own 32-key tiles through private LDS buffers with
+//                          contiguous 1 KB LDS-DMA loads (the keys are read once,
+//                          so there is nothing to share).
 // The fp32 path (small head dims) is a plain VALU kernel.
 #include <climits>
 
@@ -72,7 +73,12 @@ __device__ __forceinline__ void dma_chunk(uint8_t* buf, const uint8_t* __restric
       int key = key0 + kl;
       key = key < n_k ? key : n_k - 1;                   // past the end: any valid row
       const uint8_t* src = k + int64_t(key) * Op::kRowBytes + swz<Op>(kl, p) * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(buf + j * kWave * 16), 16, 0, 0);
+      // asm: a compiler-issued LDS-DMA would turn every later LDS wait into a
+      // full drain; the chunk's only wait is the explicit one in rows_chunk
+      asm volatile("global_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "{m0}"(ixcore::lds_addr(buf + j * kWave * 16))
+                   : "memory");
     }
   }
 }
@@ -206,8 +212,10 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // decode: one long row split over workgroups; each wave streams its own tiles
+// through its own LDS buffers
 // ---------------------------------------------------------------------------
 constexpr int kSplitThreads = 256;
+constexpr int kSplitBufs = 2;  // LDS tile buffers per wave: one tile in flight
 
 template <class Op, int MT>
 __global__ __launch_bounds__(kSplitThreads) void indexer_rowsplit_kernel(
@@ -236,7 +244,10 @@ __global__ __launch_bounds__(kSplitThreads) void indexer_rowsplit_kernel(
       scores[t * ld + s] = p;
     }
   };
-  ixcore::stream_tiles<Op, MT, kScaled>(qr, k, k_scale, a, b, i0 + wave, kWaves, i1, lane, put);
+  typedef ixcore::LdsTile<Op, kScaled> T;
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[kWaves][kSplitBufs * T::kBytes];
+  ixcore::stream_tiles_lds<Op, MT, kScaled, kSplitBufs>(qr, k, k_scale, a, b, i0 + wave, kWaves,
+                                                        i1, lane, tbuf[wave], put);
 }
 
 // ---------------------------------------------------------------------------

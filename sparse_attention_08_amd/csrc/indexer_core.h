@@ -169,5 +169,130 @@ __device__ __forceinline__ void stream_tiles(const QueryRow<Op, MT>& qr,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Key tiles staged through wave-private LDS buffers (few long rows: decode).
+//
+// A direct fragment load gives each lane 16 bytes of a different key, so one
+// load instruction touches 32 key rows for 1 KB of data, and the misses the
+// memory pipeline can keep in flight run out long before HBM is busy.  Here a
+// wave copies each 32-key tile into its own LDS buffer with LDS-DMA loads that
+// each move 1 KB of contiguous key rows, NB - 1 tiles ahead of the tile it
+// computes, and reads the MFMA fragments from LDS.  The 16-byte pieces of a
+// key are XOR-swizzled by the key (kswz) so that the fragment reads are free
+// of bank conflicts.  fp8 keys bring their scales along (one 4-byte DMA load).
+//
+// The DMA is issued through inline asm: the compiler counts a DMA it issues
+// itself on its LDS counter as well, and then waits for LDS reads only with a
+// full drain.  Its one wait is the explicit vector-memory count below; the
+// buffers are private to the wave, so no barrier is needed.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+// LDS slot (in 16-byte pieces) of piece cc of tile-local key kl (an involution).
+template <class Op>
+__device__ __forceinline__ int kswz(int kl, int cc) {
+  return Op::kRowBytes == 256 ? (cc ^ (kl & 15)) : (cc ^ ((kl >> 1) & 7));
+}
+
+template <class Op, bool kScaled>
+struct LdsTile {
+  static constexpr int kKeyBytes = kKeyTile * Op::kRowBytes;      // 8 KB bf16, 4 KB fp8
+  static constexpr int kBytes = kKeyBytes + (kScaled ? 256 : 0);  // + the scales (twice)
+  static constexpr int kKeyLoads = kKeyBytes / 1024;              // 1 KB DMA loads per tile
+  static constexpr int kLoads = kKeyLoads + (kScaled ? 1 : 0);
+
+  // DMA of the tile whose first key is s0 into buf (keys past b - 1: key s0)
+  __device__ static __forceinline__ void issue(uint8_t* buf, const uint8_t* __restrict__ k,
+                                               const float* __restrict__ k_scale, int s0, int b,
+                                               int lane) {
+    constexpr int kPieces = Op::kRowBytes / 16;
+    constexpr int kKeysPerLoad = kWave / kPieces;
+    int l = lane;
+    asm volatile("" : "+v"(l));  // recomputed here, not held in registers
+#pragma unroll
+    for (int j = 0; j < kKeyLoads; ++j) {
+      const int kl = j * kKeysPerLoad + l / kPieces;
+      const int key = s0 + kl < b ? s0 + kl : s0;
+      const uint8_t* src = k + int64_t(key) * Op::kRowBytes + kswz<Op>(kl, l % kPieces) * 16;
+      asm volatile("global_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "{m0}"(lds_addr(buf + j * 1024))
+                   : "memory");
+    }
+    if constexpr (kScaled) {
+      const int key = s0 + (l & 31) < b ? s0 + (l & 31) : s0;
+      asm volatile("global_load_lds_dword %0, off"
+                   :
+                   : "v"(k_scale + key), "{m0}"(lds_addr(buf + kKeyBytes))
+                   : "memory");
+    }
+  }
+
+  // MFMA fragments (and the scale) of the lane's key l % 32
+  __device__ static __forceinline__ void read(const uint8_t* buf, int lane,
+                                              typename Op::frag_t (&kb)[Op::kSteps],
+                                              float& ks) {
+    const int kl = lane & 31;
+    const uint8_t* row = buf + kl * Op::kRowBytes;
+    constexpr int kFragPieces = Op::kFragBytes / 16;
+#pragma unroll
+    for (int st = 0; st < Op::kSteps; ++st) {
+      const int cc = (2 * st + (lane >> 5)) * kFragPieces;
+      if constexpr (kFragPieces == 1) {
+        kb[st] = *reinterpret_cast<const typename Op::frag_t*>(row + kswz<Op>(kl, cc) * 16);
+      } else {
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + kswz<Op>(kl, cc) * 16);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(row + kswz<Op>(kl, cc + 1) * 16);
+        kb[st] = __builtin_bit_cast(typename Op::frag_t,
+                                    __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+    if constexpr (kScaled) ks = reinterpret_cast<const float*>(buf + kKeyBytes)[kl];
+  }
+};
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Scores of the tiles i = first, first + step, ... < nt of one query row through
+// the wave's NB buffers of LdsTile<Op, kScaled>::kBytes at wbuf.  Tile j of the
+// wave's sequence goes to buffer j % NB; the DMA into a buffer is issued after
+// the MFMAs of the tile it held, so its reads are done.  Past the last tile the
+// last tile is fetched again (every iteration issues the same loads, so the wait
+// count is fixed), and everything is drained before return.  put(i, score,
+// scale) receives each tile's scores (lanes l and l^32 both hold key l%32).
+template <class Op, int MT, bool kScaled, int NB, class Put>
+__device__ __forceinline__ void stream_tiles_lds(const QueryRow<Op, MT>& qr,
+                                                 const uint8_t* __restrict__ k,
+                                                 const float* __restrict__ k_scale, int base,
+                                                 int b, int first, int step, int nt, int lane,
+                                                 uint8_t* wbuf, Put put) {
+  typedef LdsTile<Op, kScaled> T;
+  if (first >= nt) return;
+  auto key0 = [&](int i) { return base + (i < nt ? i : nt - 1) * kKeyTile; };
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j) T::issue(wbuf + j * T::kBytes, k, k_scale, key0(first + j * step), b, lane);
+  int cur = 0;  // buffer of the tile computed next
+  for (int i = first; i < nt; i += step) {
+    const int nxt = cur == 0 ? NB - 1 : cur - 1;  // (cur + NB - 1) % NB: free since last iteration
+    T::issue(wbuf + nxt * T::kBytes, k, k_scale, key0(i + (NB - 1) * step), b, lane);
+    wait_vmcnt<(NB - 1) * T::kLoads>();
+    typename Op::frag_t kb[Op::kSteps];
+    float ks = 1.0f;
+    T::read(wbuf + cur * T::kBytes, lane, kb, ks);
+    put(i, qr.score(kb), ks);
+    cur = cur + 1 == NB ? 0 : cur + 1;
+  }
+  wait_vmcnt<0>();
+}
+
 }  // namespace ixcore
 }  // namespace dsa
