@@ -143,10 +143,17 @@ __device__ __forceinline__ void mfma_v_last(f32x16_t& d, bf16x8_t a, bf16x8_t b)
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3"
       : "+v"(d) : "v"(a), "v"(b));
 }
-// accumulation into O; the leading nops cover a VALU-written operand
-// (P, a repacked V fragment, or a rescaled O)
+// accumulation into O.  kNop: the leading wait states cover an operand the
+// VALU may have written just before (the first MFMAs of a tile, after P is
+// moved into place); the other operands come from LDS reads or from VALU work
+// many instructions earlier (a host test scans the compiled code for a VALU
+// write closer than two wait states to the MFMA that reads it).
+template <bool kNop>
 __device__ __forceinline__ void mfma_a(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  if constexpr (kNop)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 // before the VALU touches O after MFMAs into it
 __device__ __forceinline__ void o_fence(f32x16_t (&o)[kVTiles]) {
@@ -303,7 +310,9 @@ struct Softmax {
   f32x16_t s;      // S^T of the tile: lane = head l%32, 16 keys
   float mt;
   float ps;
-  bf16x8_t p0, p1;
+  i32x4_t p0w, p1w;  // P of keys 0..7 / 8..15 of the lane half, as packed bf16 pairs
+  __device__ __forceinline__ bf16x8_t p0() const { return __builtin_bit_cast(bf16x8_t, p0w); }
+  __device__ __forceinline__ bf16x8_t p1() const { return __builtin_bit_cast(bf16x8_t, p1w); }
 
   // The stage's inputs pass through an empty volatile asm first: the stage
   // is pure arithmetic, which the instruction selector would otherwise place
@@ -361,10 +370,8 @@ struct Softmax {
         const bf16x2_t b = {__bf16(s[r + 8]), __bf16(s[r + 9])};
         ps = __builtin_amdgcn_fdot2_f32_bf16(a, ones, ps, false);
         ps = __builtin_amdgcn_fdot2_f32_bf16(b, ones, ps, false);
-        p0[r] = a[0];
-        p0[r + 1] = a[1];
-        p1[r] = b[0];
-        p1[r + 1] = b[1];
+        p0w[r / 2] = __builtin_bit_cast(int, a);
+        p1w[r / 2] = __builtin_bit_cast(int, b);
       }
       if constexpr (K == 7) l_run += ps;
     }
@@ -432,7 +439,10 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
   for (int m = 0; m < 2 * kVTiles; ++m) {
     const bf16x8_t v = fr[m % kRingV];
     if (m + kRingV < 2 * kVTiles) fr[m % kRingV] = rd(m + kRingV);
-    mfma_a(o[m >> 1], (m & 1) == 0 ? p0 : p1, v);
+    if (m < 2)
+      mfma_a<true>(o[m >> 1], (m & 1) == 0 ? p0 : p1, v);
+    else
+      mfma_a<false>(o[m >> 1], (m & 1) == 0 ? p0 : p1, v);
     if constexpr (kSm) {
       if (m % 2 == 1 && m / 2 < kSmStages) sm_stage(m / 2, sm, scale2, m_ref, m_max, over, l_run);
     }
@@ -458,8 +468,8 @@ __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const ui
     sm.s = qk_tile<B, 0, false>(qf, vm, lane, sh.idx, 0, kvb, wave);
   }
   pv_tile<(B + 3) & 3, true>(nullptr, p0, p1, o, lane, sm, scale2, m_ref, m_max, over, l_run);
-  p0 = sm.p0;
-  p1 = sm.p1;
+  p0 = sm.p0();
+  p1 = sm.p1();
   vm = sh.vmask[i + 1];  // the next tile's mask, read well before it is needed
 }
 
@@ -557,8 +567,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
         Softmax sm;
         sm.s = qk_tile<0, 0, false>(qf, sh.vmask[0], lane, sh.idx, 0, kvb, wave);
         softmax_all(sm, scale2, m_ref, m_max, over, l_run);
-        p0 = sm.p0;
-        p1 = sm.p1;
+        p0 = sm.p0();
+        p1 = sm.p1();
       }
       uint32_t vm = sh.vmask[1];
       // tiles 1 .. nt4-1 in groups of four (one exit: a loop left in the middle
