@@ -82,8 +82,6 @@ constexpr int kDmaPerWave = kKT / kWaves + 1;  // 8 latent rows + 1 rope load: 9
 constexpr int kHeadsPerBlock = kWaves * 32;     // 128
 constexpr int kMaxIdx = 2048;                   // selected keys per workgroup (LDS-staged)
 constexpr int kMaxTiles = kMaxIdx / kKT;
-constexpr int kRingQ = 3;                     // LDS fragment reads in flight ahead of the MFMAs
-constexpr int kRingV = 3;
 constexpr float kSpan = 32.0f;                 // base-2 units: P <= 2^32 before a second pass
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -128,14 +126,21 @@ __device__ __forceinline__ uint8_t* kvbuf() {
 // same form, and S + O do not fit in the 256 accumulation registers.)  The
 // compiler does not see into the asm, so the MFMA data hazards it would
 // otherwise cover are covered here, with the counts it emits for the builtin on
-// gfx950: a VALU write feeding an MFMA operand needs 1 wait state, an MFMA
+// gfx950: a VALU write feeding an MFMA operand needs 2 wait states, an MFMA
 // result read by a VALU (or accumulation-register move) needs 12, and chained
 // accumulation (srcC = previous dst) needs none.
-__device__ __forceinline__ void mfma_v0(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+//
+// Two chained MFMAs in one asm statement (between two separate asm statements
+// the compiler puts a wait state of its own; a chain needs none).
+__device__ __forceinline__ void mfma_v0_2(f32x16_t& d, bf16x8_t a0, bf16x8_t b0, bf16x8_t a1,
+                                          bf16x8_t b1) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
+      : "=&v"(d) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
-__device__ __forceinline__ void mfma_v(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma_v_2(f32x16_t& d, bf16x8_t a0, bf16x8_t b0, bf16x8_t a1,
+                                         bf16x8_t b1) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
+      : "+v"(d) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
 // last MFMA of a chain whose result the VALU reads next; its operands are
 // VALU-written just before (the leading nop)
@@ -148,12 +153,19 @@ __device__ __forceinline__ void mfma_v_last(f32x16_t& d, bf16x8_t a, bf16x8_t b)
 // moved into place); the other operands come from LDS reads or from VALU work
 // many instructions earlier (a host test scans the compiled code for a VALU
 // write closer than two wait states to the MFMA that reads it).
+// Two chained MFMAs (both key steps of one value tile) in one asm statement.
 template <bool kNop>
-__device__ __forceinline__ void mfma_a(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+__device__ __forceinline__ void mfma_a2(f32x16_t& d, bf16x8_t a0, bf16x8_t b0, bf16x8_t a1,
+                                        bf16x8_t b1) {
   if constexpr (kNop)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+    asm volatile(
+        "s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
+        : "+a"(d) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
   else
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
+        : "+a"(d) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
 // before the VALU touches O after MFMAs into it
 __device__ __forceinline__ void o_fence(f32x16_t (&o)[kVTiles]) {
@@ -227,6 +239,13 @@ __device__ __forceinline__ void dma_tile(const int* sidx, int lt, const uint8_t*
   dma_rope<B>(rows, kv, wave, lane);
 }
 
+// s_waitcnt lgkmcnt(n), other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
+
 // Wait until this wave's LDS-DMA of the current tile has landed.  The next
 // tile's 9 loads (issued one tile later, vector-memory counters retire in
 // order) may stay in flight.
@@ -241,7 +260,7 @@ __device__ __forceinline__ void wait_tile(bool next_in_flight) {
 
 // S^T = K . Q^T for the tile in buffer B: keys on M, the wave's 32 heads on N,
 // 36 K-steps of 16 dims.  Lane l reads key l%32, dims 16*st + 8*(l/32) .. +8;
-// the fragment reads run kRingQ steps ahead of their MFMA.  With kDma, the
+// the fragment reads run two steps ahead of their MFMA.  With kDma, the
 // LDS-DMA loads of a later tile (into buffer BD) are issued between the MFMAs
 // (the wave can issue them while the matrix core works).
 template <int B, int BD, bool kDma>
@@ -259,20 +278,23 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint3
   };
   DmaRows rows{};
   if constexpr (kDma) rows = dma_rows(sidx, lt_dma, lane);  // ahead of the ring reads
-  bf16x8_t fr[kRingQ];
+  // fragment reads in pairs, two pairs ahead: one explicit wait per two MFMAs
+  bf16x8_t fr[4];
 #pragma unroll
-  for (int st = 0; st < kRingQ; ++st) fr[st] = frag(st);
+  for (int st = 0; st < 4; ++st) fr[st] = frag(st);
   f32x16_t s;
 #pragma unroll
-  for (int st = 0; st < kQSteps; ++st) {
-    const bf16x8_t a = fr[st % kRingQ];
-    if (st + kRingQ < kQSteps) fr[st % kRingQ] = frag(st + kRingQ);
-    if (st == 0) mfma_v0(s, a, qf[st]);
-    else mfma_v(s, a, qf[st]);
+  for (int st = 0; st < kQSteps; st += 2) {
+    if (st + 2 < kQSteps) wait_lgkm<2>();  // steps st, st+1 read; st+2, st+3 in flight
+    else wait_lgkm<0>();
+    if (st == 0) mfma_v0_2(s, fr[0], qf[0], fr[1], qf[1]);
+    else mfma_v_2(s, fr[st % 4], qf[st], fr[(st + 1) % 4], qf[st + 1]);
+    if (st + 4 < kQSteps) fr[st % 4] = frag(st + 4);
+    if (st + 5 < kQSteps) fr[(st + 1) % 4] = frag(st + 5);
     if constexpr (kDma) {
       // the gather of a later tile, spread between the MFMAs
-      if (st % 4 == 1 && st / 4 < kKT / kWaves) dma_latent<BD>(rows, st / 4, kv, wave, lane);
-      if (st == 33) dma_rope<BD>(rows, kv, wave, lane);
+      if (st % 4 == 0 && st / 4 < kKT / kWaves) dma_latent<BD>(rows, st / 4, kv, wave, lane);
+      if (st == 32) dma_rope<BD>(rows, kv, wave, lane);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep this order
   }
@@ -424,7 +446,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
   // 4 * (li >> 2) + half (+ 2, + 16)
   const uint8_t* vb = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) +
                       (4 * (li >> 2) + half) * kRowA + (n0 + 4 * (li & 3)) * 2;
-  // step m = 2n + ks: value tile n, key step ks; reads run kRingV steps ahead
+  // step m = 2n + ks: value tile n, key step ks
   auto rd = [&](int m) {
     const uint8_t* base = vb + 16 * (m & 1) * kRowA + (m >> 1) * 64;
     const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
@@ -432,19 +454,22 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 2 * kRowA));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  bf16x8_t fr[kRingV];
+  // fragment reads in pairs, two pairs ahead: one explicit wait per two MFMAs
+  bf16x8_t fr[4];
 #pragma unroll
-  for (int m = 0; m < kRingV; ++m) fr[m] = rd(m);
+  for (int m = 0; m < 4; ++m) fr[m] = rd(m);
 #pragma unroll
-  for (int m = 0; m < 2 * kVTiles; ++m) {
-    const bf16x8_t v = fr[m % kRingV];
-    if (m + kRingV < 2 * kVTiles) fr[m % kRingV] = rd(m + kRingV);
-    if (m < 2)
-      mfma_a<true>(o[m >> 1], (m & 1) == 0 ? p0 : p1, v);
+  for (int m = 0; m < 2 * kVTiles; m += 2) {
+    if (m + 2 < 2 * kVTiles) wait_lgkm<4>();  // steps m, m+1 read; m+2, m+3 in flight
+    else wait_lgkm<0>();
+    if (m == 0)
+      mfma_a2<true>(o[0], p0, fr[0], p1, fr[1]);
     else
-      mfma_a<false>(o[m >> 1], (m & 1) == 0 ? p0 : p1, v);
+      mfma_a2<false>(o[m >> 1], p0, fr[m % 4], p1, fr[(m + 1) % 4]);
+    if (m + 4 < 2 * kVTiles) fr[m % 4] = rd(m + 4);
+    if (m + 5 < 2 * kVTiles) fr[(m + 1) % 4] = rd(m + 5);
     if constexpr (kSm) {
-      if (m % 2 == 1 && m / 2 < kSmStages) sm_stage(m / 2, sm, scale2, m_ref, m_max, over, l_run);
+      if (m / 2 < kSmStages) sm_stage(m / 2, sm, scale2, m_ref, m_max, over, l_run);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep this order
   }
