@@ -219,6 +219,9 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale,
  *   topk_idx  int32 [n_q, index_topk]; entries in [0, n_kv) or -1
  *   out       [n_q, n_heads, d_v] of dtype;  lse f32 [n_q, n_heads] or NULL
  *   workspace at least dsa_sparse_mla_workspace_size(...) bytes (may be 0).
+ *   For few queries (BF16) each row's keys are split over several workgroups;
+ *   the workspace then holds their normalised partial outputs in bf16 and
+ *   their partial LSEs in fp32, merged by a second kernel.
  * Softmax statistics and accumulation are fp32; probabilities enter the
  * value product in the input type.  Supported: BF16 with d_qk == 576,
  * d_v == 512, n_heads a multiple of 32; F32 with d_qk <= 256, d_v <= d_qk.

@@ -505,7 +505,7 @@ __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const ui
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ idx, int H, int K, float sm_scale,
-    __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    __bf16* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_lse, int nsplit) {
   __shared__ __attribute__((aligned(16))) MlaShared sh;
 
@@ -651,16 +651,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       const int hr = h0 + acc_row(r, half);
       const float ir = __shfl(inv, acc_row(r, half));
       if (hr < H) {
-        float* orow = part_o + (slot * H + hr) * int64_t(kDv) + col0;
+        uint16_t* orow = part_o + (slot * H + hr) * int64_t(kDv) + col0;
 #pragma unroll
-        for (int n = 0; n < kVTiles; ++n) orow[n * 32] = o[n][r] * ir;
+        for (int n = 0; n < kVTiles; ++n) orow[n * 32] = f32_to_bf16_bits(o[n][r] * ir);
       }
     }
   }
 }
 
-// Merge split partials: out = sum_s e^{lse_s - L} o_s with L = logsumexp_s lse_s.
-__global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
+// Merge split partials (bf16, normalised per split): out = sum_s e^{lse_s - L} o_s
+// with L = logsumexp_s lse_s.
+__global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           int H, int nsplit,
                                                           __bf16* __restrict__ out,
@@ -675,9 +676,10 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
     const float ls = part_lse[(t * nsplit + s) * H + h];
     const float ws = ls == -INFINITY ? 0.0f : __expf(ls - mx);
     wsum += ws;
-    const float* po = part_o + ((t * nsplit + s) * H + h) * int64_t(kDv);
+    const uint16_t* po = part_o + ((t * nsplit + s) * H + h) * int64_t(kDv);
 #pragma unroll
-    for (int x = 0; x < kDv / 128; ++x) acc[x] = fmaf(ws, po[threadIdx.x + 128 * x], acc[x]);
+    for (int x = 0; x < kDv / 128; ++x)
+      acc[x] = fmaf(ws, bf16_bits_to_f32(po[threadIdx.x + 128 * x]), acc[x]);
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   uint16_t* orow = reinterpret_cast<uint16_t*>(out) + (t * H + h) * int64_t(kDv);
@@ -767,7 +769,8 @@ size_t mla_workspace_bytes(int64_t n_q, int32_t n_heads, int32_t d_qk, int32_t d
   if (dtype != 1) return 0;
   const int s = mla_splits(n_q, n_heads, K);
   if (s == 1) return 0;
-  return size_t(n_q) * s * n_heads * (size_t(d_v) + 1) * sizeof(float);
+  // bf16 partial outputs, then fp32 partial LSEs
+  return size_t(n_q) * s * n_heads * (size_t(d_v) * sizeof(uint16_t) + sizeof(float));
 }
 
 hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, int64_t n_q,
@@ -785,8 +788,9 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
   }
   const int s = mla_splits(n_q, n_heads, K);
   const unsigned hb = unsigned((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = s > 1 ? part_o + size_t(n_q) * s * n_heads * d_v : nullptr;
+  uint16_t* part_o = static_cast<uint16_t*>(workspace);
+  float* part_lse =
+      s > 1 ? reinterpret_cast<float*>(part_o + size_t(n_q) * s * n_heads * d_v) : nullptr;
   hipLaunchKernelGGL(mla_bf16_kernel, dim3(unsigned(n_q), hb, s), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(kv), idx, n_heads,
                      K, sm_scale, static_cast<__bf16*>(out), lse, part_o, part_lse, s);
