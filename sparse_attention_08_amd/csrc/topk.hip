@@ -40,13 +40,29 @@ namespace {
 using namespace topksel;
 
 // Keys of scores[a .. a+n) into LDS (n <= kCap); returns the selectable count.
+// Every thread issues a batch of loads (kCap / 2 / kThreads of them) before it
+// waits for any: a load-then-store loop would wait a full memory round trip
+// per element.
 __device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t* keys,
                                               SelectShared<kThreads>& sh) {
+  constexpr int kPer = kCap / 2 / kThreads;
   uint32_t cnt = 0;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const uint32_t k = score_key(src[i]);
-    keys[i] = k;
-    cnt += (k != 0u);
+  for (int base = 0; base < n; base += kPer * kThreads) {
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = base + int(threadIdx.x) + j * kThreads;
+      v[j] = i < n ? src[i] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = base + int(threadIdx.x) + j * kThreads;
+      if (i < n) {
+        const uint32_t k = score_key(v[j]);
+        keys[i] = k;
+        cnt += (k != 0u);
+      }
+    }
   }
   return block_sum<kThreads>(cnt, sh.tmp);  // also orders the LDS writes
 }
@@ -125,6 +141,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     int32_t* __restrict__ out, const uint32_t* __restrict__ cand_key,
     const int32_t* __restrict__ cand_col, const int32_t* __restrict__ cand_cnt) {
   __shared__ uint32_t keys[kMergeCap];
+  __shared__ int sel[kMaxSplitK];  // selected candidate positions, in output order
   __shared__ int off[kMaxChunks + 1];
   __shared__ SelectShared<kMergeThreads> sh;
   const int64_t row = blockIdx.x;
@@ -167,14 +184,23 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   }
   __syncthreads();
   int32_t* dst = out + row * int64_t(K);
-  // every candidate is selectable (-inf never becomes one)
+  // every candidate is selectable (-inf never becomes one); the selection is
+  // recorded as candidate positions first, so that the column loads below are
+  // independent of each other instead of one per step of the compaction
   select_topk<kMergeThreads>(LdsKeys{keys}, n, uint32_t(n), K, sh,
-                             [&](uint32_t p, int i, uint32_t) {
-    int c = 0;
-    while (off[c + 1] <= i) ++c;
-    dst[p] = cand_col[(row * kMaxChunks + c) * int64_t(K) + (i - off[c])];
-  });
-  for (int p = (n < K ? n : K) + threadIdx.x; p < K; p += kMergeThreads) dst[p] = -1;
+                             [&](uint32_t p, int i, uint32_t) { sel[p] = i; });
+  __syncthreads();
+  const int k_eff = n < K ? n : K;
+  for (int p = threadIdx.x; p < K; p += kMergeThreads) {
+    int col = -1;
+    if (p < k_eff) {
+      const int i = sel[p];
+      int c = 0;
+      while (off[c + 1] <= i) ++c;
+      col = cand_col[(row * kMaxChunks + c) * int64_t(K) + (i - off[c])];
+    }
+    dst[p] = col;
+  }
 }
 
 // Many rows over more than 8192 columns (k <= 2048): a row is streamed through
