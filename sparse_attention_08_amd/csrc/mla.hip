@@ -535,14 +535,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     __syncthreads();
     int last = -1;
     const int jbase = i0 * kKT;
-    for (int x = tid; x < (i1 - i0) * kKT; x += kThreads) {
+    const int nx = (i1 - i0) * kKT;
+    // every thread issues all its index loads (up to kMaxIdx / kThreads) before
+    // it waits for any of them
+    constexpr int kPer = kMaxIdx / kThreads;
+    int rv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int x = tid + u * kThreads;
       const int j = jbase + x;
-      const int r = j < K ? irow[j] : -1;
-      sh.idx[x] = r < 0 ? 0 : r;
-      const uint64_t b = __ballot(r >= 0);   // x advances by whole waves: 2 tiles per ballot
-      if (lane == 0) sh.vmask[x / kKT] = uint32_t(b);
-      if (lane == 32) sh.vmask[x / kKT] = uint32_t(b >> 32);
-      if (r >= 0) last = x;
+      rv[u] = (x < nx && j < K) ? irow[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int x = tid + u * kThreads;
+      if (x < nx) {
+        const int r = rv[u];
+        sh.idx[x] = r < 0 ? 0 : r;
+        if (r >= 0) last = x;
+      }
+      // x advances by whole waves: 2 tiles per ballot (the wave is uniform in x < nx)
+      const uint64_t b = __ballot(x < nx && rv[u] >= 0);
+      if (x < nx && lane == 0) sh.vmask[x / kKT] = uint32_t(b);
+      if (x < nx && lane == 32) sh.vmask[x / kKT] = uint32_t(b >> 32);
     }
     if (last >= 0) atomicMax(&sh.last, last);
     __syncthreads();
