@@ -240,15 +240,24 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
 
   int ncand = 0;           // keys held in LDS (the running set, then survivors)
   uint32_t floor_key = 0;  // keys <= floor_key cannot enter (0: not selectable)
-  for (int lo = 0;; lo += kPiece) {
+  // wave w owns keys [w*kPiece/4, (w+1)*kPiece/4) of a piece, lane-strided; the
+  // next piece's scores are loaded while the current one is processed
+  auto load_piece = [&](int lo, float (&f)[kPer]) {
     const int m = lo < n ? min(kPiece, n - lo) : 0;
-    // load: wave w owns keys [w*kPiece/4, (w+1)*kPiece/4) of the piece, lane-strided
-    uint32_t v[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = wave * (kPiece / kWaves) + j * kWave + lane;
-      v[j] = i < m ? score_key(src[lo + i]) : 0u;
+      f[j] = i < m ? src[lo + i] : -INFINITY;
     }
+  };
+  float fnext[kPer];
+  load_piece(0, fnext);
+  for (int lo = 0;; lo += kPiece) {
+    const int m = lo < n ? min(kPiece, n - lo) : 0;
+    uint32_t v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = score_key(fnext[j]);  // -inf -> 0: not selectable
+    load_piece(lo + kPiece, fnext);
     auto survivors = [&]() {  // survivors of this wave's part (uniform per wave)
       uint32_t c = 0;
 #pragma unroll
