@@ -62,6 +62,47 @@ __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32
   __syncthreads();
 }
 
+// The key loops below read kBatch keys before they use any of them: a loop that
+// uses each key as it is read waits a full LDS (or memory) round trip per key.
+constexpr int kBatch = 8;
+
+// f(i, key(i)) for this thread's keys i = tid, tid + NT, ... < n, in that order.
+template <int NT, class Keys, class F>
+__device__ __forceinline__ void for_keys(const Keys& key, int n, F f) {
+  for (int base = int(threadIdx.x); base < n; base += NT * kBatch) {
+    uint32_t k[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base + u * NT;
+      k[u] = i < n ? key(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base + u * NT;
+      if (i < n) f(i, k[u]);
+    }
+  }
+}
+
+// f(i, key) for i = s_lo + lane, s_lo + lane + 64, ... over the wave's segment
+// [s_lo, s_hi) (s_lo a multiple of 64): every lane of the wave calls f the same
+// number of times (key 0 past the end), so f may use wave-wide ballots.
+template <class Keys, class F>
+__device__ __forceinline__ void for_segment(const Keys& key, int s_lo, int s_hi, int lane, F f) {
+  for (int base = s_lo; base < s_hi; base += kWave * kBatch) {
+    uint32_t k[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base + u * kWave + lane;
+      k[u] = i < s_hi ? key(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (base + u * kWave < s_hi) f(base + u * kWave + lane, k[u]);
+    }
+  }
+}
+
 // Select the K largest of the n keys key(0..n-1) (n_sel of them are nonzero),
 // ties to the lowest index, and call emit(p, i, key) for each selected index i
 // in ascending order, p = its output slot in [0, min(K, n_sel)).  All NT threads
@@ -83,13 +124,12 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
   uint32_t thr = 0u, need_eq = 0u;
   if (n_sel > uint32_t(K)) {
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t k = key(i);
+    for_keys<NT>(key, n, [&](int, uint32_t k) {
       if (k != 0u) {
         kmin = min(kmin, k);
         kmax = max(kmax, k);
       }
-    }
+    });
     block_min_max<NT>(kmin, kmax, sh.tmp);
     const uint32_t diff = kmin ^ kmax;
     int shift = diff == 0u ? 0 : 32 - __builtin_clz(diff);  // varying bits [0, shift)
@@ -103,10 +143,9 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
       const uint32_t dmask = (1u << nb) - 1u;
       for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
       __syncthreads();
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t k = key(i);
+      for_keys<NT>(key, n, [&](int, uint32_t k) {
         if (k != 0u && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
-      }
+      });
       __syncthreads();
       // thread j owns the bins of slot (NT-1-j), so an exclusive prefix over
       // threads is the count of keys in higher bins
@@ -143,12 +182,10 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
   const int s_lo = wave * seg;
   const int s_hi = min(n, s_lo + seg);
   uint32_t gt = 0u, eq = 0u;
-  for (int base = s_lo; base < s_hi; base += kWave) {
-    const int i = base + lane;
-    const uint32_t k = i < s_hi ? key(i) : 0u;
+  for_segment(key, s_lo, s_hi, lane, [&](int i, uint32_t k) {
     gt += __popcll(__ballot(k > thr));
     eq += __popcll(__ballot(i < s_hi && k == thr));
-  }
+  });
   if (lane == 0) {
     sh.seg_cnt[wave] = gt;
     sh.seg_cnt[NW + wave] = eq;
@@ -160,9 +197,7 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
     eq_before += sh.seg_cnt[NW + w];
   }
   const uint64_t lt = lanemask_lt();
-  for (int base = s_lo; base < s_hi; base += kWave) {
-    const int i = base + lane;
-    const uint32_t k = i < s_hi ? key(i) : 0u;
+  for_segment(key, s_lo, s_hi, lane, [&](int i, uint32_t k) {
     const bool is_gt = k > thr;
     const bool is_eq = i < s_hi && k == thr;
     const uint64_t mgt = __ballot(is_gt);
@@ -174,7 +209,7 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
     }
     gt_before += uint32_t(__popcll(mgt));
     eq_before += uint32_t(__popcll(meq));
-  }
+  });
 }
 
 // Chunk length of a window on the split path (multiple of 64), or 0 when the
