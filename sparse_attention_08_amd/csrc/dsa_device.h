@@ -60,6 +60,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
+// within each row of 16 lanes by shifts of 1, 2, 4 and 8 (lanes shifted in
+// from outside the row add 0), then lane 15 of rows 0 and 2 into rows 1 and 3,
+// then lane 31 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  int x = int(v);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return uint32_t(x);
+}
+
 // Exclusive prefix sum over the threads of a block of NT threads (NT/64 waves).
 // `tmp` needs NT/64 entries of shared memory.  Returns the prefix; `total` gets
 // the block total.  Contains two __syncthreads().
@@ -69,12 +84,7 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* tm
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_sum(v);
   if (lane == kWave - 1) tmp[wave] = x;
   __syncthreads();
   uint32_t off = 0, tot = 0;

@@ -23,7 +23,8 @@ struct SelectShared {
   uint32_t hist[kBins];
   uint32_t tmp[2 * kNW];
   uint32_t seg_cnt[2 * kNW];
-  uint32_t pick[2];
+  uint32_t wsum[kNW];  // radix pass: wave totals of the bin counts
+  uint32_t pick[2];    // radix pass: the digit and the rank left
 };
 
 // Keys of a row held in LDS, or read (and mapped) from the fp32 scores.
@@ -123,6 +124,7 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
 
   uint32_t thr = 0u, need_eq = 0u;
   if (n_sel > uint32_t(K)) {
+    for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;  // ordered by block_min_max
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     for_keys<NT>(key, n, [&](int, uint32_t k) {
       if (k != 0u) {
@@ -136,13 +138,17 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
     uint32_t pmask = shift >= 32 ? 0u : ~((1u << shift) - 1u);
     uint32_t prefix = kmax & pmask;
     uint32_t remaining = uint32_t(K);
+    // Each pass: histogram (barrier); every thread reads its bins into registers
+    // and clears them, wave prefix sums by DPP, wave totals (barrier); the thread
+    // whose bins hold the k-th key picks the digit (barrier).  The wave totals
+    // are read before the third barrier and written again only before the next
+    // pass's second; the pick is read after the third and written again only
+    // after the next pass's second.
 #pragma unroll 1
     while (shift > 0) {
       const int nb = shift < 11 ? shift : 11;
       shift -= nb;
       const uint32_t dmask = (1u << nb) - 1u;
-      for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
-      __syncthreads();
       for_keys<NT>(key, n, [&](int, uint32_t k) {
         if (k != 0u && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
       });
@@ -150,28 +156,36 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
       // thread j owns the bins of slot (NT-1-j), so an exclusive prefix over
       // threads is the count of keys in higher bins
       const int base = (NT - 1 - tid) * kBPT;
+      uint32_t h[kBPT];
       uint32_t local = 0u;
 #pragma unroll
-      for (int j = 0; j < kBPT; ++j) local += sh.hist[base + j];
-      uint32_t total;
-      const uint32_t above = block_exclusive_sum<NT>(local, sh.tmp, total);
+      for (int j = 0; j < kBPT; ++j) {
+        h[j] = sh.hist[base + j];
+        local += h[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kBPT; ++j) sh.hist[base + j] = 0u;  // for the next pass
+      const uint32_t incl = wave_inclusive_sum(local);
+      if (lane == kWave - 1) sh.wsum[wave] = incl;
+      __syncthreads();
+      uint32_t above = incl - local;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) above += w < wave ? sh.wsum[w] : 0u;
       if (above < remaining && above + local >= remaining) {
         uint32_t c = above;
+#pragma unroll
         for (int j = kBPT - 1; j >= 0; --j) {
-          const uint32_t h = sh.hist[base + j];
-          if (c + h >= remaining) {
+          if (c < remaining && c + h[j] >= remaining) {
             sh.pick[0] = uint32_t(base + j);
             sh.pick[1] = remaining - c;
-            break;
           }
-          c += h;
+          c += h[j];
         }
       }
       __syncthreads();
       prefix |= sh.pick[0] << shift;
       pmask |= dmask << shift;
       remaining = sh.pick[1];
-      __syncthreads();
     }
     thr = prefix;
     need_eq = remaining;
