@@ -100,7 +100,7 @@ struct MlaShared {
   int idx[kMaxIdx + 3 * kKT];     // this workgroup's slice of the top-k row (-1 -> row 0),
                                   // plus up to 3 padding tiles
   uint32_t vmask[kMaxTiles + 3];  // per tile: bit j set = selected key j is valid
-  int last;
+  int wlast[kWaves];              // per wave: last valid position of its index loads, or -1
   int redo[2];                    // per pass: some head needs the second pass
 };
 
@@ -526,42 +526,50 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   int i1 = int(int64_t(ntiles) * (blockIdx.z + 1) / nsplit);
   const int32_t* irow = idx + t * K;
 
-  // Stage this workgroup's index slice in LDS (padded with -1 to whole tiles,
-  // -1 stored as row 0) with per-tile validity masks, and drop trailing tiles
-  // that hold only -1 padding (top-k rows are -1 padded at the end); padding
-  // elsewhere is masked per key.
+  // The index slice and the query's Q^T are loaded together: the index loads
+  // first (vector-memory loads complete in order, so staging the indices waits
+  // only for them), then Q, which stays in flight until the first tile.
+  const int jbase = i0 * kKT;
+  const int nx = (i1 - i0) * kKT;
+  constexpr int kPer = kMaxIdx / kThreads;
+  int rv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int x = tid + u * kThreads;
+    const int j = jbase + x;
+    rv[u] = (x < nx && j < K) ? irow[j] : -1;
+  }
+  // Q^T fragments: lane holds q[t, head, 16*st + 8*half .. +8].  A head past H
+  // (the last head block of a head count that is not a multiple of 128) reads
+  // head H-1 instead: finite values whose results are never written.
+  bf16x8_t qf[kQSteps];
   {
-    if (tid == 0) sh.last = -1;
-    __syncthreads();
-    int last = -1;
-    const int jbase = i0 * kKT;
-    const int nx = (i1 - i0) * kKT;
-    // every thread issues all its index loads (up to kMaxIdx / kThreads) before
-    // it waits for any of them
-    constexpr int kPer = kMaxIdx / kThreads;
-    int rv[kPer];
+    const __bf16* qr = q + (t * H + (hvalid ? head : H - 1)) * int64_t(kDqk) + 8 * half;
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * st);
+  }
+
+  // Stage the index slice in LDS (padded with -1 to whole tiles, -1 stored as
+  // row 0) with per-tile validity masks, and drop trailing tiles that hold only
+  // -1 padding (top-k rows are -1 padded at the end); padding elsewhere is
+  // masked per key.
+  {
+    int wl = -1;  // last valid position among this wave's loads (wave-uniform)
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int x = tid + u * kThreads;
-      const int j = jbase + x;
-      rv[u] = (x < nx && j < K) ? irow[j] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int x = tid + u * kThreads;
-      if (x < nx) {
-        const int r = rv[u];
-        sh.idx[x] = r < 0 ? 0 : r;
-        if (r >= 0) last = x;
-      }
+      if (x < nx) sh.idx[x] = rv[u] < 0 ? 0 : rv[u];
       // x advances by whole waves: 2 tiles per ballot (the wave is uniform in x < nx)
       const uint64_t b = __ballot(x < nx && rv[u] >= 0);
       if (x < nx && lane == 0) sh.vmask[x / kKT] = uint32_t(b);
       if (x < nx && lane == 32) sh.vmask[x / kKT] = uint32_t(b >> 32);
+      if (b != 0ull) wl = u * kThreads + wave * kWave + 63 - __builtin_clzll(b);
     }
-    if (last >= 0) atomicMax(&sh.last, last);
+    if (lane == 0) sh.wlast[wave] = wl;
     __syncthreads();
-    last = sh.last;
+    int last = sh.wlast[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) last = max(last, sh.wlast[w]);
     i1 = last < 0 ? i0 : i0 + last / kKT + 1;
   }
   const int nt = i1 - i0;
@@ -574,17 +582,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   }
   if (tid < 2) sh.redo[tid] = 0;
   __syncthreads();
-
-  // Q^T fragments: lane holds q[t, head, 16*st + 8*half .. +8]
-  bf16x8_t qf[kQSteps];
-  {
-    const __bf16* qr = q + (t * H + (hvalid ? head : 0)) * int64_t(kDqk) + 8 * half;
-#pragma unroll
-    for (int st = 0; st < kQSteps; ++st) {
-      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qr + 16 * st);
-      qf[st] = hvalid ? v : bf16x8_t{};
-    }
-  }
+  // Q^T has landed before the first gather is issued.  (The gathers are inline
+  // asm that the compiler does not count; waiting for Q at its first use would
+  // make it wait for gathers issued after Q as well.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   f32x16_t o[kVTiles];
   float m_ref = -FLT_MAX;  // per head (lane column, base-2 units), same in both lane halves
@@ -641,17 +642,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   int lane_e = lane;
   asm volatile("" : "+v"(lane_e));
   const int head_e = h0 + (lane_e & 31);
+  const int half_e = lane_e >> 5;
   const bool hvalid_e = head_e < H;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_h = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-  const int col0 = lane & 31;
+  const int col0 = lane_e & 31;
   if (nsplit == 1) {
-    if (lse && half == 0 && hvalid_e) lse[t * H + head_e] = lse_h;
+    if (lse && half_e == 0 && hvalid_e) lse[t * H + head_e] = lse_h;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int hr = h0 + acc_row(r, half);
-      const float ir = __shfl(inv, acc_row(r, half));
+      const int hr = h0 + acc_row(r, half_e);
+      const float ir = __shfl(inv, acc_row(r, half_e));
       if (hr < H) {
         uint16_t* orow = reinterpret_cast<uint16_t*>(out) + (t * H + hr) * int64_t(kDv) + col0;
 #pragma unroll
@@ -660,11 +662,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     }
   } else {
     const int64_t slot = t * nsplit + blockIdx.z;
-    if (half == 0 && hvalid_e) part_lse[slot * H + head_e] = lse_h;
+    if (half_e == 0 && hvalid_e) part_lse[slot * H + head_e] = lse_h;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int hr = h0 + acc_row(r, half);
-      const float ir = __shfl(inv, acc_row(r, half));
+      const int hr = h0 + acc_row(r, half_e);
+      const float ir = __shfl(inv, acc_row(r, half_e));
       if (hr < H) {
         uint16_t* orow = part_o + (slot * H + hr) * int64_t(kDv) + col0;
 #pragma unroll
