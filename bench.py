@@ -135,7 +135,12 @@ def stage_bench(args, dsa, synth, np, torch):
     lse = torch.empty((lay.n_q, w.mla_heads), dtype=torch.float32, device=dev)
     ws = torch.empty(max(dsa.sparse_mla_workspace(lay.n_q, w.mla_heads, w.d_qk, w.d_v, K, 1), 1),
                      dtype=torch.uint8, device=dev)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    # Cache flush for the HBM-bound stages: a 1 GiB read.  A write would leave up to
+    # the size of the last-level cache in dirty lines, whose write-back would then
+    # run inside the timed region and halve the bandwidth the stage sees.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush.sum()
+    torch.cuda.synchronize()
     hbm_bound = {"indexer": w.decode, "topk": True, "mla": w.decode}
     fns = {
         "indexer": lambda: dsa.dsa_indexer_scores(q, k, wt, rs, re, k_scale=ks, scores=scores),
@@ -160,7 +165,7 @@ def stage_bench(args, dsa, synth, np, torch):
         times = []
         for _ in range(args.steps):
             if hbm_bound[name]:
-                flush.fill_(float(len(times)))
+                flush.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             f()

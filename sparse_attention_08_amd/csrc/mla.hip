@@ -73,6 +73,7 @@ constexpr bool kslot_is_permutation() {
 }
 static_assert(kslot_is_permutation(), "slots are a permutation of 0 .. 31");
 constexpr int kRegionB = kKT * 128;             // 4096
+constexpr int kEpCol = 72;                      // epilogue staging: bytes per value column
 constexpr int kTileBytes = kRegionA + kRegionB;  // 37376
 constexpr int kQSteps = kDqk / 16;              // 36 K-steps of 16 dims
 constexpr int kVTiles = kDv / 32;               // 16 value tiles of 32 columns
@@ -87,6 +88,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
 
@@ -130,42 +132,37 @@ __device__ __forceinline__ uint8_t* kvbuf() {
 // result read by a VALU (or accumulation-register move) needs 12, and chained
 // accumulation (srcC = previous dst) needs none.
 //
-// Two chained MFMAs in one asm statement (between two separate asm statements
-// the compiler puts a wait state of its own; a chain needs none).
-__device__ __forceinline__ void mfma_v0_2(f32x16_t& d, bf16x8_t a0, bf16x8_t b0, bf16x8_t a1,
-                                          bf16x8_t b1) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
-      : "=&v"(d) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+// One MFMA per asm statement.  The matrix core runs an MFMA for 32 cycles; the
+// wave issues the instructions that follow it meanwhile and waits for the core
+// only at the next MFMA, so the LDS reads, gathers and softmax steps are spread
+// one small group per MFMA gap (a chained pair in one statement would leave one
+// gap per two MFMAs, too short for the work placed there).  Between two asm
+// statements the compiler may add a wait state of its own; a chain needs none.
+__device__ __forceinline__ void mfma_v0(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_v_2(f32x16_t& d, bf16x8_t a0, bf16x8_t b0, bf16x8_t a1,
-                                         bf16x8_t b1) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
-      : "+v"(d) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+__device__ __forceinline__ void mfma_v(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-// last MFMA of a chain whose result the VALU reads next; its operands are
-// VALU-written just before (the leading nop)
-__device__ __forceinline__ void mfma_v_last(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3"
-      : "+v"(d) : "v"(a), "v"(b));
+// an MFMA whose operands are VALU-written just before (the leading nop)
+__device__ __forceinline__ void mfma_v_nop(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// 12 wait states: an MFMA result (arch VGPRs) may be read by the VALU after them
+__device__ __forceinline__ void mfma_result_wait(f32x16_t& d) {
+  asm volatile("s_nop 7\n\ts_nop 3" : "+v"(d));
 }
 // accumulation into O.  kNop: the leading wait states cover an operand the
 // VALU may have written just before (the first MFMAs of a tile, after P is
 // moved into place); the other operands come from LDS reads or from VALU work
 // many instructions earlier (a host test scans the compiled code for a VALU
 // write closer than two wait states to the MFMA that reads it).
-// Two chained MFMAs (both key steps of one value tile) in one asm statement.
 template <bool kNop>
-__device__ __forceinline__ void mfma_a2(f32x16_t& d, bf16x8_t a0, bf16x8_t b0, bf16x8_t a1,
-                                        bf16x8_t b1) {
+__device__ __forceinline__ void mfma_a(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
   if constexpr (kNop)
-    asm volatile(
-        "s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
-        : "+a"(d) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
   else
-    asm volatile(
-        "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
-        : "+a"(d) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 // before the VALU touches O after MFMAs into it
 __device__ __forceinline__ void o_fence(f32x16_t (&o)[kVTiles]) {
@@ -278,31 +275,34 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint3
   };
   DmaRows rows{};
   if constexpr (kDma) rows = dma_rows(sidx, lt_dma, lane);  // ahead of the ring reads
-  // fragment reads in pairs, two pairs ahead: one explicit wait per two MFMAs
+  // fragment reads four steps ahead: one explicit wait per MFMA
   bf16x8_t fr[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) fr[st] = frag(st);
   f32x16_t s;
 #pragma unroll
-  for (int st = 0; st < kQSteps; st += 2) {
-    if (st + 2 < kQSteps) wait_lgkm<2>();  // steps st, st+1 read; st+2, st+3 in flight
+  for (int st = 0; st < kQSteps; ++st) {
+    // reads of steps st+1 .. st+3 may stay in flight
+    if (st + 3 < kQSteps) wait_lgkm<3>();
+    else if (st + 2 < kQSteps) wait_lgkm<2>();
+    else if (st + 1 < kQSteps) wait_lgkm<1>();
     else wait_lgkm<0>();
-    if (st == 0) mfma_v0_2(s, fr[0], qf[0], fr[1], qf[1]);
-    else mfma_v_2(s, fr[st % 4], qf[st], fr[(st + 1) % 4], qf[st + 1]);
+    if (st == 0) mfma_v0(s, fr[0], qf[0]);
+    else mfma_v(s, fr[st % 4], qf[st]);
     if (st + 4 < kQSteps) fr[st % 4] = frag(st + 4);
-    if (st + 5 < kQSteps) fr[(st + 1) % 4] = frag(st + 5);
     if constexpr (kDma) {
       // the gather of a later tile, spread between the MFMAs
-      if (st % 4 == 0 && st / 4 < kKT / kWaves) dma_latent<BD>(rows, st / 4, kv, wave, lane);
-      if (st == 32) dma_rope<BD>(rows, kv, wave, lane);
+      if (st % 4 == 1 && st / 4 < kKT / kWaves) dma_latent<BD>(rows, st / 4, kv, wave, lane);
+      if (st == 33) dma_rope<BD>(rows, kv, wave, lane);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep this order
   }
   // The key mask as one more K-step: dim 0 of the step is -inf for a masked key
   // (lanes 0..31 of the K side) against 1 on the Q side, every other product is
   // 0 * 0, so S = -inf exactly for masked keys and unchanged for the others.
-  // Lanes 32..63 carry dims 8..15 of the step: zero on both sides.
-  {
+  // Lanes 32..63 carry dims 8..15 of the step: zero on both sides.  Tiles whose
+  // 32 keys are all valid (all but the last of a row in practice) skip it.
+  if (__builtin_amdgcn_readfirstlane(int(vmask)) != -1) {
     // operands are rebuilt for every tile, not held in registers across the loop
     int l = lane;
     asm volatile("" : "+v"(l));
@@ -314,8 +314,11 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint3
     // the nop: the lane mask may have just been written by the VALU (readfirstlane)
     asm("s_nop 3\n\tv_cndmask_b32_e64 %0, %1, 0, %2" : "=v"(ka[0]) : "v"(ninf), "s"(keep));
     const i32x4_t qa = {l < 32 ? 0x3F80 : 0, 0, 0, 0};
-    mfma_v_last(s, __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qa));
+    mfma_v_nop(s, __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qa));
   }
+  // S is complete: the compiler, which does not see the MFMAs, may reuse
+  // registers or read S right after this point
+  mfma_result_wait(s);
   return s;
 }
 
@@ -325,9 +328,17 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint3
 // the max of the first tile that has a finite logit for the head, so
 // P <= 2^kSpan unless a later tile's max exceeds m_ref + kSpan; that sets
 // `over` and the query is computed again with m_ref = the true max (m_max
-// tracks it).  O is never rescaled inside the loop.  The work is cut into
-// kSmStages stages that the P.V of the previous tile interleaves with its
-// MFMAs.
+// tracks it).  O is never rescaled inside the loop.
+//
+// The work is cut into kSmPieces pieces of at most about four VALU operations
+// (a transcendental counts as several): the wave runs that much beside an MFMA
+// at no cost, and the P.V of the previous tile issues one piece after each of
+// its MFMAs from the third on:
+//   0 .. 3   max over 4 of the lane's 16 keys each
+//   4        max over the lane pair that shares the head, scaled
+//   5, 6     reference and running max; overflow flag
+//   7 .. 22  P of key register r = piece - 7
+//   23 .. 26 bf16 rounding and row sum of key registers 2j, 2j+1, 2j+8, 2j+9
 struct Softmax {
   f32x16_t s;      // S^T of the tile: lane = head l%32, 16 keys
   float mt;
@@ -336,93 +347,73 @@ struct Softmax {
   __device__ __forceinline__ bf16x8_t p0() const { return __builtin_bit_cast(bf16x8_t, p0w); }
   __device__ __forceinline__ bf16x8_t p1() const { return __builtin_bit_cast(bf16x8_t, p1w); }
 
-  // The stage's inputs pass through an empty volatile asm first: the stage
-  // is pure arithmetic, which the instruction selector would otherwise place
+  // A piece's inputs pass through an empty volatile asm first: the pieces are
+  // pure arithmetic, which the instruction selector would otherwise place
   // anywhere (in practice all of it ahead of the P.V MFMAs it is meant to hide
   // behind).
   template <int K>
-  __device__ __forceinline__ void pin() {
-    if constexpr (K == 0) {
-      asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]), "+v"(s[4]), "+v"(s[5]),
-                   "+v"(s[6]), "+v"(s[7]));
-      asm volatile("" : "+v"(s[8]), "+v"(s[9]), "+v"(s[10]), "+v"(s[11]), "+v"(s[12]),
-                   "+v"(s[13]), "+v"(s[14]), "+v"(s[15]));
-    } else if constexpr (K == 1) {
-      asm volatile("" : "+v"(mt));
-    } else if constexpr (K < 6) {
-      const int r0 = 4 * (K - 2);
-      asm volatile("" : "+v"(s[r0]), "+v"(s[r0 + 1]), "+v"(s[r0 + 2]), "+v"(s[r0 + 3]));
-    } else {
-      const int r0 = 4 * (K - 6);
-      asm volatile("" : "+v"(s[r0]), "+v"(s[r0 + 1]), "+v"(s[r0 + 2]), "+v"(s[r0 + 3]),
-                   "+v"(s[r0 + 8]), "+v"(s[r0 + 9]), "+v"(s[r0 + 10]), "+v"(s[r0 + 11]));
-    }
-  }
-
-  template <int K>
-  __device__ __forceinline__ void stage(float scale2, float& m_ref, float& m_max, bool& over,
+  __device__ __forceinline__ void piece(float scale2, float& m_ref, float& m_max, bool& over,
                                         float& l_run) {
-    pin<K>();
-    if constexpr (K == 0) {
-      mt = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-    } else if constexpr (K == 1) {
+    if constexpr (K < 4) {
+      constexpr int r0 = 4 * K;
+      asm volatile("" : "+v"(s[r0]), "+v"(s[r0 + 1]), "+v"(s[r0 + 2]), "+v"(s[r0 + 3]));
+      const float m = fmaxf(fmaxf(s[r0], s[r0 + 1]), fmaxf(s[r0 + 2], s[r0 + 3]));
+      mt = K == 0 ? m : fmaxf(mt, m);
+    } else if constexpr (K == 4) {
+      asm volatile("" : "+v"(mt));
       // lanes l and l^32 hold the two key halves of head l%32
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                        false, false);
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
+    } else if constexpr (K == 5) {
+      asm volatile("" : "+v"(mt));
       // -FLT_MAX = no finite logit yet (an all-masked tile keeps it)
       m_ref = m_ref == -FLT_MAX ? fmaxf(mt, -FLT_MAX) : m_ref;
       m_max = fmaxf(m_max, mt);
+    } else if constexpr (K == 6) {
+      asm volatile("" : "+v"(mt));
       over = over || mt > m_ref + kSpan;
-    } else if constexpr (K < 6) {
-#pragma unroll
-      for (int r = 4 * (K - 2); r < 4 * (K - 2) + 4; ++r)
-        s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale2, -m_ref));
+    } else if constexpr (K < 23) {
+      constexpr int r = K - 7;
+      asm volatile("" : "+v"(s[r]));
+      s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale2, -m_ref));
     } else {
       // P rounded to bf16 (v_cvt_pk_bf16_f32, round to nearest even); the row
       // sum adds the rounded values (v_dot2 with ones), so the output is an
       // exact convex combination of value rows up to fp32 accumulation
+      constexpr int r = 2 * (K - 23);
+      asm volatile("" : "+v"(s[r]), "+v"(s[r + 1]), "+v"(s[r + 8]), "+v"(s[r + 9]));
       const bf16x2_t ones = {__bf16(1.0f), __bf16(1.0f)};
-      if constexpr (K == 6) ps = 0.0f;
-#pragma unroll
-      for (int r = 4 * (K - 6); r < 4 * (K - 6) + 4; r += 2) {
-        const bf16x2_t a = {__bf16(s[r]), __bf16(s[r + 1])};
-        const bf16x2_t b = {__bf16(s[r + 8]), __bf16(s[r + 9])};
-        ps = __builtin_amdgcn_fdot2_f32_bf16(a, ones, ps, false);
-        ps = __builtin_amdgcn_fdot2_f32_bf16(b, ones, ps, false);
-        p0w[r / 2] = __builtin_bit_cast(int, a);
-        p1w[r / 2] = __builtin_bit_cast(int, b);
-      }
-      if constexpr (K == 7) l_run += ps;
+      const bf16x2_t a = {__bf16(s[r]), __bf16(s[r + 1])};
+      const bf16x2_t b = {__bf16(s[r + 8]), __bf16(s[r + 9])};
+      float x = K == 23 ? 0.0f : ps;
+      x = __builtin_amdgcn_fdot2_f32_bf16(a, ones, x, false);
+      x = __builtin_amdgcn_fdot2_f32_bf16(b, ones, x, false);
+      p0w[r / 2] = __builtin_bit_cast(int, a);
+      p1w[r / 2] = __builtin_bit_cast(int, b);
+      if constexpr (K == 26) l_run += x;
+      else ps = x;
     }
   }
 };
-constexpr int kSmStages = 8;
+constexpr int kSmPieces = 27;
+constexpr int kSmFirstGap = 2;  // the first P.V gaps carry only the reads that start the ring
+static_assert(kSmFirstGap + kSmPieces <= 2 * kVTiles, "the softmax pieces fit the P.V gaps");
 
-template <int K>
-__device__ __forceinline__ void sm_stage_if(int k, Softmax& sm, float scale2, float& m_ref,
-                                            float& m_max, bool& over, float& l_run) {
-  if (k == K) sm.template stage<K>(scale2, m_ref, m_max, over, l_run);
-}
-
-__device__ __forceinline__ void sm_stage(int k, Softmax& sm, float scale2, float& m_ref,
+// piece k of the softmax (k is a constant after unrolling)
+template <int K = 0>
+__device__ __forceinline__ void sm_piece(int k, Softmax& sm, float scale2, float& m_ref,
                                          float& m_max, bool& over, float& l_run) {
-  sm_stage_if<0>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<1>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<2>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<3>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<4>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<5>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<6>(k, sm, scale2, m_ref, m_max, over, l_run);
-  sm_stage_if<7>(k, sm, scale2, m_ref, m_max, over, l_run);
+  if constexpr (K < kSmPieces) {
+    if (k == K) sm.template piece<K>(scale2, m_ref, m_max, over, l_run);
+    else sm_piece<K + 1>(k, sm, scale2, m_ref, m_max, over, l_run);
+  }
 }
 
 __device__ __forceinline__ void softmax_all(Softmax& sm, float scale2, float& m_ref,
                                             float& m_max, bool& over, float& l_run) {
 #pragma unroll
-  for (int k = 0; k < kSmStages; ++k) sm_stage(k, sm, scale2, m_ref, m_max, over, l_run);
+  for (int k = 0; k < kSmPieces; ++k) sm_piece(k, sm, scale2, m_ref, m_max, over, l_run);
 }
 
 // O += P . V for the tile in buffer B (B < 0: the buffer `buf` chosen at run
@@ -431,8 +422,8 @@ __device__ __forceinline__ void softmax_all(Softmax& sm, float scale2, float& m_
 // reads 4 value columns of key row k0+m and the transpose hands lane i the 4
 // keys k0..k0+3 of column n0+i.  Lane half h needs keys {4h..4h+3} (first read)
 // and {8+4h..8+4h+3} (second read) of each 16-key step: the order in which P
-// sits in the S^T accumulator.  With sm, the softmax stages of the current tile
-// are interleaved with the MFMAs.
+// sits in the S^T accumulator.  With kSm, one softmax piece of the current tile
+// follows each MFMA from gap kSmFirstGap on.
 template <int B, bool kSm>
 __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_t p1,
                                         f32x16_t (&o)[kVTiles], int lane, Softmax& sm,
@@ -454,22 +445,25 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 2 * kRowA));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // fragment reads in pairs, two pairs ahead: one explicit wait per two MFMAs
+  // fragment reads four steps ahead (two LDS reads each): one explicit wait per MFMA
   bf16x8_t fr[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) fr[m] = rd(m);
 #pragma unroll
-  for (int m = 0; m < 2 * kVTiles; m += 2) {
-    if (m + 2 < 2 * kVTiles) wait_lgkm<4>();  // steps m, m+1 read; m+2, m+3 in flight
+  for (int m = 0; m < 2 * kVTiles; ++m) {
+    // reads of steps m+1 .. m+3 may stay in flight
+    if (m + 3 < 2 * kVTiles) wait_lgkm<6>();
+    else if (m + 2 < 2 * kVTiles) wait_lgkm<4>();
+    else if (m + 1 < 2 * kVTiles) wait_lgkm<2>();
     else wait_lgkm<0>();
-    if (m == 0)
-      mfma_a2<true>(o[0], p0, fr[0], p1, fr[1]);
+    if (m < 2)
+      mfma_a<true>(o[m >> 1], (m & 1) ? p1 : p0, fr[m % 4]);
     else
-      mfma_a2<false>(o[m >> 1], p0, fr[m % 4], p1, fr[(m + 1) % 4]);
+      mfma_a<false>(o[m >> 1], (m & 1) ? p1 : p0, fr[m % 4]);
     if (m + 4 < 2 * kVTiles) fr[m % 4] = rd(m + 4);
-    if (m + 5 < 2 * kVTiles) fr[(m + 1) % 4] = rd(m + 5);
     if constexpr (kSm) {
-      if (m / 2 < kSmStages) sm_stage(m / 2, sm, scale2, m_ref, m_max, over, l_run);
+      if (m >= kSmFirstGap && m - kSmFirstGap < kSmPieces)
+        sm_piece(m - kSmFirstGap, sm, scale2, m_ref, m_max, over, l_run);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep this order
   }
@@ -647,31 +641,58 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_h = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // Output rows (or split partials) of the wave's 32 heads, 1 KB each in bf16:
+  // the tile buffers are free now (the barrier above follows every wave's last
+  // read), so each wave stages its block in its own buffer, value column by value
+  // column (32 heads x 2 bytes per column, kEpCol bytes apart), then reads it back
+  // with transposing reads that hand each lane 8 consecutive columns of one head,
+  // which it writes with one 16-byte store.
+  //   write: accumulator registers 4g .. 4g+3 of a lane are 4 consecutive heads
+  //          of one column: scaled, rounded, one 8-byte write;
+  //   read:  in each 16-lane group, lane 4m+q reads heads 4q .. 4q+3 of column
+  //          c0+m; the transpose hands lane i columns c0 .. c0+3 of head i.
   const int col0 = lane_e & 31;
-  if (nsplit == 1) {
-    if (lse && half_e == 0 && hvalid_e) lse[t * H + head_e] = lse_h;
+  uint8_t* eb = wave == 0 ? g_kv0 : wave == 1 ? g_kv1 : wave == 2 ? g_kv2 : g_kv3;
+  {
+    float ir[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int hr = h0 + acc_row(r, half_e);
-      const float ir = __shfl(inv, acc_row(r, half_e));
-      if (hr < H) {
-        uint16_t* orow = reinterpret_cast<uint16_t*>(out) + (t * H + hr) * int64_t(kDv) + col0;
+    for (int r = 0; r < 16; ++r) ir[r] = __shfl(inv, acc_row(r, half_e));
+    uint8_t* wb = eb + col0 * kEpCol + 8 * half_e;
 #pragma unroll
-        for (int n = 0; n < kVTiles; ++n) orow[n * 32] = f32_to_bf16_bits(o[n][r] * ir);
+    for (int n = 0; n < kVTiles; ++n) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x2_t lo = {__bf16(o[n][4 * g] * ir[4 * g]), __bf16(o[n][4 * g + 1] * ir[4 * g + 1])};
+        const bf16x2_t hi = {__bf16(o[n][4 * g + 2] * ir[4 * g + 2]),
+                             __bf16(o[n][4 * g + 3] * ir[4 * g + 3])};
+        const uint2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        *reinterpret_cast<uint2*>(wb + n * 32 * kEpCol + g * 16) = v;
       }
     }
-  } else {
-    const int64_t slot = t * nsplit + blockIdx.z;
-    if (half_e == 0 && hvalid_e) part_lse[slot * H + head_e] = lse_h;
+  }
+  const int li = lane_e & 15;
+  const int grp = lane_e >> 4;
+  uint16_t* obase = nsplit == 1 ? reinterpret_cast<uint16_t*>(out) + t * H * int64_t(kDv)
+                                : part_o + (t * nsplit + blockIdx.z) * H * int64_t(kDv);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int hr = h0 + acc_row(r, half_e);
-      const float ir = __shfl(inv, acc_row(r, half_e));
-      if (hr < H) {
-        uint16_t* orow = part_o + (slot * H + hr) * int64_t(kDv) + col0;
+  for (int hh = 0; hh < 2; ++hh) {
+    const int hd = h0 + 16 * hh + li;  // the head this lane stores
 #pragma unroll
-        for (int n = 0; n < kVTiles; ++n) orow[n * 32] = f32_to_bf16_bits(o[n][r] * ir);
-      }
+    for (int cb = 0; cb < kVTiles; ++cb) {
+      const int c0 = 32 * cb + 8 * grp;
+      const uint8_t* rb = eb + (c0 + (li >> 2)) * kEpCol + (16 * hh + 4 * (li & 3)) * 2;
+      const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(rb));
+      const v4i16_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(rb + 4 * kEpCol));
+      if (hd < H)
+        *reinterpret_cast<v8i16_t*>(obase + hd * int64_t(kDv) + c0) =
+            __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+  if (half_e == 0 && hvalid_e) {
+    if (nsplit == 1) {
+      if (lse) lse[t * H + head_e] = lse_h;
+    } else {
+      part_lse[(t * nsplit + blockIdx.z) * H + head_e] = lse_h;
     }
   }
 }

@@ -11,9 +11,9 @@ gfx950 with the build's flags and checks, on the generated code, that
   after the MFMA (likewise), and
 * the kernel does not spill (a spill would put scratch traffic into the loop).
 
-A wait state is one instruction, or N+1 for ``s_nop N``.  A label closer than
-the required distance is reported too: a branch into it could bring a VALU write
-from elsewhere."""
+A wait state is one instruction, or N+1 for ``s_nop N``.  The check follows
+every control-flow path (fall-through and branch targets) within those
+distances."""
 import os
 import re
 import shutil
@@ -43,44 +43,80 @@ def _operands(line):
     return [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
 
 
+def _cfg(lines):
+    """Successor and predecessor lists of the instruction lines (labels end with ':')."""
+    label_at = {ln[:-1]: i for i, ln in enumerate(lines) if ln.endswith(":")}
+    succ = [[] for _ in lines]
+    pred = [[] for _ in lines]
+    for i, ln in enumerate(lines):
+        op = ln.split()[0]
+        nxt = []
+        if op.startswith("s_cbranch") or op == "s_branch":
+            target = ln.split()[1]
+            if target in label_at:
+                nxt.append(label_at[target])
+        if op not in ("s_branch", "s_endpgm", "s_setpc_b64") and i + 1 < len(lines):
+            nxt.append(i + 1)
+        succ[i] = nxt
+        for j in nxt:
+            pred[j].append(i)
+    return succ, pred
+
+
 def scan(lines):
-    """Problems found in one kernel's instruction lines (labels end with ':')."""
+    """Problems found in one kernel's instruction lines (labels end with ':').
+
+    Every path is followed, through branches and into labels, in both
+    directions: backwards from an MFMA for a VALU write of one of its operands,
+    forwards from an MFMA with an arch-VGPR result for a VALU read of it."""
+    succ, pred = _cfg(lines)
     problems = []
+
+    def back(i, srcs, ws, mfma, seen):
+        for j in pred[i]:
+            if (j, ws) in seen:
+                continue
+            seen.add((j, ws))
+            p = lines[j]
+            if p.endswith(":"):
+                back(j, srcs, ws, mfma, seen)
+                continue
+            op = p.split()[0]
+            if op.startswith("v_") and not op.startswith("v_mfma") and _operands(p):
+                if _regs(_operands(p)[0]) & srcs:
+                    problems.append(f"{p} writes an operand of {mfma} {ws} wait states before it")
+                    continue
+            w = ws + _wait_states(p)
+            if w < 2:
+                back(j, srcs, w, mfma, seen)
+
+    def fwd(i, dst, ws, mfma, seen):
+        for j in succ[i]:
+            if (j, ws) in seen:
+                continue
+            seen.add((j, ws))
+            n = lines[j]
+            if n.endswith(":"):
+                fwd(j, dst, ws, mfma, seen)
+                continue
+            op = n.split()[0]
+            if op.startswith("v_") and not op.startswith("v_mfma"):
+                if any(_regs(o) & dst for o in _operands(n)[1:]):
+                    problems.append(f"{n} reads the result of {mfma} {ws} wait states after it")
+                    continue
+            w = ws + _wait_states(n)
+            if w < 12:
+                fwd(j, dst, w, mfma, seen)
+
     for i, ins in enumerate(lines):
         if not ins.startswith("v_mfma"):
             continue
         ops = _operands(ins)
-        srcs = _regs(ops[1]) | _regs(ops[2])
-        ws = 0
-        for p in reversed(lines[max(0, i - 16):i]):
-            if p.endswith(":"):
-                problems.append(f"label {p} {ws} wait states before {ins}")
-                break
-            op = p.split()[0]
-            if op.startswith("v_") and not op.startswith("v_mfma") and _operands(p):
-                if _regs(_operands(p)[0]) & srcs:
-                    problems.append(f"{p} writes an operand of {ins} {ws} wait states before it")
-                    break
-            ws += _wait_states(p)
-            if ws >= 2:
-                break
+        back(i, _regs(ops[1]) | _regs(ops[2]), 0, ins, set())
         dst = _regs(ops[0])
-        if not any(r.startswith("v") for r in dst):
-            continue  # accumulation registers: read only by accvgpr moves after a fence
-        ws = 0
-        for n in lines[i + 1:i + 24]:
-            if n.endswith(":"):
-                if ws < 12:
-                    problems.append(f"label {n} {ws} wait states after {ins}")
-                break
-            op = n.split()[0]
-            if op.startswith("v_") and not op.startswith("v_mfma"):
-                if any(_regs(o) & dst for o in _operands(n)[1:]) and ws < 12:
-                    problems.append(f"{n} reads the result of {ins} {ws} wait states after it")
-                    break
-            ws += _wait_states(n)
-            if ws >= 12:
-                break
+        if any(r.startswith("v") for r in dst):
+            # accumulation registers are read only by accvgpr moves after a fence
+            fwd(i, dst, 0, ins, set())
     return problems
 
 
@@ -134,3 +170,15 @@ def test_scanner_catches_planted_hazards():
     late_read = ["v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]", "s_nop 7", "s_nop 3",
                  "v_max_f32_e32 v30, v1, v1"]
     assert not scan(late_read)
+    # through a taken branch: the read at the target is 2 wait states away
+    branch_read = ["v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]", "s_cbranch_scc1 .LBB0_9",
+                   "s_nop 7", "s_nop 7", ".LBB0_9:", "v_max_f32_e32 v30, v1, v1"]
+    assert scan(branch_read)
+    # a write on the path that jumps to the MFMA's block
+    branch_write = ["v_mov_b32_e32 v18, v3", "s_branch .LBB0_4", "s_nop 7", ".LBB0_4:",
+                    "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]"]
+    assert scan(branch_write)
+    # both paths into a join far enough from the MFMA: clean
+    join = ["v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]", "s_cbranch_scc1 .LBB0_7",
+            "s_nop 7", ".LBB0_7:", "s_nop 7", "s_nop 3", "v_max_f32_e32 v30, v1, v1"]
+    assert not scan(join)
