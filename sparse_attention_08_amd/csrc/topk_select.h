@@ -16,6 +16,8 @@ constexpr int kMaxSplitK = 2048;  // largest k on the split path
 constexpr int kMergeCap = kMaxChunks * kMaxSplitK;  // candidates merged in LDS
 constexpr int64_t kMaxSplitRows = 1024;
 constexpr int kMergeThreads = 1024;
+constexpr int kCandCap = 1024;   // boundary-bin keys refined on their own
+constexpr int kRankMax = 128;    // up to this many: refined by counting ranks
 
 template <int NT>
 struct SelectShared {
@@ -24,7 +26,10 @@ struct SelectShared {
   uint32_t tmp[2 * kNW];
   uint32_t seg_cnt[2 * kNW];
   uint32_t wsum[kNW];  // radix pass: wave totals of the bin counts
-  uint32_t pick[2];    // radix pass: the digit and the rank left
+  uint32_t pick[3];    // radix pass: the digit, the rank left, the digit's count
+  uint32_t ccount;     // boundary-bin keys gathered
+  alignas(16) uint32_t ckey[kCandCap + 4];  // the boundary bin's keys (4 zero keys after the last) ...
+  uint8_t cwave[kCandCap];      // ... and the wave whose segment each came from
 };
 
 // Keys of a row held in LDS, or read (and mapped) from the fp32 scores.
@@ -109,10 +114,19 @@ __device__ __forceinline__ void for_segment(const Keys& key, int s_lo, int s_hi,
 // in ascending order, p = its output slot in [0, min(K, n_sel)).  All NT threads
 // of the workgroup call it.
 //
-// The radix passes start at the highest bit in which the row's selectable keys
-// differ (the bits above are common to all of them), in digits of at most 11
-// bits: close scores then spread over the histogram instead of piling into a
-// few bins, and narrow ranges need fewer passes.
+// The radix passes run on key - kmin (kmin = the smallest selectable key; an
+// order-preserving shift) from the highest bit of kmax - kmin down, in digits of
+// at most 11 bits: the first digit then cuts the row's actual key range into
+// equal parts (close scores spread over the histogram instead of piling into a
+// few bins, also across a power of two), and narrow ranges need fewer passes.
+// After the first pass every key
+// outside the boundary digit is decided; when that digit holds at most kCandCap
+// keys they are gathered (with the wave whose segment they came from) in one
+// more pass over the keys, and the rest of the search runs on them alone: by
+// counting ranks for at most kRankMax of them, else by radix passes over the
+// gathered keys.  The same pass counts, per wave segment, the keys above the
+// boundary digit, so that the compaction needs no counting pass of its own.  A
+// larger boundary digit (many equal scores) takes the radix passes over all keys.
 template <int NT, class Keys, class Emit>
 __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_sel, int K,
                                             SelectShared<NT>& sh, Emit emit) {
@@ -121,10 +135,18 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const uint64_t lt = lanemask_lt();
+  // wave w owns the contiguous segment [s_lo, s_hi) in the compaction
+  const int seg = ((n + NW - 1) / NW + kWave - 1) & ~(kWave - 1);
+  const int s_lo = wave * seg;
+  const int s_hi = min(n, s_lo + seg);
 
   uint32_t thr = 0u, need_eq = 0u;
+  uint32_t gt = 0u, eq = 0u;  // this wave's segment: keys > thr, keys == thr
+  bool counted = false;
   if (n_sel > uint32_t(K)) {
     for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;  // ordered by block_min_max
+    if (tid == 0) sh.ccount = 0u;
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     for_keys<NT>(key, n, [&](int, uint32_t k) {
       if (k != 0u) {
@@ -133,24 +155,26 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
       }
     });
     block_min_max<NT>(kmin, kmax, sh.tmp);
-    const uint32_t diff = kmin ^ kmax;
-    int shift = diff == 0u ? 0 : 32 - __builtin_clz(diff);  // varying bits [0, shift)
+    // d = key - kmin for selectable keys: d in [0, range]
+    const uint32_t range = kmax - kmin;
+    int shift = range == 0u ? 0 : 32 - __builtin_clz(range);  // d has bits [0, shift)
     uint32_t pmask = shift >= 32 ? 0u : ~((1u << shift) - 1u);
-    uint32_t prefix = kmax & pmask;
+    uint32_t prefix = 0u;  // the digits of d picked so far (bits under pmask)
     uint32_t remaining = uint32_t(K);
-    // Each pass: histogram (barrier); every thread reads its bins into registers
-    // and clears them, wave prefix sums by DPP, wave totals (barrier); the thread
-    // whose bins hold the k-th key picks the digit (barrier).  The wave totals
-    // are read before the third barrier and written again only before the next
-    // pass's second; the pick is read after the third and written again only
-    // after the next pass's second.
-#pragma unroll 1
-    while (shift > 0) {
+    // One radix pass over keys(0..cnt-1): histogram (barrier); every thread
+    // reads its bins into registers and clears them, wave prefix sums by DPP,
+    // wave totals (barrier); the thread whose bins hold the k-th key picks the
+    // digit (barrier).  The wave totals are read before the third barrier and
+    // written again only before the next pass's second; the pick is read after
+    // the third and written again only after the next pass's second.  Returns
+    // the number of keys with the picked digit.
+    auto radix_pass = [&](const auto& keys, int cnt) -> uint32_t {
       const int nb = shift < 11 ? shift : 11;
       shift -= nb;
       const uint32_t dmask = (1u << nb) - 1u;
-      for_keys<NT>(key, n, [&](int, uint32_t k) {
-        if (k != 0u && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
+      for_keys<NT>(keys, cnt, [&](int, uint32_t k) {
+        const uint32_t d = k - kmin;
+        if (k != 0u && (d & pmask) == prefix) atomicAdd(&sh.hist[(d >> shift) & dmask], 1u);
       });
       __syncthreads();
       // thread j owns the bins of slot (NT-1-j), so an exclusive prefix over
@@ -178,6 +202,7 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
           if (c < remaining && c + h[j] >= remaining) {
             sh.pick[0] = uint32_t(base + j);
             sh.pick[1] = remaining - c;
+            sh.pick[2] = h[j];
           }
           c += h[j];
         }
@@ -186,20 +211,82 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
       prefix |= sh.pick[0] << shift;
       pmask |= dmask << shift;
       remaining = sh.pick[1];
+      return sh.pick[2];
+    };
+    const uint32_t in_bin = shift > 0 ? radix_pass(key, n) : 0u;
+    if (shift > 0 && in_bin <= uint32_t(kCandCap)) {
+      // gather the boundary digit's keys; count the keys above it per segment
+      const uint32_t bin_max = prefix | ~pmask;  // largest d with the boundary digit
+      for_segment(key, s_lo, s_hi, lane, [&](int i, uint32_t k) {
+        const uint32_t d = k - kmin;
+        gt += __popcll(__ballot(k != 0u && d > bin_max));
+        const bool take = k != 0u && (d & pmask) == prefix;
+        const uint64_t b = __ballot(take);
+        if (b != 0ull) {
+          uint32_t at = 0u;
+          if (lane == 0) at = atomicAdd(&sh.ccount, uint32_t(__popcll(b)));
+          at = uint32_t(__shfl(int(at), 0)) + uint32_t(__popcll(b & lt));
+          if (take) {
+            sh.ckey[at] = k;
+            sh.cwave[at] = uint8_t(wave);
+          }
+        }
+        (void)i;
+      });
+      if (tid < 4) sh.ckey[in_bin + tid] = 0u;  // zero keys after the last: never counted
+      __syncthreads();
+      const int m = int(in_bin);
+      if (m <= kRankMax) {
+        // the remaining-th largest gathered key, by counting: key c is it when
+        // #(keys > c) < remaining <= #(keys >= c)
+        if (tid < m) {
+          const uint32_t c = sh.ckey[tid];
+          uint32_t ngt = 0u, nge = 0u;
+          for (int j = 0; j < m; j += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(&sh.ckey[j]);
+            ngt += uint32_t(v.x > c) + uint32_t(v.y > c) + uint32_t(v.z > c) + uint32_t(v.w > c);
+            nge += uint32_t(v.x >= c) + uint32_t(v.y >= c) + uint32_t(v.z >= c) + uint32_t(v.w >= c);
+          }
+          if (ngt < remaining && remaining <= nge) {
+            sh.pick[0] = c;
+            sh.pick[1] = remaining - ngt;
+          }
+        }
+        __syncthreads();
+        thr = sh.pick[0];
+        need_eq = sh.pick[1];
+      } else {
+        const LdsKeys cand{sh.ckey};
+        while (shift > 0) radix_pass(cand, m);
+        thr = kmin + prefix;
+        need_eq = remaining;
+      }
+      // the gathered keys of this wave's segment: > thr and == thr (gt so far is
+      // the same in every lane: the keys above the boundary digit)
+      uint32_t cgt = 0u, ceq = 0u;
+      for (int j = lane; j < m; j += kWave) {
+        if (sh.cwave[j] == uint8_t(wave)) {
+          cgt += uint32_t(sh.ckey[j] > thr);
+          ceq += uint32_t(sh.ckey[j] == thr);
+        }
+      }
+      gt += wave_sum(cgt);
+      eq = wave_sum(ceq);
+      counted = true;
+    } else {
+      while (shift > 0) radix_pass(key, n);
+      thr = kmin + prefix;
+      need_eq = remaining;
     }
-    thr = prefix;
-    need_eq = remaining;
   }
 
   // ordered compaction
-  const int seg = ((n + NW - 1) / NW + kWave - 1) & ~(kWave - 1);
-  const int s_lo = wave * seg;
-  const int s_hi = min(n, s_lo + seg);
-  uint32_t gt = 0u, eq = 0u;
-  for_segment(key, s_lo, s_hi, lane, [&](int i, uint32_t k) {
-    gt += __popcll(__ballot(k > thr));
-    eq += __popcll(__ballot(i < s_hi && k == thr));
-  });
+  if (!counted) {
+    for_segment(key, s_lo, s_hi, lane, [&](int i, uint32_t k) {
+      gt += __popcll(__ballot(k > thr));
+      eq += __popcll(__ballot(i < s_hi && k == thr));
+    });
+  }
   if (lane == 0) {
     sh.seg_cnt[wave] = gt;
     sh.seg_cnt[NW + wave] = eq;
@@ -210,7 +297,6 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
     gt_before += sh.seg_cnt[w];
     eq_before += sh.seg_cnt[NW + w];
   }
-  const uint64_t lt = lanemask_lt();
   for_segment(key, s_lo, s_hi, lane, [&](int i, uint32_t k) {
     const bool is_gt = k > thr;
     const bool is_eq = i < s_hi && k == thr;
