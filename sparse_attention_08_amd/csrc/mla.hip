@@ -255,14 +255,35 @@ __device__ __forceinline__ void wait_tile(bool next_in_flight) {
   static_assert(kDmaPerWave == 9, "vmcnt immediate");
 }
 
+// V fragment m = 2n + ks (value tile n, key step ks) of the tile in buffer B (or
+// `buf` when B < 0): the B operand of the P.V MFMA (8 keys x 1 value column per
+// lane), read from the row-major tile with ds_read_b64_tr_b16: in each group of
+// 16 lanes, lane 4m'+q reads 4 value columns of key row k0+m' and the transpose
+// hands lane i the 4 keys k0..k0+3 of column n0+i.  Lane half h needs keys
+// {4h..4h+3} (first read) and {8+4h..8+4h+3} (second read) of each 16-key step:
+// the order in which P sits in the S^T accumulator.  Key (li >> 2) + 4 * half
+// (+ 8, + 16 per read and step) is in slot 4 * (li >> 2) + half (+ 2, + 16).
+template <int B>
+__device__ __forceinline__ bf16x8_t vfrag(const uint8_t* buf, int m, int lane) {
+  const int half = lane >> 5;
+  const int li = lane & 15;
+  const int n0 = 16 * ((lane >> 4) & 1);  // value column offset of the group inside a 32-wide tile
+  const uint8_t* base = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) +
+                        (4 * (li >> 2) + half) * kRowA + (n0 + 4 * (li & 3)) * 2 +
+                        16 * (m & 1) * kRowA + (m >> 1) * 64;
+  const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
+  const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 2 * kRowA));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // S^T = K . Q^T for the tile in buffer B: keys on M, the wave's 32 heads on N,
 // 36 K-steps of 16 dims.  Lane l reads key l%32, dims 16*st + 8*(l/32) .. +8;
 // the fragment reads run two steps ahead of their MFMA.  With kDma, the
 // LDS-DMA loads of a later tile (into buffer BD) are issued between the MFMAs
 // (the wave can issue them while the matrix core works).
-template <int B, int BD, bool kDma>
-__device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint32_t vmask,
-                                            int lane, const int* sidx, int lt_dma,
+template <int B, int BD, bool kDma, int BV>
+__device__ __forceinline__ f32x16_t qk_tile(bf16x8_t (&fr)[4], const bf16x8_t (&qf)[kQSteps],
+                                            uint32_t vmask, int lane, const int* sidx, int lt_dma,
                                             const uint8_t* __restrict__ kv, int wave) {
   const int kk = lane & 31;
   const int h = lane >> 5;
@@ -275,21 +296,24 @@ __device__ __forceinline__ f32x16_t qk_tile(const bf16x8_t (&qf)[kQSteps], uint3
   };
   DmaRows rows{};
   if constexpr (kDma) rows = dma_rows(sidx, lt_dma, lane);  // ahead of the ring reads
-  // fragment reads four steps ahead: one explicit wait per MFMA
-  bf16x8_t fr[4];
+  // fragment reads four steps ahead: one explicit wait per MFMA.  With BV >= 0
+  // the last four steps read V fragments 0..3 of buffer BV into the ring for
+  // the P.V that follows (two LDS reads each), so that it starts without a wait.
+  constexpr int kV = BV >= 0 ? 2 : 0;
 #pragma unroll
   for (int st = 0; st < 4; ++st) fr[st] = frag(st);
   f32x16_t s;
 #pragma unroll
   for (int st = 0; st < kQSteps; ++st) {
-    // reads of steps st+1 .. st+3 may stay in flight
+    // the reads of ring fragments st+1 .. st+3 may stay in flight
     if (st + 3 < kQSteps) wait_lgkm<3>();
-    else if (st + 2 < kQSteps) wait_lgkm<2>();
-    else if (st + 1 < kQSteps) wait_lgkm<1>();
-    else wait_lgkm<0>();
+    else if (st + 2 < kQSteps) wait_lgkm<2 + kV>();
+    else if (st + 1 < kQSteps) wait_lgkm<1 + 2 * kV>();
+    else wait_lgkm<3 * kV>();
     if (st == 0) mfma_v0(s, fr[0], qf[0]);
     else mfma_v(s, fr[st % 4], qf[st]);
     if (st + 4 < kQSteps) fr[st % 4] = frag(st + 4);
+    else if constexpr (BV >= 0) fr[st % 4] = vfrag<BV>(nullptr, st + 4 - kQSteps, lane);
     if constexpr (kDma) {
       // the gather of a later tile, spread between the MFMAs
       if (st % 4 == 1 && st / 4 < kKT / kWaves) dma_latent<BD>(rows, st / 4, kv, wave, lane);
@@ -417,41 +441,21 @@ __device__ __forceinline__ void softmax_all(Softmax& sm, float scale2, float& m_
 }
 
 // O += P . V for the tile in buffer B (B < 0: the buffer `buf` chosen at run
-// time).  The B operand (8 keys x 1 value column per lane) is read from the
-// row-major tile with ds_read_b64_tr_b16: in each group of 16 lanes, lane 4m+q
-// reads 4 value columns of key row k0+m and the transpose hands lane i the 4
-// keys k0..k0+3 of column n0+i.  Lane half h needs keys {4h..4h+3} (first read)
-// and {8+4h..8+4h+3} (second read) of each 16-key step: the order in which P
-// sits in the S^T accumulator.  With kSm, one softmax piece of the current tile
-// follows each MFMA from gap kSmFirstGap on.
-template <int B, bool kSm>
-__device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_t p1,
-                                        f32x16_t (&o)[kVTiles], int lane, Softmax& sm,
-                                        float scale2, float& m_ref, float& m_max, bool& over,
-                                        float& l_run) {
-  const int half = lane >> 5;
-  const int grp = lane >> 4;      // 16-lane group
-  const int li = lane & 15;
-  const int n0 = 16 * (grp & 1);  // value column offset of the group inside a 32-wide tile
-  // key (li >> 2) + 4 * half (+ 8, + 16 per read and step) is in slot
-  // 4 * (li >> 2) + half (+ 2, + 16)
-  const uint8_t* vb = (B >= 0 ? kvbuf<(B < 0 ? 0 : B)>() : buf) +
-                      (4 * (li >> 2) + half) * kRowA + (n0 + 4 * (li & 3)) * 2;
-  // step m = 2n + ks: value tile n, key step ks
-  auto rd = [&](int m) {
-    const uint8_t* base = vb + 16 * (m & 1) * kRowA + (m >> 1) * 64;
-    const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
-    const v4i16_t b =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 2 * kRowA));
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  // fragment reads four steps ahead (two LDS reads each): one explicit wait per MFMA
-  bf16x8_t fr[4];
+// time).  The B operand comes from vfrag; on entry the ring holds V fragments
+// 0..3 (kFill: read them first).  With kSm, one softmax piece of the current
+// tile follows each MFMA from gap kSmFirstGap on.
+template <int B, bool kSm, bool kFill>
+__device__ __forceinline__ void pv_tile(bf16x8_t (&fr)[4], const uint8_t* buf, bf16x8_t p0,
+                                        bf16x8_t p1, f32x16_t (&o)[kVTiles], int lane,
+                                        Softmax& sm, float scale2, float& m_ref, float& m_max,
+                                        bool& over, float& l_run) {
+  if constexpr (kFill) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) fr[m] = rd(m);
+    for (int m = 0; m < 4; ++m) fr[m] = vfrag<B>(buf, m, lane);
+  }
 #pragma unroll
   for (int m = 0; m < 2 * kVTiles; ++m) {
-    // reads of steps m+1 .. m+3 may stay in flight
+    // reads of steps m+1 .. m+3 may stay in flight (two per fragment)
     if (m + 3 < 2 * kVTiles) wait_lgkm<6>();
     else if (m + 2 < 2 * kVTiles) wait_lgkm<4>();
     else if (m + 1 < 2 * kVTiles) wait_lgkm<2>();
@@ -460,7 +464,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, bf16x8_t p0, bf16x8_
       mfma_a<true>(o[m >> 1], (m & 1) ? p1 : p0, fr[m % 4]);
     else
       mfma_a<false>(o[m >> 1], (m & 1) ? p1 : p0, fr[m % 4]);
-    if (m + 4 < 2 * kVTiles) fr[m % 4] = rd(m + 4);
+    if (m + 4 < 2 * kVTiles) fr[m % 4] = vfrag<B>(buf, m + 4, lane);
     if constexpr (kSm) {
       if (m >= kSmFirstGap && m - kSmFirstGap < kSmPieces)
         sm_piece(m - kSmFirstGap, sm, scale2, m_ref, m_max, over, l_run);
@@ -481,12 +485,14 @@ __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const ui
   wait_tile(i + 1 < nt);
   __builtin_amdgcn_s_barrier();
   Softmax sm;
+  bf16x8_t fr[4];  // the fragment ring, shared by the QK and the P.V that follows
   if (i + 2 < nt) {
-    sm.s = qk_tile<B, (B + 2) & 3, true>(qf, vm, lane, sh.idx, i + 2, kvb, wave);
+    sm.s = qk_tile<B, (B + 2) & 3, true, (B + 3) & 3>(fr, qf, vm, lane, sh.idx, i + 2, kvb, wave);
   } else {
-    sm.s = qk_tile<B, 0, false>(qf, vm, lane, sh.idx, 0, kvb, wave);
+    sm.s = qk_tile<B, 0, false, (B + 3) & 3>(fr, qf, vm, lane, sh.idx, 0, kvb, wave);
   }
-  pv_tile<(B + 3) & 3, true>(nullptr, p0, p1, o, lane, sm, scale2, m_ref, m_max, over, l_run);
+  pv_tile<(B + 3) & 3, true, false>(fr, nullptr, p0, p1, o, lane, sm, scale2, m_ref, m_max, over,
+                                    l_run);
   p0 = sm.p0();
   p1 = sm.p1();
   vm = sh.vmask[i + 1];  // the next tile's mask, read well before it is needed
@@ -600,7 +606,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       if (nt4 > 2) dma_tile<2>(sh.idx, 2, kvb, wave, lane);
       {
         Softmax sm;
-        sm.s = qk_tile<0, 0, false>(qf, sh.vmask[0], lane, sh.idx, 0, kvb, wave);
+        bf16x8_t fr[4];
+        sm.s = qk_tile<0, 0, false, -1>(fr, qf, sh.vmask[0], lane, sh.idx, 0, kvb, wave);
         softmax_all(sm, scale2, m_ref, m_max, over, l_run);
         p0 = sm.p0();
         p1 = sm.p1();
@@ -622,7 +629,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       const int lb = (nt4 - 1) & 3;
       const uint8_t* buf = lb == 0 ? g_kv0 : lb == 1 ? g_kv1 : lb == 2 ? g_kv2 : g_kv3;
       Softmax none;
-      pv_tile<-1, false>(buf, p0, p1, o, lane, none, scale2, m_ref, m_max, over, l_run);
+      bf16x8_t fr[4];
+      pv_tile<-1, false, true>(fr, buf, p0, p1, o, lane, none, scale2, m_ref, m_max, over, l_run);
     }
     o_fence(o);  // the last MFMAs into O finish before O is read or cleared
     // the whole workgroup agrees on a second pass (its waves share barriers)
