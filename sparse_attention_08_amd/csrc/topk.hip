@@ -206,15 +206,21 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
 // Many rows over more than 8192 columns (k <= 2048): a row is streamed through
 // LDS in pieces of kPiece keys.  The keys that can still be in the top-k are
 // held in LDS with their columns, in column order; a new key enters only if it
-// is above the floor (the k-th key of everything seen at the last shrink: a key
-// not above it can no longer be selected, as on a tie the older, lower column
-// wins).  When a piece's survivors do not fit, the held keys are first shrunk
-// to their top k and the floor raised.  The scores are read once.
+// is above the floor (a key not above it has at least k keys above it, or is
+// the k-th key of everything seen with an older, lower-column tie).  When a
+// piece's survivors do not fit, the floor is raised and the held keys are
+// compacted: one histogram pass over them (the first digit of the exact
+// search) finds the digit that holds their k-th key, every key below that digit
+// goes, and when that leaves room for a piece the held keys above the floor are
+// compacted in place; otherwise (a crowded digit: many equal keys) they are
+// shrunk to their exact top k.  The scores are read once.
 constexpr int kPiece = 4096;
+constexpr int kSlack = 128;  // held keys past k that the histogram shrink may keep
+constexpr int kHeldCap = kMaxSplitK + kPiece + kSlack;
 
 struct StreamShared {
-  uint32_t keys[kMaxSplitK + kPiece];
-  int32_t cols[kMaxSplitK + kPiece];
+  uint32_t keys[kHeldCap];
+  int32_t cols[kHeldCap];
   uint32_t tkey[kMaxSplitK];
   int32_t tcol[kMaxSplitK];
   uint32_t wcnt[kWaves];
@@ -250,6 +256,42 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
       f[j] = i < m ? src[lo + i] : -INFINITY;
     }
   };
+  // In-place ordered compaction of the held keys above f: every wave reads its
+  // segment into registers and counts (barrier), then writes its kept keys at
+  // their new positions (barrier); all reads precede all writes.
+  auto compact_held = [&](uint32_t f, int cnt) {
+    constexpr int kHeldPer = (kHeldCap + kThreads - 1) / kThreads;
+    const int seg = ((cnt + kWaves - 1) / kWaves + kWave - 1) & ~(kWave - 1);
+    const int s_lo = wave * seg;
+    const int s_hi = min(cnt, s_lo + seg);
+    uint32_t hk[kHeldPer];
+    int32_t hc[kHeldPer];
+    uint32_t c = 0u;
+#pragma unroll
+    for (int j = 0; j < kHeldPer; ++j) {
+      const int i = s_lo + j * kWave + lane;
+      hk[j] = i < s_hi ? sh.keys[i] : 0u;
+      hc[j] = i < s_hi ? sh.cols[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kHeldPer; ++j) c += __popcll(__ballot(hk[j] > f));
+    if (lane == 0) sh.wcnt[wave] = c;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += int(sh.wcnt[w]);
+#pragma unroll
+    for (int j = 0; j < kHeldPer; ++j) {
+      const bool keep = hk[j] > f;
+      const uint64_t bal = __ballot(keep);
+      if (keep) {
+        const int at = base + __popcll(bal & lt);
+        sh.keys[at] = hk[j];
+        sh.cols[at] = hc[j];
+      }
+      base += __popcll(bal);
+    }
+    __syncthreads();
+  };
   float fnext[kPer];
   load_piece(0, fnext);
   for (int lo = 0;; lo += kPiece) {
@@ -269,8 +311,30 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
       return tot;
     };
     int s_all = survivors();
-    if (ncand + s_all > kMaxSplitK + kPiece) {
-      // no room: shrink the held keys to their top k and raise the floor
+    if (ncand + s_all > kHeldCap) {
+      // no room: raise the floor from the first digit of the held keys' k-th key
+      bool shrunk = false;
+      {
+        RadixSearch<kThreads> rs{sh.sel};
+        rs.init(LdsKeys{sh.keys}, ncand, K);
+        if (rs.shift > 0) {
+          const uint32_t in_bin = rs.pass(LdsKeys{sh.keys}, ncand);
+          // keys whose d has the picked digit or a higher one: at least k
+          const uint32_t keep = uint32_t(K) - rs.remaining + in_bin;
+          if (keep <= uint32_t(kMaxSplitK + kSlack)) {
+            // every key <= f is below all of those keys
+            const uint32_t f = rs.kmin + rs.prefix - 1u;
+            compact_held(f, ncand);
+            ncand = int(keep);
+            floor_key = f;
+            shrunk = true;
+          }
+        }
+      }
+      if (shrunk) {
+        s_all = survivors();
+      } else {
+      // a crowded digit: shrink the held keys to their exact top k
       select_topk<kThreads>(LdsKeys{sh.keys}, ncand, uint32_t(ncand), K, sh.sel,
                             [&](uint32_t p, int i, uint32_t key) {
                               sh.tkey[p] = key;
@@ -288,6 +352,7 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
       ncand = K;
       floor_key = kmin;  // the k-th key of everything seen so far
       s_all = survivors();
+      }
     }
     // ordered compaction of the survivors behind the held keys
     int base = ncand;

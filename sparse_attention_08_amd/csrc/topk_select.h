@@ -109,6 +109,103 @@ __device__ __forceinline__ void for_segment(const Keys& key, int s_lo, int s_hi,
   }
 }
 
+// Radix search for the k-th largest selectable key.  init() takes the min and
+// max of the selectable keys (and clears the histogram, ordered by its
+// barriers); the digits are then taken from d = key - kmin over the bits of
+// kmax - kmin, most significant first, at most 11 at a time.  After each pass()
+// `prefix` holds the digits of d picked so far (the bits under pmask), the
+// k-th largest key lies among the keys whose d has that prefix, and it is the
+// `remaining`-th largest of them.
+template <int NT>
+struct RadixSearch {
+  SelectShared<NT>& sh;
+  uint32_t kmin = 0u;
+  int shift = 0;        // d's bits below the digits picked so far
+  uint32_t pmask = 0u;
+  uint32_t prefix = 0u;
+  uint32_t remaining = 0u;
+
+  template <class Keys>
+  __device__ __forceinline__ void init(const Keys& key, int n, int K) {
+    for (int i = int(threadIdx.x); i < kBins; i += NT) sh.hist[i] = 0u;  // ordered by block_min_max
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for_keys<NT>(key, n, [&](int, uint32_t k) {
+      if (k != 0u) {
+        lo = min(lo, k);
+        hi = max(hi, k);
+      }
+    });
+    block_min_max<NT>(lo, hi, sh.tmp);
+    kmin = lo;
+    const uint32_t range = hi - lo;  // d in [0, range]
+    shift = range == 0u ? 0 : 32 - __builtin_clz(range);
+    pmask = shift >= 32 ? 0u : ~((1u << shift) - 1u);
+    prefix = 0u;
+    remaining = uint32_t(K);
+  }
+
+  // One radix pass over keys(0..cnt-1): histogram (barrier); every thread reads
+  // its bins into registers and clears them, wave prefix sums by DPP, wave
+  // totals (barrier); the thread whose bins hold the k-th key picks the digit
+  // (barrier).  The wave totals are read before the third barrier and written
+  // again only before the next pass's second; the pick is read after the third
+  // and written again only after the next pass's second.  Returns the number of
+  // keys with the picked digit.
+  template <class Keys>
+  __device__ __forceinline__ uint32_t pass(const Keys& keys, int cnt) {
+    constexpr int NW = NT / kWave;
+    constexpr int kBPT = kBins / NT;  // histogram bins owned per thread in the scan
+    const int tid = int(threadIdx.x);
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int nb = shift < 11 ? shift : 11;
+    shift -= nb;
+    const uint32_t dmask = (1u << nb) - 1u;
+    const uint32_t km = kmin, pm = pmask, pf = prefix;
+    const int sh_ = shift;
+    for_keys<NT>(keys, cnt, [&](int, uint32_t k) {
+      const uint32_t d = k - km;
+      if (k != 0u && (d & pm) == pf) atomicAdd(&sh.hist[(d >> sh_) & dmask], 1u);
+    });
+    __syncthreads();
+    // thread j owns the bins of slot (NT-1-j), so an exclusive prefix over
+    // threads is the count of keys in higher bins
+    const int base = (NT - 1 - tid) * kBPT;
+    uint32_t h[kBPT];
+    uint32_t local = 0u;
+#pragma unroll
+    for (int j = 0; j < kBPT; ++j) {
+      h[j] = sh.hist[base + j];
+      local += h[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kBPT; ++j) sh.hist[base + j] = 0u;  // for the next pass
+    const uint32_t incl = wave_inclusive_sum(local);
+    if (lane == kWave - 1) sh.wsum[wave] = incl;
+    __syncthreads();
+    uint32_t above = incl - local;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) above += w < wave ? sh.wsum[w] : 0u;
+    if (above < remaining && above + local >= remaining) {
+      uint32_t c = above;
+#pragma unroll
+      for (int j = kBPT - 1; j >= 0; --j) {
+        if (c < remaining && c + h[j] >= remaining) {
+          sh.pick[0] = uint32_t(base + j);
+          sh.pick[1] = remaining - c;
+          sh.pick[2] = h[j];
+        }
+        c += h[j];
+      }
+    }
+    __syncthreads();
+    prefix |= sh.pick[0] << shift;
+    pmask |= dmask << shift;
+    remaining = sh.pick[1];
+    return sh.pick[2];
+  }
+};
+
 // Select the K largest of the n keys key(0..n-1) (n_sel of them are nonzero),
 // ties to the lowest index, and call emit(p, i, key) for each selected index i
 // in ascending order, p = its output slot in [0, min(K, n_sel)).  All NT threads
@@ -131,7 +228,6 @@ template <int NT, class Keys, class Emit>
 __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_sel, int K,
                                             SelectShared<NT>& sh, Emit emit) {
   constexpr int NW = NT / kWave;
-  constexpr int kBPT = kBins / NT;  // histogram bins owned per thread in the scan
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -145,78 +241,14 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
   uint32_t gt = 0u, eq = 0u;  // this wave's segment: keys > thr, keys == thr
   bool counted = false;
   if (n_sel > uint32_t(K)) {
-    for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;  // ordered by block_min_max
-    if (tid == 0) sh.ccount = 0u;
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for_keys<NT>(key, n, [&](int, uint32_t k) {
-      if (k != 0u) {
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
-      }
-    });
-    block_min_max<NT>(kmin, kmax, sh.tmp);
-    // d = key - kmin for selectable keys: d in [0, range]
-    const uint32_t range = kmax - kmin;
-    int shift = range == 0u ? 0 : 32 - __builtin_clz(range);  // d has bits [0, shift)
-    uint32_t pmask = shift >= 32 ? 0u : ~((1u << shift) - 1u);
-    uint32_t prefix = 0u;  // the digits of d picked so far (bits under pmask)
-    uint32_t remaining = uint32_t(K);
-    // One radix pass over keys(0..cnt-1): histogram (barrier); every thread
-    // reads its bins into registers and clears them, wave prefix sums by DPP,
-    // wave totals (barrier); the thread whose bins hold the k-th key picks the
-    // digit (barrier).  The wave totals are read before the third barrier and
-    // written again only before the next pass's second; the pick is read after
-    // the third and written again only after the next pass's second.  Returns
-    // the number of keys with the picked digit.
-    auto radix_pass = [&](const auto& keys, int cnt) -> uint32_t {
-      const int nb = shift < 11 ? shift : 11;
-      shift -= nb;
-      const uint32_t dmask = (1u << nb) - 1u;
-      for_keys<NT>(keys, cnt, [&](int, uint32_t k) {
-        const uint32_t d = k - kmin;
-        if (k != 0u && (d & pmask) == prefix) atomicAdd(&sh.hist[(d >> shift) & dmask], 1u);
-      });
-      __syncthreads();
-      // thread j owns the bins of slot (NT-1-j), so an exclusive prefix over
-      // threads is the count of keys in higher bins
-      const int base = (NT - 1 - tid) * kBPT;
-      uint32_t h[kBPT];
-      uint32_t local = 0u;
-#pragma unroll
-      for (int j = 0; j < kBPT; ++j) {
-        h[j] = sh.hist[base + j];
-        local += h[j];
-      }
-#pragma unroll
-      for (int j = 0; j < kBPT; ++j) sh.hist[base + j] = 0u;  // for the next pass
-      const uint32_t incl = wave_inclusive_sum(local);
-      if (lane == kWave - 1) sh.wsum[wave] = incl;
-      __syncthreads();
-      uint32_t above = incl - local;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) above += w < wave ? sh.wsum[w] : 0u;
-      if (above < remaining && above + local >= remaining) {
-        uint32_t c = above;
-#pragma unroll
-        for (int j = kBPT - 1; j >= 0; --j) {
-          if (c < remaining && c + h[j] >= remaining) {
-            sh.pick[0] = uint32_t(base + j);
-            sh.pick[1] = remaining - c;
-            sh.pick[2] = h[j];
-          }
-          c += h[j];
-        }
-      }
-      __syncthreads();
-      prefix |= sh.pick[0] << shift;
-      pmask |= dmask << shift;
-      remaining = sh.pick[1];
-      return sh.pick[2];
-    };
-    const uint32_t in_bin = shift > 0 ? radix_pass(key, n) : 0u;
-    if (shift > 0 && in_bin <= uint32_t(kCandCap)) {
+    if (tid == 0) sh.ccount = 0u;  // ordered by the barriers of init
+    RadixSearch<NT> rs{sh};
+    rs.init(key, n, K);
+    const uint32_t in_bin = rs.shift > 0 ? rs.pass(key, n) : 0u;
+    if (rs.shift > 0 && in_bin <= uint32_t(kCandCap)) {
       // gather the boundary digit's keys; count the keys above it per segment
-      const uint32_t bin_max = prefix | ~pmask;  // largest d with the boundary digit
+      const uint32_t bin_max = rs.prefix | ~rs.pmask;  // largest d with the boundary digit
+      const uint32_t kmin = rs.kmin, pmask = rs.pmask, prefix = rs.prefix;
       for_segment(key, s_lo, s_hi, lane, [&](int i, uint32_t k) {
         const uint32_t d = k - kmin;
         gt += __popcll(__ballot(k != 0u && d > bin_max));
@@ -247,9 +279,9 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
             ngt += uint32_t(v.x > c) + uint32_t(v.y > c) + uint32_t(v.z > c) + uint32_t(v.w > c);
             nge += uint32_t(v.x >= c) + uint32_t(v.y >= c) + uint32_t(v.z >= c) + uint32_t(v.w >= c);
           }
-          if (ngt < remaining && remaining <= nge) {
+          if (ngt < rs.remaining && rs.remaining <= nge) {
             sh.pick[0] = c;
-            sh.pick[1] = remaining - ngt;
+            sh.pick[1] = rs.remaining - ngt;
           }
         }
         __syncthreads();
@@ -257,9 +289,9 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
         need_eq = sh.pick[1];
       } else {
         const LdsKeys cand{sh.ckey};
-        while (shift > 0) radix_pass(cand, m);
-        thr = kmin + prefix;
-        need_eq = remaining;
+        while (rs.shift > 0) rs.pass(cand, m);
+        thr = rs.kmin + rs.prefix;
+        need_eq = rs.remaining;
       }
       // the gathered keys of this wave's segment: > thr and == thr (gt so far is
       // the same in every lane: the keys above the boundary digit)
@@ -274,9 +306,9 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
       eq = wave_sum(ceq);
       counted = true;
     } else {
-      while (shift > 0) radix_pass(key, n);
-      thr = kmin + prefix;
-      need_eq = remaining;
+      while (rs.shift > 0) rs.pass(key, n);
+      thr = rs.kmin + rs.prefix;
+      need_eq = rs.remaining;
     }
   }
 

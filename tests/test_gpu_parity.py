@@ -168,6 +168,23 @@ def test_topk_many_long_rows_stream_path(dsa):
         _topk_case(dsa, S, rs, re, K, f"stream K={K}")
 
 
+def test_topk_many_long_rows_stream_shrinks(dsa):
+    # windows of up to 40000 keys: the held keys are shrunk several times per
+    # row, by the histogram floor and (on the rows of tied values) by the exact
+    # select
+    g = np.random.default_rng(106)
+    n_q, n = 1030, 40000
+    S = g.standard_normal((n_q, n)).astype(np.float32)
+    S[::3] = np.round(S[::3] * 4) / 4                       # crowded digits: many equal keys
+    S[1::5, ::7] = -np.inf                                  # unselectable keys
+    S[2::6] = np.linspace(-1.0, 3.0, n, dtype=np.float32)   # rising scores: a shrink per piece
+    rs = g.integers(0, 2000, n_q).astype(np.int32)
+    re = np.minimum(n, rs + g.integers(9000, 40000, n_q)).astype(np.int32)
+    assert dsa._lib_or_load().dsa_topk_workspace_size(n_q, n, 2048) == 0
+    for K in (2048, 100):
+        _topk_case(dsa, S, rs, re, K, f"stream shrinks K={K}")
+
+
 def test_topk_many_rows_large_k_global_path(dsa):
     # k above 2048 over long windows: one workgroup per row re-reads from memory
     g = np.random.default_rng(106)
