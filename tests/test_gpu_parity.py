@@ -168,6 +168,52 @@ def test_topk_many_long_rows_stream_path(dsa):
         _topk_case(dsa, S, rs, re, K, f"stream K={K}")
 
 
+def _select_path_rows(n, g):
+    # rows built so that the k-th score falls, for k = 2048, into:
+    #   0: a spread row (the boundary digit holds a few keys: ranks counted)
+    #   1: a cluster of ~1000 keys inside one first digit (radix passes over the
+    #      gathered keys)
+    #   2: 2000 equal keys across the boundary (radix passes over all keys)
+    #   3: equal keys only; 4: fewer selectable keys than k
+    rows = np.empty((5, n), np.float32)
+    rows[0] = g.uniform(0.0, 100.0, n)
+    rows[1] = g.uniform(0.0, 100.0, n)
+    top = rows[1] > 60.0
+    rows[1][~top] = g.uniform(0.0, 50.0, int((~top).sum()))
+    cl = g.choice(np.nonzero(~top)[0], 1000, replace=False)
+    rows[1][cl] = 50.0 + g.uniform(0.0, 0.01, 1000).astype(np.float32)
+    rows[2] = g.uniform(0.0, 100.0, n)
+    rows[2][g.choice(n, 2000, replace=False)] = 70.0
+    rows[3] = 3.25
+    rows[4] = -np.inf
+    rows[4][g.choice(n, 1500, replace=False)] = g.standard_normal(1500)
+    return rows
+
+
+def test_topk_select_paths(dsa):
+    g = np.random.default_rng(107)
+    n = 4096
+    S = np.tile(_select_path_rows(n, g), (3, 1))
+    n_q = S.shape[0]
+    rs = np.zeros(n_q, np.int32)
+    re = np.full(n_q, n, np.int32)
+    for K in (2048, 1500):
+        _topk_case(dsa, S, rs, re, K, f"select paths K={K}")
+
+
+def test_topk_select_paths_stream_shrinks(dsa):
+    # the same kinds of rows, 20480 keys wide, over > 1024 rows: the stream
+    # kernel's shrinks see each kind of boundary digit
+    g = np.random.default_rng(108)
+    n = 20480
+    base = _select_path_rows(n, g)
+    S = np.repeat(base, 206, axis=0)[:1030]
+    rs = np.zeros(S.shape[0], np.int32)
+    re = np.full(S.shape[0], n, np.int32)
+    assert dsa._lib_or_load().dsa_topk_workspace_size(S.shape[0], n, 2048) == 0
+    _topk_case(dsa, S, rs, re, 2048, "select paths, stream")
+
+
 def test_topk_many_long_rows_stream_shrinks(dsa):
     # windows of up to 40000 keys: the held keys are shrunk several times per
     # row, by the histogram floor and (on the rows of tied values) by the exact
