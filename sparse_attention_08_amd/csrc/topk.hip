@@ -39,13 +39,14 @@ namespace {
 
 using namespace topksel;
 
-// Keys of scores[a .. a+n) into LDS (n <= kCap); returns the selectable count.
-// Every thread issues a batch of loads (kCap / 2 / kThreads of them) before it
+// Keys of scores[a .. a+n) into LDS (n <= CAP); returns the selectable count.
+// Every thread issues a batch of loads (CAP / 2 / kThreads of them) before it
 // waits for any: a load-then-store loop would wait a full memory round trip
 // per element.
+template <int CAP>
 __device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t* keys,
                                               SelectShared<kThreads>& sh) {
-  constexpr int kPer = kCap / 2 / kThreads;
+  constexpr int kPer = CAP / 2 / kThreads;
   uint32_t cnt = 0;
   for (int base = 0; base < n; base += kPer * kThreads) {
     float v[kPer];
@@ -68,6 +69,8 @@ __device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t*
 }
 
 // Whole row by one workgroup; writes topk_idx[row] including the -1 padding.
+// Windows of at most CAP keys are held in LDS.
+template <int CAP>
 __device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64_t ld,
                                          int64_t row, int a, int b, int32_t K,
                                          int32_t* __restrict__ out, uint32_t* keys,
@@ -77,8 +80,8 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64
   int32_t* dst = out + row * int64_t(K);
   uint32_t n_sel;
   auto emit = [&](uint32_t p, int i, uint32_t) { dst[p] = a + i; };
-  if (n <= kCap) {
-    n_sel = load_keys(src, n, keys, sh);
+  if (n <= CAP) {
+    n_sel = load_keys<CAP>(src, n, keys, sh);
     select_topk<kThreads>(LdsKeys{keys}, n, n_sel, K, sh, emit);
   } else {
     uint32_t cnt = 0;
@@ -90,17 +93,21 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64
   for (uint32_t p = k_eff + threadIdx.x; p < uint32_t(K); p += kThreads) dst[p] = -1;
 }
 
-// skip_long: rows whose window exceeds kCap are left to the stream kernel
+// skip_long: rows whose window exceeds CAP are left to the stream kernel.
+// CAP = 4096 for score matrices of at most 4096 columns: a smaller LDS
+// footprint (29 KB instead of 46 KB) fits five workgroups per CU instead of
+// three, which hides more of each row's load latency.
+template <int CAP>
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
     const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out, int skip_long) {
-  __shared__ uint32_t keys[kCap];
+  __shared__ uint32_t keys[CAP];
   __shared__ SelectShared<kThreads> sh;
   const int64_t row = blockIdx.x;
   const int a = row_starts[row];
   const int b = row_ends[row];
-  if (skip_long && b - a > kCap) return;
-  row_topk(scores, ld, row, a, b, K, out, keys, sh);
+  if (skip_long && b - a > CAP) return;
+  row_topk<CAP>(scores, ld, row, a, b, K, out, keys, sh);
 }
 
 // Split path, phase 1: workgroup (row, c) selects the top-k of chunk c.
@@ -118,13 +125,13 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   const int n = b > a ? b - a : 0;
   const int clen = split_chunk_len(n);
   if (clen == 0) {
-    if (c == 0) row_topk(scores, ld, row, a, b, K, out, keys, sh);
+    if (c == 0) row_topk<kCap>(scores, ld, row, a, b, K, out, keys, sh);
     return;
   }
   const int64_t slot = row * kMaxChunks + c;
   const int lo = c * clen;
   const int m = lo < n ? min(clen, n - lo) : 0;
-  const uint32_t n_sel = load_keys(scores + row * ld + a + lo, m, keys, sh);
+  const uint32_t n_sel = load_keys<kCap>(scores + row * ld + a + lo, m, keys, sh);
   uint32_t* ck = cand_key + slot * K;
   int32_t* cc = cand_col + slot * K;
   select_topk<kThreads>(LdsKeys{keys}, m, n_sel, K, sh, [&](uint32_t p, int i, uint32_t k) {
@@ -398,8 +405,12 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
     // windows of at most kCap keys: held whole in LDS by the rows kernel; longer
     // ones (only possible when n_cols > kCap) streamed by the stream kernel
     const bool stream_long = n_cols > kCap && K <= kMaxSplitK;
-    hipLaunchKernelGGL(topk_rows_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
-                       ld, row_starts, row_ends, K, out, int(stream_long));
+    if (n_cols <= 4096)
+      hipLaunchKernelGGL(topk_rows_kernel<4096>, dim3(unsigned(n_q)), dim3(kThreads), 0, stream,
+                         scores, ld, row_starts, row_ends, K, out, 0);
+    else
+      hipLaunchKernelGGL(topk_rows_kernel<kCap>, dim3(unsigned(n_q)), dim3(kThreads), 0, stream,
+                         scores, ld, row_starts, row_ends, K, out, int(stream_long));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !stream_long) return e;
     hipLaunchKernelGGL(topk_stream_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
