@@ -93,20 +93,22 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64
   for (uint32_t p = k_eff + threadIdx.x; p < uint32_t(K); p += kThreads) dst[p] = -1;
 }
 
-// skip_long: rows whose window exceeds CAP are left to the stream kernel.
-// CAP = 4096 for score matrices of at most 4096 columns: a smaller LDS
-// footprint (29 KB instead of 46 KB) fits five workgroups per CU instead of
-// three, which hides more of each row's load latency.
+// Rows whose window is longer than CAP (skip_long) or at most `skip_below`
+// keys are left to another launch.  CAP = 4096 takes 29.8 KB of LDS instead of
+// 46.2 KB: five workgroups per CU instead of three, which hides more of each
+// row's load latency, so windows of at most 4096 keys go to that instance.
 template <int CAP>
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
-    const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out, int skip_long) {
+    const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out, int skip_long,
+    int skip_below) {
   __shared__ uint32_t keys[CAP];
   __shared__ SelectShared<kThreads> sh;
   const int64_t row = blockIdx.x;
   const int a = row_starts[row];
   const int b = row_ends[row];
-  if (skip_long && b - a > CAP) return;
+  const int n = b > a ? b - a : 0;
+  if ((skip_long && n > CAP) || n <= skip_below) return;
   row_topk<CAP>(scores, ld, row, a, b, K, out, keys, sh);
 }
 
@@ -405,13 +407,17 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
     // windows of at most kCap keys: held whole in LDS by the rows kernel; longer
     // ones (only possible when n_cols > kCap) streamed by the stream kernel
     const bool stream_long = n_cols > kCap && K <= kMaxSplitK;
-    if (n_cols <= 4096)
-      hipLaunchKernelGGL(topk_rows_kernel<4096>, dim3(unsigned(n_q)), dim3(kThreads), 0, stream,
-                         scores, ld, row_starts, row_ends, K, out, 0);
-    else
-      hipLaunchKernelGGL(topk_rows_kernel<kCap>, dim3(unsigned(n_q)), dim3(kThreads), 0, stream,
-                         scores, ld, row_starts, row_ends, K, out, int(stream_long));
+    // windows of at most 4096 keys: the 4096-key instance; longer ones up to
+    // kCap (and, without the stream kernel, all longer ones): the kCap instance
+    hipLaunchKernelGGL(topk_rows_kernel<4096>, dim3(unsigned(n_q)), dim3(kThreads), 0, stream,
+                       scores, ld, row_starts, row_ends, K, out, 1, -1);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (n_cols > 4096) {
+      hipLaunchKernelGGL(topk_rows_kernel<kCap>, dim3(unsigned(n_q)), dim3(kThreads), 0, stream,
+                         scores, ld, row_starts, row_ends, K, out, int(stream_long), 4096);
+      e = hipGetLastError();
+    }
     if (e != hipSuccess || !stream_long) return e;
     hipLaunchKernelGGL(topk_stream_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
                        ld, row_starts, row_ends, K, out);
