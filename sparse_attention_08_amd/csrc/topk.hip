@@ -222,17 +222,16 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
 // search) finds the digit that holds their k-th key, every key below that digit
 // goes, and when that leaves room for a piece the held keys above the floor are
 // compacted in place; otherwise (a crowded digit: many equal keys) they are
-// shrunk to their exact top k.  The scores are read once.
-constexpr int kPiece = 4096;
+// shrunk in place to their exact top k.  The scores are read once.  47 KB of
+// LDS: three workgroups per CU.
+constexpr int kPiece = 2048;
 constexpr int kSlack = 128;  // held keys past k that the histogram shrink may keep
 constexpr int kHeldCap = kMaxSplitK + kPiece + kSlack;
 
 struct StreamShared {
   uint32_t keys[kHeldCap];
   int32_t cols[kHeldCap];
-  uint32_t tkey[kMaxSplitK];
-  int32_t tcol[kMaxSplitK];
-  uint32_t wcnt[kWaves];
+  uint32_t wcnt[2 * kWaves];
   SelectShared<kThreads> sel;
 };
 
@@ -265,17 +264,17 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
       f[j] = i < m ? src[lo + i] : -INFINITY;
     }
   };
-  // In-place ordered compaction of the held keys above f: every wave reads its
+  // In-place ordered compaction of the held keys: those > thr and the first
+  // need_eq of those == thr (in column order) stay.  Every wave reads its
   // segment into registers and counts (barrier), then writes its kept keys at
   // their new positions (barrier); all reads precede all writes.
-  auto compact_held = [&](uint32_t f, int cnt) {
+  auto compact_held = [&](uint32_t thr, uint32_t need_eq, int cnt) {
     constexpr int kHeldPer = (kHeldCap + kThreads - 1) / kThreads;
-    const int seg = ((cnt + kWaves - 1) / kWaves + kWave - 1) & ~(kWave - 1);
-    const int s_lo = wave * seg;
-    const int s_hi = min(cnt, s_lo + seg);
+    int s_lo, s_hi;
+    select_segment<kThreads>(cnt, s_lo, s_hi);
     uint32_t hk[kHeldPer];
     int32_t hc[kHeldPer];
-    uint32_t c = 0u;
+    uint32_t gt = 0u, eq = 0u;
 #pragma unroll
     for (int j = 0; j < kHeldPer; ++j) {
       const int i = s_lo + j * kWave + lane;
@@ -283,21 +282,34 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
       hc[j] = i < s_hi ? sh.cols[i] : 0;
     }
 #pragma unroll
-    for (int j = 0; j < kHeldPer; ++j) c += __popcll(__ballot(hk[j] > f));
-    if (lane == 0) sh.wcnt[wave] = c;
+    for (int j = 0; j < kHeldPer; ++j) {
+      gt += __popcll(__ballot(hk[j] > thr));
+      eq += __popcll(__ballot(hk[j] == thr && s_lo + j * kWave + lane < s_hi));
+    }
+    if (lane == 0) {
+      sh.wcnt[wave] = gt;
+      sh.wcnt[kWaves + wave] = eq;
+    }
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += int(sh.wcnt[w]);
+    uint32_t gt_before = 0u, eq_before = 0u;
+    for (int w = 0; w < wave; ++w) {
+      gt_before += sh.wcnt[w];
+      eq_before += sh.wcnt[kWaves + w];
+    }
 #pragma unroll
     for (int j = 0; j < kHeldPer; ++j) {
-      const bool keep = hk[j] > f;
-      const uint64_t bal = __ballot(keep);
-      if (keep) {
-        const int at = base + __popcll(bal & lt);
+      const bool is_gt = hk[j] > thr;
+      const bool is_eq = hk[j] == thr && s_lo + j * kWave + lane < s_hi;
+      const uint64_t mgt = __ballot(is_gt);
+      const uint64_t meq = __ballot(is_eq);
+      const uint32_t eq_rank = eq_before + uint32_t(__popcll(meq & lt));
+      if (is_gt || (is_eq && eq_rank < need_eq)) {
+        const uint32_t at = gt_before + uint32_t(__popcll(mgt & lt)) + min(eq_rank, need_eq);
         sh.keys[at] = hk[j];
         sh.cols[at] = hc[j];
       }
-      base += __popcll(bal);
+      gt_before += uint32_t(__popcll(mgt));
+      eq_before += uint32_t(__popcll(meq));
     }
     __syncthreads();
   };
@@ -333,35 +345,22 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
           if (keep <= uint32_t(kMaxSplitK + kSlack)) {
             // every key <= f is below all of those keys
             const uint32_t f = rs.kmin + rs.prefix - 1u;
-            compact_held(f, ncand);
+            compact_held(f, 0u, ncand);
             ncand = int(keep);
             floor_key = f;
             shrunk = true;
           }
         }
       }
-      if (shrunk) {
-        s_all = survivors();
-      } else {
-      // a crowded digit: shrink the held keys to their exact top k
-      select_topk<kThreads>(LdsKeys{sh.keys}, ncand, uint32_t(ncand), K, sh.sel,
-                            [&](uint32_t p, int i, uint32_t key) {
-                              sh.tkey[p] = key;
-                              sh.tcol[p] = sh.cols[i];
-                            });
-      __syncthreads();
-      uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-      for (int p = tid; p < K; p += kThreads) {
-        sh.keys[p] = sh.tkey[p];
-        sh.cols[p] = sh.tcol[p];
-        kmin = min(kmin, sh.tkey[p]);
-        kmax = max(kmax, sh.tkey[p]);
+      if (!shrunk) {
+        // a crowded digit: shrink the held keys in place to their exact top k
+        const SelectThreshold r =
+            select_search<kThreads>(LdsKeys{sh.keys}, ncand, uint32_t(ncand), K, sh.sel);
+        compact_held(r.thr, r.need_eq, ncand);
+        ncand = K;
+        floor_key = r.thr;  // the k-th key of everything seen so far
       }
-      block_min_max<kThreads>(kmin, kmax, sh.sel.tmp);  // also orders the copies
-      ncand = K;
-      floor_key = kmin;  // the k-th key of everything seen so far
       s_all = survivors();
-      }
     }
     // ordered compaction of the survivors behind the held keys
     int base = ncand;

@@ -224,18 +224,34 @@ struct RadixSearch {
 // gathered keys.  The same pass counts, per wave segment, the keys above the
 // boundary digit, so that the compaction needs no counting pass of its own.  A
 // larger boundary digit (many equal scores) takes the radix passes over all keys.
-template <int NT, class Keys, class Emit>
-__device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_sel, int K,
-                                            SelectShared<NT>& sh, Emit emit) {
+// The selection as a threshold: the k-th largest key `thr` and how many of the
+// keys equal to it (the lowest-indexed ones) are selected; with n_sel <= K,
+// thr = 0 and need_eq = 0 (every selectable key).  When `counted`, gt and eq
+// are the counts of keys > thr and == thr in this wave's compaction segment.
+struct SelectThreshold {
+  uint32_t thr = 0u, need_eq = 0u;
+  uint32_t gt = 0u, eq = 0u;
+  bool counted = false;
+};
+
+// Wave w's contiguous segment [s_lo, s_hi) of n keys in the ordered compaction.
+template <int NT>
+__device__ __forceinline__ void select_segment(int n, int& s_lo, int& s_hi) {
   constexpr int NW = NT / kWave;
+  const int seg = ((n + NW - 1) / NW + kWave - 1) & ~(kWave - 1);
+  s_lo = int(threadIdx.x / kWave) * seg;
+  s_hi = min(n, s_lo + seg);
+}
+
+template <int NT, class Keys>
+__device__ __forceinline__ SelectThreshold select_search(const Keys& key, int n, uint32_t n_sel,
+                                                         int K, SelectShared<NT>& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const uint64_t lt = lanemask_lt();
-  // wave w owns the contiguous segment [s_lo, s_hi) in the compaction
-  const int seg = ((n + NW - 1) / NW + kWave - 1) & ~(kWave - 1);
-  const int s_lo = wave * seg;
-  const int s_hi = min(n, s_lo + seg);
+  int s_lo, s_hi;
+  select_segment<NT>(n, s_lo, s_hi);
 
   uint32_t thr = 0u, need_eq = 0u;
   uint32_t gt = 0u, eq = 0u;  // this wave's segment: keys > thr, keys == thr
@@ -312,8 +328,30 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
     }
   }
 
+  SelectThreshold r;
+  r.thr = thr;
+  r.need_eq = need_eq;
+  r.gt = gt;
+  r.eq = eq;
+  r.counted = counted;
+  return r;
+}
+
+template <int NT, class Keys, class Emit>
+__device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_sel, int K,
+                                            SelectShared<NT>& sh, Emit emit) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const uint64_t lt = lanemask_lt();
+  int s_lo, s_hi;
+  select_segment<NT>(n, s_lo, s_hi);
+  const SelectThreshold r = select_search<NT>(key, n, n_sel, K, sh);
+  const uint32_t thr = r.thr, need_eq = r.need_eq;
+  uint32_t gt = r.gt, eq = r.eq;
   // ordered compaction
-  if (!counted) {
+  if (!r.counted) {
     for_segment(key, s_lo, s_hi, lane, [&](int i, uint32_t k) {
       gt += __popcll(__ballot(k > thr));
       eq += __popcll(__ballot(i < s_hi && k == thr));
