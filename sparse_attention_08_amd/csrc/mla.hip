@@ -706,32 +706,43 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
 }
 
 // Merge split partials (bf16, normalised per split): out = sum_s e^{lse_s - L} o_s
-// with L = logsumexp_s lse_s.
-__global__ __launch_bounds__(128) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse,
-                                                          int H, int nsplit,
-                                                          __bf16* __restrict__ out,
-                                                          float* __restrict__ lse) {
+// with L = logsumexp_s lse_s.  One wave per (query, head), four heads per
+// workgroup; lane l takes value columns 8l .. 8l+7 (16-byte loads and stores).
+constexpr int kCombineHeads = 4;
+__global__ __launch_bounds__(kCombineHeads * kWave) void mla_combine_kernel(
+    const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse, int H, int nsplit,
+    __bf16* __restrict__ out, float* __restrict__ lse) {
   const int64_t t = blockIdx.x;
-  const int h = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int h = int(blockIdx.y) * kCombineHeads + int(threadIdx.x) / kWave;
+  if (h >= H) return;
   float mx = -INFINITY;
   for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_lse[(t * nsplit + s) * H + h]);
   float wsum = 0.0f;
-  float acc[kDv / 128] = {};
+  float acc[8] = {};
   for (int s = 0; s < nsplit; ++s) {
     const float ls = part_lse[(t * nsplit + s) * H + h];
     const float ws = ls == -INFINITY ? 0.0f : __expf(ls - mx);
     wsum += ws;
-    const uint16_t* po = part_o + ((t * nsplit + s) * H + h) * int64_t(kDv);
+    const uint4 v = *reinterpret_cast<const uint4*>(part_o + ((t * nsplit + s) * H + h) *
+                                                                 int64_t(kDv) + 8 * lane);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int x = 0; x < kDv / 128; ++x)
-      acc[x] = fmaf(ws, bf16_bits_to_f32(po[threadIdx.x + 128 * x]), acc[x]);
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = fmaf(ws, bf16_bits_to_f32(uint16_t(w4[j] & 0xFFFFu)), acc[2 * j]);
+      acc[2 * j + 1] = fmaf(ws, bf16_bits_to_f32(uint16_t(w4[j] >> 16)), acc[2 * j + 1]);
+    }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  uint16_t* orow = reinterpret_cast<uint16_t*>(out) + (t * H + h) * int64_t(kDv);
+  uint4 r;
+  uint32_t* r4 = reinterpret_cast<uint32_t*>(&r);
 #pragma unroll
-  for (int x = 0; x < kDv / 128; ++x) orow[threadIdx.x + 128 * x] = f32_to_bf16_bits(acc[x] * inv);
-  if (lse && threadIdx.x == 0) lse[t * H + h] = wsum > 0.0f ? mx + __logf(wsum) : -INFINITY;
+  for (int j = 0; j < 4; ++j)
+    r4[j] = uint32_t(f32_to_bf16_bits(acc[2 * j] * inv)) |
+            (uint32_t(f32_to_bf16_bits(acc[2 * j + 1] * inv)) << 16);
+  *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (t * H + h) * int64_t(kDv) +
+                            8 * lane) = r;
+  if (lse && lane == 0) lse[t * H + h] = wsum > 0.0f ? mx + __logf(wsum) : -INFINITY;
 }
 
 // fp32 inputs: one workgroup per (query, head).
@@ -842,8 +853,10 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
                      K, sm_scale, static_cast<__bf16*>(out), lse, part_o, part_lse, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(unsigned(n_q), n_heads), dim3(128), 0, stream,
-                     part_o, part_lse, n_heads, s, static_cast<__bf16*>(out), lse);
+  static_assert(kDv == 8 * kWave, "one wave per head row in the combine");
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(unsigned(n_q), (n_heads + kCombineHeads - 1) / kCombineHeads),
+                     dim3(kCombineHeads * kWave), 0, stream, part_o, part_lse, n_heads, s,
+                     static_cast<__bf16*>(out), lse);
   return hipGetLastError();
 }
 
