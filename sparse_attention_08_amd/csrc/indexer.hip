@@ -116,6 +116,36 @@ __device__ __forceinline__ uint8_t* kbuf() {
   return kBuf == 0 ? g_kb0 : g_kb1;
 }
 
+// A wave's tiles go through its matrix core in pairs (A, B), with one tile
+// pending across pairs: the MFMAs of A run beside the ReLU / weight epilogue of
+// the pending tile, the MFMAs of B beside that of A, and B is left pending.  So
+// one wave keeps both the matrix core and the VALU busy instead of leaving the
+// overlap to the other wave of its SIMD.  The pending logits always sit in the
+// same registers between pairs.
+template <class Op, int MT>
+struct PendingTile {
+  f32x16_t acc[MT];
+  int s0 = 0;         // first key of the tile
+  float ksc = 1.0f;   // the lane's key scale (fp8)
+  bool live = false;
+};
+
+// Order of one pair half: each MFMA followed by kV VALU operations of the other
+// tile's epilogue.  With kDsStep > 0, the kDsStep fragment reads of step st of
+// the second tile follow the last MFMA that uses step st of the first (MFMA i
+// is step i / MT), so the second tile's fragments can take the first's
+// registers.
+template <int kMf, int kV, int MT, int kDsStep, int I = 0>
+__device__ __forceinline__ void sched_mfma_valu() {
+  if constexpr (I < kMf) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);  // kV VALU
+    if constexpr (kDsStep > 0 && I % MT == MT - 1)
+      __builtin_amdgcn_sched_group_barrier(0x100, kDsStep, 0);  // DS reads
+    sched_mfma_valu<kMf, kV, MT, kDsStep, I + 1>();
+  }
+}
+
 // Scores of one wave's row over chunk c (keys key0 .. key0+255), which sits in
 // buffer kCur; the DMA of chunk c+1 goes to the other buffer kNn.
 template <class Op, int MT, int kCur, int kNn>
@@ -123,31 +153,49 @@ __device__ __forceinline__ void rows_chunk(int c, int nchunks, int key0, int hi,
                                            const uint8_t* __restrict__ k,
                                            const float* __restrict__ k_scale,
                                            const QueryRow<Op, MT>& qr, bool active, int a, int b,
-                                           float* srow, int wave, int lane) {
+                                           float* srow, int wave, int lane,
+                                           PendingTile<Op, MT>& pd) {
+  constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
   // per-lane key scales of this chunk, read before the next DMA is issued so that
   // waiting for them never waits for that DMA
   float ksc[kChunkTiles];
 #pragma unroll
   for (int kt = 0; kt < kChunkTiles; ++kt) {
     const int s = key0 + kt * kKeyTile + (lane & 31);
-    ksc[kt] = (k_scale != nullptr && s < hi) ? k_scale[s] : 1.0f;
+    ksc[kt] = (kScaled && k_scale != nullptr && s < hi) ? k_scale[s] : 1.0f;
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA pieces of chunk c landed
   __syncthreads();                // ... everyone's; all waves are done with chunk c-1
   if (c + 1 < nchunks) dma_chunk<Op>(kbuf<kNn>(), k, key0 + kChunkKeys, n_k, wave, lane);
   if (!active || key0 >= b || key0 + kChunkKeys <= a) return;
-  // Plain per-tile order (fragment reads, MFMAs, epilogue): the two waves that
-  // share a SIMD interleave each other's MFMA and VALU phases, which measured
-  // faster than interleaving one wave's next-tile MFMAs with its own epilogue.
-#pragma unroll
-  for (int kt = 0; kt < kChunkTiles; ++kt) {
-    const int s0 = key0 + kt * kKeyTile;
-    if (s0 >= b || s0 + kKeyTile <= a) continue;
-    typename Op::frag_t kb[Op::kSteps];
-    load_kfrags<Op>(kbuf<kCur>(), kt, lane, kb);
-    const float p = qr.score(kb) * ksc[kt];
+  constexpr int kMf = Op::kSteps * MT;                   // MFMAs per tile
+  constexpr int kDs = Op::kSteps * (Op::kFragBytes / 16);  // fragment reads per tile
+  constexpr int kV = (32 * MT + kMf - 1) / kMf;          // epilogue VALU per MFMA
+  auto put = [&](int s0, float p, float ks) {
     const int s = s0 + lane;
-    if (lane < 32 && s >= a && s < b) srow[s] = p;
+    if (lane < 32 && s >= a && s < b) srow[s] = p * ks;
+  };
+#pragma unroll
+  for (int pr = 0; pr < kChunkTiles / 2; ++pr) {
+    const int sA = key0 + 2 * pr * kKeyTile;
+    if (sA >= b || sA + 2 * kKeyTile <= a) continue;
+    typename Op::frag_t kA[Op::kSteps], kB[Op::kSteps];
+    load_kfrags<Op>(kbuf<kCur>(), 2 * pr, lane, kA);
+    load_kfrags<Op>(kbuf<kCur>(), 2 * pr + 1, lane, kB);
+    f32x16_t acc1[MT];
+    qr.mma(kA, acc1);
+    const float pP = qr.epilogue(pd.acc);
+    __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // tile A's fragments
+    __builtin_amdgcn_sched_group_barrier(0x002, 2 * kV, 0);
+    sched_mfma_valu<kMf, kV, MT, kDs / Op::kSteps>();
+    if (pd.live) put(pd.s0, pP, pd.ksc);
+    qr.mma(kB, pd.acc);
+    const float pA = qr.epilogue(acc1);
+    sched_mfma_valu<kMf, kV, MT, 0>();
+    put(sA, pA, ksc[2 * pr]);
+    pd.s0 = sA + kKeyTile;
+    pd.ksc = ksc[2 * pr + 1];
+    pd.live = true;
   }
 }
 
@@ -200,13 +248,21 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
   QueryRow<Op, MT> qr;
   if (active) qr.load(q, w, t, H, lane);
   float* srow = scores + t * ld;
+  PendingTile<Op, MT> pd;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) pd.acc[mt] = f32x16_t{};
 
   for (int c = 0; c < nchunks; c += 2) {
     rows_chunk<Op, MT, 0, 1>(c, nchunks, lo + c * kChunkKeys, hi, n_k, k, k_scale, qr, active,
-                             a, b, srow, wave, lane);
+                             a, b, srow, wave, lane, pd);
     if (c + 1 >= nchunks) break;
     rows_chunk<Op, MT, 1, 0>(c + 1, nchunks, lo + (c + 1) * kChunkKeys, hi, n_k, k, k_scale, qr,
-                             active, a, b, srow, wave, lane);
+                             active, a, b, srow, wave, lane, pd);
+  }
+  if (pd.live) {
+    const float p = qr.epilogue(pd.acc) * pd.ksc;
+    const int s = pd.s0 + lane;
+    if (lane < 32 && s >= a && s < b) srow[s] = p;
   }
 }
 
