@@ -57,31 +57,59 @@ __device__ __forceinline__ int swz(int kl, int cc) {
   return Op::kRowBytes == 256 ? (cc ^ (kl & 15)) : (cc ^ ((kl >> 1) & 7));
 }
 
+// Chunk DMA.  Wave w issues the 1 KB loads j = w, w + 8, ...; load j covers the
+// kKeysPerLoad keys from j * kKeysPerLoad, and lane l moves piece l % kPieces of
+// key l / kPieces into LDS slot j * 64 + l.  The piece's source position in the
+// key row (the swizzle) depends on the key only through key & 15 (bf16) or
+// (key >> 1) & 7 (fp8), which for every load of a wave is the same per lane, so
+// the lane part of the source address is one fixed offset and each load only
+// moves a wave-uniform base (global_load_lds with an SGPR base).
 template <class Op>
-__device__ __forceinline__ void dma_chunk(uint8_t* buf, const uint8_t* __restrict__ k,
-                                          int key0, int n_k, int wave, int lane) {
-  constexpr int kPieces = Op::kRowBytes / 16;            // per key
-  constexpr int kKeysPerLoad = kWave / kPieces;          // keys per 1 KB wave load
-  constexpr int kLoads = kChunkKeys / kKeysPerLoad;      // wave loads per chunk
-  asm volatile("" : "+v"(lane));
+struct ChunkDma {
+  static constexpr int kPieces = Op::kRowBytes / 16;      // per key
+  static constexpr int kKeysPerLoad = kWave / kPieces;    // keys per 1 KB wave load
+  static constexpr int kLoads = kChunkKeys / kKeysPerLoad;  // wave loads per chunk
+  static_assert(kLoads % kRowsPerBlock == 0, "every wave issues the same loads");
+  int lane_off;  // byte offset of this lane's piece from the load's first key row
+
+  __device__ __forceinline__ ChunkDma(int wave, int lane) {
+    const int kl = wave * kKeysPerLoad + lane / kPieces;  // local key of load j = wave
+    lane_off = (lane / kPieces) * Op::kRowBytes + swz<Op>(kl, lane % kPieces) * 16;
+  }
+
+  __device__ __forceinline__ void issue(uint8_t* buf, const uint8_t* __restrict__ k, int key0,
+                                        int n_k, int wave, int lane) const {
+    if (key0 + kChunkKeys <= n_k) {
 #pragma unroll
-  for (int u = 0; u < (kLoads + kRowsPerBlock - 1) / kRowsPerBlock; ++u) {
-    const int j = wave + kRowsPerBlock * u;
-    if (j < kLoads) {
-      const int kl = j * kKeysPerLoad + lane / kPieces;  // local key of this lane's piece
-      const int p = lane % kPieces;                      // its LDS position
+      for (int u = 0; u < kLoads / kRowsPerBlock; ++u) {
+        const int j = wave + kRowsPerBlock * u;
+        const uint8_t* base = k + (int64_t(key0) + j * kKeysPerLoad) * Op::kRowBytes;
+        // asm: a compiler-issued LDS-DMA would turn every later LDS wait into a
+        // full drain; the chunk's only wait is the explicit one in rows_chunk
+        asm volatile("global_load_lds_dwordx4 %0, %1 offset:0"
+                     :
+                     : "v"(lane_off), "s"(base), "{m0}"(ixcore::lds_addr(buf + j * kWave * 16))
+                     : "memory");
+      }
+      return;
+    }
+    // the last chunk runs past the keys: lanes past the end read the last key
+    // (lane laundered so that none of this is hoisted out of the chunk loop)
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int u = 0; u < kLoads / kRowsPerBlock; ++u) {
+      const int j = wave + kRowsPerBlock * u;
+      const int kl = j * kKeysPerLoad + lane / kPieces;
       int key = key0 + kl;
-      key = key < n_k ? key : n_k - 1;                   // past the end: any valid row
-      const uint8_t* src = k + int64_t(key) * Op::kRowBytes + swz<Op>(kl, p) * 16;
-      // asm: a compiler-issued LDS-DMA would turn every later LDS wait into a
-      // full drain; the chunk's only wait is the explicit one in rows_chunk
+      key = key < n_k ? key : n_k - 1;
+      const uint8_t* src = k + int64_t(key) * Op::kRowBytes + swz<Op>(kl, lane % kPieces) * 16;
       asm volatile("global_load_lds_dwordx4 %0, off"
                    :
                    : "v"(src), "{m0}"(ixcore::lds_addr(buf + j * kWave * 16))
                    : "memory");
     }
   }
-}
+};
 
 // K fragments of one 32-key tile (local keys kt*32 .. +32) from a chunk buffer.
 template <class Op>
@@ -154,7 +182,7 @@ __device__ __forceinline__ void rows_chunk(int c, int nchunks, int key0, int hi,
                                            const float* __restrict__ k_scale,
                                            const QueryRow<Op, MT>& qr, bool active, int a, int b,
                                            float* srow, int wave, int lane,
-                                           PendingTile<Op, MT>& pd) {
+                                           const ChunkDma<Op>& dma, PendingTile<Op, MT>& pd) {
   constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
   // per-lane key scales of this chunk, read before the next DMA is issued so that
   // waiting for them never waits for that DMA
@@ -166,7 +194,7 @@ __device__ __forceinline__ void rows_chunk(int c, int nchunks, int key0, int hi,
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA pieces of chunk c landed
   __syncthreads();                // ... everyone's; all waves are done with chunk c-1
-  if (c + 1 < nchunks) dma_chunk<Op>(kbuf<kNn>(), k, key0 + kChunkKeys, n_k, wave, lane);
+  if (c + 1 < nchunks) dma.issue(kbuf<kNn>(), k, key0 + kChunkKeys, n_k, wave, lane);
   if (!active || key0 >= b || key0 + kChunkKeys <= a) return;
   constexpr int kMf = Op::kSteps * MT;                   // MFMAs per tile
   constexpr int kDs = Op::kSteps * (Op::kFragBytes / 16);  // fragment reads per tile
@@ -237,10 +265,12 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
     span[1] = hi;
   }
   __syncthreads();
-  const int lo = span[0], hi = span[1];
+  const int lo = __builtin_amdgcn_readfirstlane(span[0]);
+  const int hi = __builtin_amdgcn_readfirstlane(span[1]);
   if (hi <= lo) return;
   const int nchunks = (hi - lo + kChunkKeys - 1) / kChunkKeys;
-  dma_chunk<Op>(kbuf<0>(), k, lo, n_k, wave, lane);
+  const ChunkDma<Op> dma(wave, lane);
+  dma.issue(kbuf<0>(), k, lo, n_k, wave, lane);
 
   const int64_t t = t0 + wave;
   const int a = win[wave], b = win[kRowsPerBlock + wave];
@@ -254,10 +284,10 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
 
   for (int c = 0; c < nchunks; c += 2) {
     rows_chunk<Op, MT, 0, 1>(c, nchunks, lo + c * kChunkKeys, hi, n_k, k, k_scale, qr, active,
-                             a, b, srow, wave, lane, pd);
+                             a, b, srow, wave, lane, dma, pd);
     if (c + 1 >= nchunks) break;
     rows_chunk<Op, MT, 1, 0>(c + 1, nchunks, lo + (c + 1) * kChunkKeys, hi, n_k, k, k_scale, qr,
-                             active, a, b, srow, wave, lane, pd);
+                             active, a, b, srow, wave, lane, dma, pd);
   }
   if (pd.live) {
     const float p = qr.epilogue(pd.acc) * pd.ksc;
