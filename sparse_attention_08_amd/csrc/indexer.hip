@@ -144,6 +144,18 @@ __device__ __forceinline__ uint8_t* kbuf() {
   return kBuf == 0 ? g_kb0 : g_kb1;
 }
 
+// The scores of the 32 keys s0 .. s0+31 (lanes l and l + 32 both hold key
+// s0 + l % 32) into a row through a buffer resource whose size ends at the
+// window end b, so keys past b are dropped by the hardware's range check;
+// keys before a get an offset past any size.  Both lane halves store the same
+// values to the same addresses.
+__device__ __forceinline__ void store_scores(__amdgpu_buffer_rsrc_t row, int a, int s0, int lane,
+                                             float p) {
+  const int s = s0 + (lane & 31);
+  const unsigned off = s >= a ? unsigned(s) * 4u : 0xFFFFFFF0u;
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p), row, off, 0, 0);
+}
+
 // A wave's tiles go through its matrix core in pairs (A, B), with one tile
 // pending across pairs: the MFMAs of A run beside the ReLU / weight epilogue of
 // the pending tile, the MFMAs of B beside that of A, and B is left pending.  So
@@ -181,7 +193,7 @@ __device__ __forceinline__ void rows_chunk(int c, int nchunks, int key0, int hi,
                                            const uint8_t* __restrict__ k,
                                            const float* __restrict__ k_scale,
                                            const QueryRow<Op, MT>& qr, bool active, int a, int b,
-                                           float* srow, int wave, int lane,
+                                           __amdgpu_buffer_rsrc_t srow, int wave, int lane,
                                            const ChunkDma<Op>& dma, PendingTile<Op, MT>& pd) {
   constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
   // per-lane key scales of this chunk, read before the next DMA is issued so that
@@ -199,10 +211,7 @@ __device__ __forceinline__ void rows_chunk(int c, int nchunks, int key0, int hi,
   constexpr int kMf = Op::kSteps * MT;                   // MFMAs per tile
   constexpr int kDs = Op::kSteps * (Op::kFragBytes / 16);  // fragment reads per tile
   constexpr int kV = (32 * MT + kMf - 1) / kMf;          // epilogue VALU per MFMA
-  auto put = [&](int s0, float p, float ks) {
-    const int s = s0 + lane;
-    if (lane < 32 && s >= a && s < b) srow[s] = p * ks;
-  };
+  auto put = [&](int s0, float p, float ks) { store_scores(srow, a, s0, lane, p * ks); };
 #pragma unroll
   for (int pr = 0; pr < kChunkTiles / 2; ++pr) {
     const int sA = key0 + 2 * pr * kKeyTile;
@@ -277,7 +286,9 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
   const bool active = b > a;
   QueryRow<Op, MT> qr;
   if (active) qr.load(q, w, t, H, lane);
-  float* srow = scores + t * ld;
+  // row t's scores, sized to end at its window end (empty for an idle wave)
+  const __amdgpu_buffer_rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc(
+      scores + t * ld, 0, active ? b * 4 : 0, 0x00020000);
   PendingTile<Op, MT> pd;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) pd.acc[mt] = f32x16_t{};
@@ -289,11 +300,7 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
     rows_chunk<Op, MT, 1, 0>(c + 1, nchunks, lo + (c + 1) * kChunkKeys, hi, n_k, k, k_scale, qr,
                              active, a, b, srow, wave, lane, dma, pd);
   }
-  if (pd.live) {
-    const float p = qr.epilogue(pd.acc) * pd.ksc;
-    const int s = pd.s0 + lane;
-    if (lane < 32 && s >= a && s < b) srow[s] = p;
-  }
+  if (pd.live) store_scores(srow, a, pd.s0, lane, qr.epilogue(pd.acc) * pd.ksc);
 }
 
 // ---------------------------------------------------------------------------
@@ -368,7 +375,11 @@ hipError_t launch_mfma(const void* q, const void* k, const float* k_scale, const
                        int H, float* scores, int64_t ld, hipStream_t stream) {
   const uint8_t* qb = static_cast<const uint8_t*>(q);
   const uint8_t* kb = static_cast<const uint8_t*>(k);
-  if (n_q <= 256) {
+  // the rows kernel addresses a score row through a buffer resource of b * 4
+  // bytes (an int); wider score rows, which no GPU holds for more than a few
+  // hundred rows, take the row-split kernel
+  constexpr int64_t kRowsMaxKeys = (int64_t(1) << 29) - 1;
+  if (n_q <= 256 || n_k > kRowsMaxKeys) {
     // few long rows (decode): split every row's keys over workgroups
     int nsplit = int(2048 / n_q);
     nsplit = nsplit < 1 ? 1 : (nsplit > 128 ? 128 : nsplit);
