@@ -325,6 +325,36 @@ def test_indexer_fp8_small(dsa):
                   rope=False)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_rows_random_windows(dsa, dtype):
+    # > 256 rows (the row-block kernel) with unrelated windows in one block of 8
+    # rows: empty, one key, starts and ends inside a 32-key tile, windows that
+    # skip whole key pairs and chunks, and windows reaching the last key
+    w = P4K if dtype == "bf16" else synth.WORKLOADS["fp8_64k"]
+    lay = synth.layout_from_lengths([1000])
+    p, _, _ = canonical_indexer(w, lay, dtype, signed=True, rope=dtype == "bf16")
+    g = np.random.default_rng(11)
+    n_q, n_k = lay.n_q, lay.n_k
+    rs = g.integers(0, n_k, n_q).astype(np.int32)
+    re = np.minimum(n_k, rs + g.integers(0, 700, n_q)).astype(np.int32)
+    rs[:8] = [0, 5, 40, 63, 64, 300, 999, 700]
+    re[:8] = [0, 6, 41, 65, 1000, 301, 1000, 690]   # empty, one key, ..., end < start
+    rs[8:16] = np.arange(8) * 97
+    re[8:16] = np.minimum(n_k, rs[8:16] + np.array([31, 32, 33, 63, 64, 65, 257, 513]))
+    q, k, wt, ks = to_device_indexer(p, dtype)
+    say(f"indexer random windows {dtype}: n_q={n_q} n_k={n_k}")
+    G = host(dsa.dsa_indexer_scores(q, k, wt, i32(rs), i32(re), k_scale=ks))
+    worst = 0.0
+    for t in range(n_q):
+        a, b = int(rs[t]), max(int(rs[t]), int(re[t]))
+        if b > a:
+            ksw = None if p["k_scale"] is None else p["k_scale"][a:b]
+            o, c = o_idx.score_row(p["q"][t], p["k"][a:b], p["w"][t], ksw, with_cond=True)
+            worst = max(worst, check_scores(G[t, a:b], o, c, 2e-2, f"{dtype} row {t}"))
+        assert np.isnan(G[t, :a]).all() and np.isnan(G[t, b:]).all(), f"row {t}: wrote outside window"
+    say(f"  max rel err {worst:.2e}")
+
+
 # ---------------------------------------------------------------------------
 # fused indexer + top-k (end to end against oracle scores + oracle top-k)
 # ---------------------------------------------------------------------------
