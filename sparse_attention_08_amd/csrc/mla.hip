@@ -73,10 +73,11 @@ constexpr bool kslot_is_permutation() {
 }
 static_assert(kslot_is_permutation(), "slots are a permutation of 0 .. 31");
 constexpr int kRegionB = kKT * 128;             // 4096
-constexpr int kEpCol = 72;                      // epilogue staging: bytes per value column
+constexpr int kEpRow = 2 * kDv + 16;            // epilogue staging: bytes per head row
 constexpr int kTileBytes = kRegionA + kRegionB;  // 37376
 constexpr int kQSteps = kDqk / 16;              // 36 K-steps of 16 dims
 constexpr int kVTiles = kDv / 32;               // 16 value tiles of 32 columns
+static_assert(32 * kEpRow <= kTileBytes, "a wave's 32 staged output rows fit its tile buffer");
 constexpr int kThreads = 256;                   // 4 waves x 32 heads
 constexpr int kWaves = kThreads / kWave;
 constexpr int kDmaPerWave = kKT / kWaves + 1;  // 8 latent rows + 1 rope load: 9
@@ -460,10 +461,13 @@ __device__ __forceinline__ void pv_tile(bf16x8_t (&fr)[4], const uint8_t* buf, b
     else if (m + 2 < 2 * kVTiles) wait_lgkm<4>();
     else if (m + 1 < 2 * kVTiles) wait_lgkm<2>();
     else wait_lgkm<0>();
+    // O^T += V^T . P^T: the V fragment is the A operand (value column = row)
+    // and the P fragment the B operand (head = column), so lane l accumulates
+    // head l % 32
     if (m < 2)
-      mfma_a<true>(o[m >> 1], (m & 1) ? p1 : p0, fr[m % 4]);
+      mfma_a<true>(o[m >> 1], fr[m % 4], (m & 1) ? p1 : p0);
     else
-      mfma_a<false>(o[m >> 1], (m & 1) ? p1 : p0, fr[m % 4]);
+      mfma_a<false>(o[m >> 1], fr[m % 4], (m & 1) ? p1 : p0);
     if (m + 4 < 2 * kVTiles) fr[m % 4] = vfrag<B>(buf, m + 4, lane);
     if constexpr (kSm) {
       if (m >= kSmFirstGap && m - kSmFirstGap < kSmPieces)
@@ -649,53 +653,40 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_h = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-  // Output rows (or split partials) of the wave's 32 heads, 1 KB each in bf16:
-  // the tile buffers are free now (the barrier above follows every wave's last
-  // read), so each wave stages its block in its own buffer, value column by value
-  // column (32 heads x 2 bytes per column, kEpCol bytes apart), then reads it back
-  // with transposing reads that hand each lane 8 consecutive columns of one head,
-  // which it writes with one 16-byte store.
-  //   write: accumulator registers 4g .. 4g+3 of a lane are 4 consecutive heads
-  //          of one column: scaled, rounded, one 8-byte write;
-  //   read:  in each 16-lane group, lane 4m+q reads heads 4q .. 4q+3 of column
-  //          c0+m; the transpose hands lane i columns c0 .. c0+3 of head i.
-  const int col0 = lane_e & 31;
+  // Output rows (or split partials) of the wave's 32 heads, 1 KB each in bf16.
+  // O^T puts head h0 + l % 32 in lane l, value columns 32 n + acc_row(r, half)
+  // in its registers, so the lane scales by its own head's 1 / l.  The tile
+  // buffers are free now (the barrier above follows every wave's last read):
+  // each wave stages its block in its own buffer row-major per head (kEpRow
+  // bytes per head: 16 bytes of padding move successive heads 4 banks apart),
+  // four consecutive columns per 8-byte write, then reads back whole head rows
+  // (lane j: columns 8 j .. 8 j + 7) and writes each with one 1 KB store.
   uint8_t* eb = wave == 0 ? g_kv0 : wave == 1 ? g_kv1 : wave == 2 ? g_kv2 : g_kv3;
   {
-    float ir[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ir[r] = __shfl(inv, acc_row(r, half_e));
-    uint8_t* wb = eb + col0 * kEpCol + 8 * half_e;
+    uint8_t* wb = eb + (lane_e & 31) * kEpRow + 8 * half_e;
 #pragma unroll
     for (int n = 0; n < kVTiles; ++n) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const bf16x2_t lo = {__bf16(o[n][4 * g] * ir[4 * g]), __bf16(o[n][4 * g + 1] * ir[4 * g + 1])};
-        const bf16x2_t hi = {__bf16(o[n][4 * g + 2] * ir[4 * g + 2]),
-                             __bf16(o[n][4 * g + 3] * ir[4 * g + 3])};
+        const bf16x2_t lo = {__bf16(o[n][4 * g] * inv), __bf16(o[n][4 * g + 1] * inv)};
+        const bf16x2_t hi = {__bf16(o[n][4 * g + 2] * inv), __bf16(o[n][4 * g + 3] * inv)};
         const uint2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        *reinterpret_cast<uint2*>(wb + n * 32 * kEpCol + g * 16) = v;
+        *reinterpret_cast<uint2*>(wb + (32 * n + 8 * g) * 2) = v;
       }
     }
   }
-  const int li = lane_e & 15;
-  const int grp = lane_e >> 4;
   uint16_t* obase = nsplit == 1 ? reinterpret_cast<uint16_t*>(out) + t * H * int64_t(kDv)
                                 : part_o + (t * nsplit + blockIdx.z) * H * int64_t(kDv);
+  // every row is read before the first store (the registers that held Q^T are
+  // free), so the LDS latency is paid once
+  v8i16_t ov[32];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int hd = h0 + 16 * hh + li;  // the head this lane stores
+  for (int h = 0; h < 32; ++h)
+    ov[h] = *reinterpret_cast<const v8i16_t*>(eb + h * kEpRow + 16 * lane_e);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int cb = 0; cb < kVTiles; ++cb) {
-      const int c0 = 32 * cb + 8 * grp;
-      const uint8_t* rb = eb + (c0 + (li >> 2)) * kEpCol + (16 * hh + 4 * (li & 3)) * 2;
-      const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(rb));
-      const v4i16_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(rb + 4 * kEpCol));
-      if (hd < H)
-        *reinterpret_cast<v8i16_t*>(obase + hd * int64_t(kDv) + c0) =
-            __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  }
+  for (int h = 0; h < 32; ++h)
+    if (h0 + h < H) *reinterpret_cast<v8i16_t*>(obase + (h0 + h) * int64_t(kDv) + 8 * lane_e) = ov[h];
   if (half_e == 0 && hvalid_e) {
     if (nsplit == 1) {
       if (lse) lse[t * H + head_e] = lse_h;
