@@ -143,56 +143,63 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   if (threadIdx.x == 0) cand_cnt[slot] = int32_t(n_sel < uint32_t(K) ? n_sel : uint32_t(K));
 }
 
-// Split path, phase 2: merge the candidates of a row (chunk order = column
-// order) and write the row's top-k with its -1 padding.
+// Split path, phase 2: merge candidate slots (slot order = column order), in
+// two levels so that the whole GPU takes part.  Level 1 (kFinal = false):
+// workgroup (row, g) merges the kGroup slots from g * kGroup and writes its
+// top-k back as the candidates of slot g * kGroup (every slot it reads is read
+// before any is written, and no other workgroup reads them).  Level 2 (kFinal):
+// one workgroup per row merges the slots 0, kStride, 2 kStride, ... and writes
+// the row's top-k with its -1 padding.
+template <int kGroup, int kStride, bool kFinal>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ row_ends, int32_t K,
-    int32_t* __restrict__ out, const uint32_t* __restrict__ cand_key,
-    const int32_t* __restrict__ cand_col, const int32_t* __restrict__ cand_cnt) {
-  __shared__ uint32_t keys[kMergeCap];
-  __shared__ int sel[kMaxSplitK];  // selected candidate positions, in output order
-  __shared__ int off[kMaxChunks + 1];
+    int32_t* __restrict__ out, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col,
+    int32_t* __restrict__ cand_cnt) {
+  __shared__ uint32_t keys[kGroup * kMaxSplitK];
+  __shared__ int sel[kMaxSplitK];  // selected candidate positions, then (level 1) their columns
+  __shared__ uint32_t skey[kFinal ? 1 : kMaxSplitK];
+  __shared__ int off[kGroup + 1];
   __shared__ SelectShared<kMergeThreads> sh;
   const int64_t row = blockIdx.x;
   const int n_win = row_ends[row] - row_starts[row];
   if (split_chunk_len(n_win) == 0) return;  // written whole by phase 1
+  const int64_t slot0 = row * kMaxChunks + int64_t(blockIdx.y) * kGroup * kStride;
   if (threadIdx.x == 0) {
     int o = 0;
-    for (int c = 0; c < kMaxChunks; ++c) {
-      off[c] = o;
-      o += cand_cnt[row * kMaxChunks + c];
+    for (int m = 0; m < kGroup; ++m) {
+      off[m] = o;
+      o += cand_cnt[slot0 + m * kStride];
     }
-    off[kMaxChunks] = o;
+    off[kGroup] = o;
   }
   __syncthreads();
-  const int n = off[kMaxChunks];
+  const int n = off[kGroup];
   // every thread issues all its candidate loads before storing any of them:
-  // slot s of chunk c for s = tid, tid + kMergeThreads (k <= 2048)
+  // slot s of member m for s = tid, tid + kMergeThreads (k <= 2048)
+  constexpr int kPer = kMaxSplitK / kMergeThreads;
   {
-    constexpr int kPer = kMaxSplitK / kMergeThreads;
-    uint32_t v[kMaxChunks][kPer];
+    uint32_t v[kGroup][kPer];
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const uint32_t* ck = cand_key + (row * kMaxChunks + c) * int64_t(K);
-      const int cnt = off[c + 1] - off[c];
+    for (int m = 0; m < kGroup; ++m) {
+      const uint32_t* ck = cand_key + (slot0 + m * kStride) * int64_t(K);
+      const int cnt = off[m + 1] - off[m];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int sl = int(threadIdx.x) + j * kMergeThreads;
-        v[c][j] = sl < cnt ? ck[sl] : 0u;
+        v[m][j] = sl < cnt ? ck[sl] : 0u;
       }
     }
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int cnt = off[c + 1] - off[c];
+    for (int m = 0; m < kGroup; ++m) {
+      const int cnt = off[m + 1] - off[m];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int sl = int(threadIdx.x) + j * kMergeThreads;
-        if (sl < cnt) keys[off[c] + sl] = v[c][j];
+        if (sl < cnt) keys[off[m] + sl] = v[m][j];
       }
     }
   }
   __syncthreads();
-  int32_t* dst = out + row * int64_t(K);
   // every candidate is selectable (-inf never becomes one); the selection is
   // recorded as candidate positions first, so that the column loads below are
   // independent of each other instead of one per step of the compaction
@@ -200,15 +207,45 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
                              [&](uint32_t p, int i, uint32_t) { sel[p] = i; });
   __syncthreads();
   const int k_eff = n < K ? n : K;
-  for (int p = threadIdx.x; p < K; p += kMergeThreads) {
-    int col = -1;
-    if (p < k_eff) {
-      const int i = sel[p];
-      int c = 0;
-      while (off[c + 1] <= i) ++c;
-      col = cand_col[(row * kMaxChunks + c) * int64_t(K) + (i - off[c])];
+  auto column = [&](int i) {
+    int m = 0;
+    while (off[m + 1] <= i) ++m;
+    return cand_col[(slot0 + m * kStride) * int64_t(K) + (i - off[m])];
+  };
+  if constexpr (kFinal) {
+    int32_t* dst = out + row * int64_t(K);
+    for (int p = threadIdx.x; p < K; p += kMergeThreads) dst[p] = p < k_eff ? column(sel[p]) : -1;
+  } else {
+    // gather the selection in LDS (its columns read from every member slot)
+    // before slot0 is overwritten
+    int cv[kPer];
+    uint32_t kv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = int(threadIdx.x) + j * kMergeThreads;
+      if (p < k_eff) {
+        const int i = sel[p];
+        cv[j] = column(i);
+        kv[j] = keys[i];
+      }
     }
-    dst[p] = col;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = int(threadIdx.x) + j * kMergeThreads;
+      if (p < k_eff) {
+        sel[p] = cv[j];
+        skey[p] = kv[j];
+      }
+    }
+    __syncthreads();
+    uint32_t* ck = cand_key + slot0 * int64_t(K);
+    int32_t* cc = cand_col + slot0 * int64_t(K);
+    for (int p = threadIdx.x; p < k_eff; p += kMergeThreads) {
+      ck[p] = skey[p];
+      cc[p] = sel[p];
+    }
+    if (threadIdx.x == 0) cand_cnt[slot0] = k_eff;
   }
 }
 
@@ -433,8 +470,16 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
 hipError_t launch_topk_merge(const int32_t* row_starts, const int32_t* row_ends, int64_t n_q,
                              int32_t K, int32_t* out, void* workspace, hipStream_t stream) {
   const Candidates cd = Candidates::at(workspace, n_q, K);
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(n_q)), dim3(kMergeThreads), 0, stream,
-                     row_starts, row_ends, K, out, cd.key, cd.col, cd.cnt);
+  constexpr int kGroup = 4;  // slots per level-1 merge
+  static_assert(kMaxChunks == kGroup * kGroup, "two levels of kGroup-way merges");
+  hipLaunchKernelGGL((topk_merge_kernel<kGroup, 1, false>), dim3(unsigned(n_q), kGroup),
+                     dim3(kMergeThreads), 0, stream, row_starts, row_ends, K, out, cd.key, cd.col,
+                     cd.cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((topk_merge_kernel<kGroup, kGroup, true>), dim3(unsigned(n_q), 1),
+                     dim3(kMergeThreads), 0, stream, row_starts, row_ends, K, out, cd.key, cd.col,
+                     cd.cnt);
   return hipGetLastError();
 }
 

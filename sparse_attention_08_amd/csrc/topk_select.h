@@ -13,7 +13,6 @@ constexpr int kCap = 8192;        // keys held in LDS by one workgroup
 constexpr int kBins = 2048;       // 11-bit digit
 constexpr int kMaxChunks = 16;    // chunks per row on the split path
 constexpr int kMaxSplitK = 2048;  // largest k on the split path
-constexpr int kMergeCap = kMaxChunks * kMaxSplitK;  // candidates merged in LDS
 constexpr int64_t kMaxSplitRows = 1024;
 constexpr int kMergeThreads = 1024;
 constexpr int kCandCap = 1024;   // boundary-bin keys refined on their own
