@@ -45,9 +45,9 @@ using namespace topksel;
 // per element.
 template <int CAP>
 __device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t* keys,
-                                              SelectShared<kThreads>& sh) {
+                                              SelectShared<kThreads>& sh, KeyRange& kr) {
   constexpr int kPer = CAP / 2 / kThreads;
-  uint32_t cnt = 0;
+  uint32_t cnt = 0, lo = 0xFFFFFFFFu, hi = 0u;
   for (int base = 0; base < n; base += kPer * kThreads) {
     float v[kPer];
 #pragma unroll
@@ -61,11 +61,43 @@ __device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t*
       if (i < n) {
         const uint32_t k = score_key(v[j]);
         keys[i] = k;
-        cnt += (k != 0u);
+        if (k != 0u) {
+          ++cnt;
+          lo = min(lo, k);
+          hi = max(hi, k);
+        }
       }
     }
   }
-  return block_sum<kThreads>(cnt, sh.tmp);  // also orders the LDS writes
+  // count, smallest and largest selectable key of the row in one reduction
+  // (its barriers also order the LDS writes)
+  constexpr int NW = kThreads / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    cnt += uint32_t(__shfl_xor(int(cnt), o));
+    lo = min(lo, uint32_t(__shfl_xor(int(lo), o)));
+    hi = max(hi, uint32_t(__shfl_xor(int(hi), o)));
+  }
+  if (lane == 0) {
+    sh.tmp[wave] = cnt;
+    sh.tmp[NW + wave] = lo;
+    sh.tmp[2 * NW + wave] = hi;
+  }
+  __syncthreads();
+  cnt = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    cnt += sh.tmp[w];
+    lo = min(lo, sh.tmp[NW + w]);
+    hi = max(hi, sh.tmp[2 * NW + w]);
+  }
+  __syncthreads();
+  kr.lo = lo;
+  kr.hi = hi;
+  kr.known = true;
+  return cnt;
 }
 
 // Whole row by one workgroup; writes topk_idx[row] including the -1 padding.
@@ -81,8 +113,9 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64
   uint32_t n_sel;
   auto emit = [&](uint32_t p, int i, uint32_t) { dst[p] = a + i; };
   if (n <= CAP) {
-    n_sel = load_keys<CAP>(src, n, keys, sh);
-    select_topk<kThreads>(LdsKeys{keys}, n, n_sel, K, sh, emit);
+    KeyRange kr;
+    n_sel = load_keys<CAP>(src, n, keys, sh, kr);
+    select_topk<kThreads>(LdsKeys{keys}, n, n_sel, K, sh, emit, kr);
   } else {
     uint32_t cnt = 0;
     for (int i = threadIdx.x; i < n; i += kThreads) cnt += (score_key(src[i]) != 0u);
@@ -133,13 +166,17 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   const int64_t slot = row * kMaxChunks + c;
   const int lo = c * clen;
   const int m = lo < n ? min(clen, n - lo) : 0;
-  const uint32_t n_sel = load_keys<kCap>(scores + row * ld + a + lo, m, keys, sh);
+  KeyRange kr;
+  const uint32_t n_sel = load_keys<kCap>(scores + row * ld + a + lo, m, keys, sh, kr);
   uint32_t* ck = cand_key + slot * K;
   int32_t* cc = cand_col + slot * K;
-  select_topk<kThreads>(LdsKeys{keys}, m, n_sel, K, sh, [&](uint32_t p, int i, uint32_t k) {
-    ck[p] = k;
-    cc[p] = a + lo + i;
-  });
+  select_topk<kThreads>(
+      LdsKeys{keys}, m, n_sel, K, sh,
+      [&](uint32_t p, int i, uint32_t k) {
+        ck[p] = k;
+        cc[p] = a + lo + i;
+      },
+      kr);
   if (threadIdx.x == 0) cand_cnt[slot] = int32_t(n_sel < uint32_t(K) ? n_sel : uint32_t(K));
 }
 
@@ -374,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
       bool shrunk = false;
       {
         RadixSearch<kThreads> rs{sh.sel};
-        rs.init(LdsKeys{sh.keys}, ncand, K);
+        rs.init(LdsKeys{sh.keys}, ncand, K, KeyRange{});
         if (rs.shift > 0) {
           const uint32_t in_bin = rs.pass(LdsKeys{sh.keys}, ncand);
           // keys whose d has the picked digit or a higher one: at least k

@@ -22,7 +22,7 @@ template <int NT>
 struct SelectShared {
   static constexpr int kNW = NT / kWave;
   uint32_t hist[kBins];
-  uint32_t tmp[2 * kNW];
+  uint32_t tmp[3 * kNW];
   uint32_t seg_cnt[2 * kNW];
   uint32_t wsum[kNW];  // radix pass: wave totals of the bin counts
   uint32_t pick[3];    // radix pass: the digit, the rank left, the digit's count
@@ -115,6 +115,14 @@ __device__ __forceinline__ void for_segment(const Keys& key, int s_lo, int s_hi,
 // `prefix` holds the digits of d picked so far (the bits under pmask), the
 // k-th largest key lies among the keys whose d has that prefix, and it is the
 // `remaining`-th largest of them.
+// The smallest and largest selectable (nonzero) key of a row, when the caller
+// already has them (the keys were mapped in registers on their way to LDS);
+// `known` is uniform over the workgroup.
+struct KeyRange {
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  bool known = false;
+};
+
 template <int NT>
 struct RadixSearch {
   SelectShared<NT>& sh;
@@ -125,16 +133,20 @@ struct RadixSearch {
   uint32_t remaining = 0u;
 
   template <class Keys>
-  __device__ __forceinline__ void init(const Keys& key, int n, int K) {
-    for (int i = int(threadIdx.x); i < kBins; i += NT) sh.hist[i] = 0u;  // ordered by block_min_max
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for_keys<NT>(key, n, [&](int, uint32_t k) {
-      if (k != 0u) {
-        lo = min(lo, k);
-        hi = max(hi, k);
-      }
-    });
-    block_min_max<NT>(lo, hi, sh.tmp);
+  __device__ __forceinline__ void init(const Keys& key, int n, int K, const KeyRange& kr) {
+    for (int i = int(threadIdx.x); i < kBins; i += NT) sh.hist[i] = 0u;
+    uint32_t lo = kr.lo, hi = kr.hi;
+    if (kr.known) {
+      __syncthreads();  // orders the clears before the first pass's counts
+    } else {
+      for_keys<NT>(key, n, [&](int, uint32_t k) {
+        if (k != 0u) {
+          lo = min(lo, k);
+          hi = max(hi, k);
+        }
+      });
+      block_min_max<NT>(lo, hi, sh.tmp);  // its barrier also orders the clears
+    }
     kmin = lo;
     const uint32_t range = hi - lo;  // d in [0, range]
     shift = range == 0u ? 0 : 32 - __builtin_clz(range);
@@ -244,7 +256,8 @@ __device__ __forceinline__ void select_segment(int n, int& s_lo, int& s_hi) {
 
 template <int NT, class Keys>
 __device__ __forceinline__ SelectThreshold select_search(const Keys& key, int n, uint32_t n_sel,
-                                                         int K, SelectShared<NT>& sh) {
+                                                         int K, SelectShared<NT>& sh,
+                                                         const KeyRange& kr = KeyRange{}) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -258,7 +271,7 @@ __device__ __forceinline__ SelectThreshold select_search(const Keys& key, int n,
   if (n_sel > uint32_t(K)) {
     if (tid == 0) sh.ccount = 0u;  // ordered by the barriers of init
     RadixSearch<NT> rs{sh};
-    rs.init(key, n, K);
+    rs.init(key, n, K, kr);
     const uint32_t in_bin = rs.shift > 0 ? rs.pass(key, n) : 0u;
     if (rs.shift > 0 && in_bin <= uint32_t(kCandCap)) {
       // gather the boundary digit's keys; count the keys above it per segment
@@ -338,7 +351,8 @@ __device__ __forceinline__ SelectThreshold select_search(const Keys& key, int n,
 
 template <int NT, class Keys, class Emit>
 __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_sel, int K,
-                                            SelectShared<NT>& sh, Emit emit) {
+                                            SelectShared<NT>& sh, Emit emit,
+                                            const KeyRange& kr = KeyRange{}) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -346,7 +360,7 @@ __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_s
   const uint64_t lt = lanemask_lt();
   int s_lo, s_hi;
   select_segment<NT>(n, s_lo, s_hi);
-  const SelectThreshold r = select_search<NT>(key, n, n_sel, K, sh);
+  const SelectThreshold r = select_search<NT>(key, n, n_sel, K, sh, kr);
   const uint32_t thr = r.thr, need_eq = r.need_eq;
   uint32_t gt = r.gt, eq = r.eq;
   // ordered compaction
