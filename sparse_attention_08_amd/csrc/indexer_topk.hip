@@ -49,7 +49,8 @@ template <class Op, int MT, bool kScaled>
 __device__ __forceinline__ uint32_t score_range(const QueryRow<Op, MT>& qr,
                                                 const uint8_t* __restrict__ k,
                                                 const float* __restrict__ k_scale, int s_lo,
-                                                int m, uint32_t* out, int lane, int wave) {
+                                                int m, uint32_t* out, int lane, int wave,
+                                                uint32_t& kmin, uint32_t& kmax) {
   constexpr int NW = kThreads / kWave;
   const int nt = (m + kKeyTile - 1) / kKeyTile;
   const int hi = s_lo + m;
@@ -60,7 +61,11 @@ __device__ __forceinline__ uint32_t score_range(const QueryRow<Op, MT>& qr,
       if constexpr (kScaled) p *= ks;
       const uint32_t key = score_key(p);
       out[j] = key;
-      cnt += key != 0u;
+      if (key != 0u) {
+        ++cnt;
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
     }
   };
   ixcore::stream_tiles<Op, MT, kScaled>(qr, k, k_scale, s_lo, hi, wave, NW, nt, lane, put);
@@ -94,16 +99,21 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
     const int64_t slot = t * kMaxChunks + c;
     const int lo = c * clen;
     const int m = lo < n ? min(clen, n - lo) : 0;
-    const uint32_t cnt =
-        score_range<Op, MT, kScaled>(qr, k, k_scale, a + lo, m, sh.keys, lane, wave);
-    const uint32_t n_sel = block_sum<kThreads>(cnt, sh.sel.tmp);  // also orders the LDS writes
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    const uint32_t cnt = score_range<Op, MT, kScaled>(qr, k, k_scale, a + lo, m, sh.keys, lane,
+                                                      wave, kmin, kmax);
+    KeyRange kr;
+    const uint32_t n_sel =
+        block_count_range<kThreads>(cnt, kmin, kmax, sh.sel, kr);  // also orders the LDS writes
     uint32_t* ck = cand_key + slot * K;
     int32_t* cc = cand_col + slot * K;
-    select_topk<kThreads>(LdsKeys{sh.keys}, m, n_sel, K, sh.sel,
-                          [&](uint32_t p, int i, uint32_t key) {
-                            ck[p] = key;
-                            cc[p] = a + lo + i;
-                          });
+    select_topk<kThreads>(
+        LdsKeys{sh.keys}, m, n_sel, K, sh.sel,
+        [&](uint32_t p, int i, uint32_t key) {
+          ck[p] = key;
+          cc[p] = a + lo + i;
+        },
+        kr);
     if (threadIdx.x == 0) cand_cnt[slot] = int32_t(n_sel < uint32_t(K) ? n_sel : uint32_t(K));
     return;
   }
@@ -113,8 +123,9 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
   uint32_t ncand = 0u;
   for (int lo = 0;; lo += kCap) {
     const int m = lo < n ? min(kCap, n - lo) : 0;
-    const uint32_t cnt =
-        score_range<Op, MT, kScaled>(qr, k, k_scale, a + lo, m, sh.keys + ncand, lane, wave);
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // not used: the running candidates join the keys
+    const uint32_t cnt = score_range<Op, MT, kScaled>(qr, k, k_scale, a + lo, m, sh.keys + ncand,
+                                                      lane, wave, kmin, kmax);
     const uint32_t n_sel = ncand + block_sum<kThreads>(cnt, sh.sel.tmp);
     const int total = int(ncand) + m;
     const int nc = int(ncand);

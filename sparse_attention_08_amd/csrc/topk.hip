@@ -69,35 +69,7 @@ __device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t*
       }
     }
   }
-  // count, smallest and largest selectable key of the row in one reduction
-  // (its barriers also order the LDS writes)
-  constexpr int NW = kThreads / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) {
-    cnt += uint32_t(__shfl_xor(int(cnt), o));
-    lo = min(lo, uint32_t(__shfl_xor(int(lo), o)));
-    hi = max(hi, uint32_t(__shfl_xor(int(hi), o)));
-  }
-  if (lane == 0) {
-    sh.tmp[wave] = cnt;
-    sh.tmp[NW + wave] = lo;
-    sh.tmp[2 * NW + wave] = hi;
-  }
-  __syncthreads();
-  cnt = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    cnt += sh.tmp[w];
-    lo = min(lo, sh.tmp[NW + w]);
-    hi = max(hi, sh.tmp[2 * NW + w]);
-  }
-  __syncthreads();
-  kr.lo = lo;
-  kr.hi = hi;
-  kr.known = true;
-  return cnt;
+  return block_count_range<kThreads>(cnt, lo, hi, sh, kr);  // also orders the LDS writes
 }
 
 // Whole row by one workgroup; writes topk_idx[row] including the -1 padding.

@@ -123,6 +123,42 @@ struct KeyRange {
   bool known = false;
 };
 
+// Count, smallest and largest selectable key over the workgroup in one
+// reduction of per-thread values (two barriers: the first also orders the
+// caller's earlier LDS writes, the second the reuse of tmp).  Returns the count
+// and fills kr.
+template <int NT>
+__device__ __forceinline__ uint32_t block_count_range(uint32_t cnt, uint32_t lo, uint32_t hi,
+                                                      SelectShared<NT>& sh, KeyRange& kr) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    cnt += uint32_t(__shfl_xor(int(cnt), o));
+    lo = min(lo, uint32_t(__shfl_xor(int(lo), o)));
+    hi = max(hi, uint32_t(__shfl_xor(int(hi), o)));
+  }
+  if (lane == 0) {
+    sh.tmp[wave] = cnt;
+    sh.tmp[NW + wave] = lo;
+    sh.tmp[2 * NW + wave] = hi;
+  }
+  __syncthreads();
+  cnt = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    cnt += sh.tmp[w];
+    lo = min(lo, sh.tmp[NW + w]);
+    hi = max(hi, sh.tmp[2 * NW + w]);
+  }
+  __syncthreads();
+  kr.lo = lo;
+  kr.hi = hi;
+  kr.known = true;
+  return cnt;
+}
+
 template <int NT>
 struct RadixSearch {
   SelectShared<NT>& sh;
