@@ -8,16 +8,17 @@
 // of v_mfma_f32_32x32x16_bf16 (or v_mfma_f32_32x32x64_f8f6f4) holds, in lane l,
 // 16 heads of key column l%32.  The ReLU and the weighted head sum happen in
 // those registers; one cross-lane add (lane l + lane l^32) finishes the head sum,
-// and lanes 0..31 store 32 consecutive scores (one 128-byte line).  The [H x T]
-// logits never leave the registers.
+// and 32 consecutive scores leave as one 128-byte line.  The [H x T] logits
+// never leave the registers.
 //
 // Two work layouts:
 //   rows kernel (prefill)  8 waves = 8 consecutive query rows share 256-key
 //                          chunks staged in LDS by LDS-DMA (XOR-swizzled rows:
 //                          conflict-free b128 fragment reads); q and w of a row
-//                          stay in registers for the whole key loop; row blocks
-//                          are issued latest-first so the longest causal rows
-//                          start first.
+//                          stay in registers for the whole key loop; each wave
+//                          overlaps its tiles' MFMAs with its own epilogue (tile
+//                          pairs with one tile pending); row blocks are issued
+//                          latest-first so the longest causal rows start first.
 //   rowsplit kernel (decode) one long row per workgroup slice: each wave streams
 //                          its own 32-key tiles through private LDS buffers with
 //                          contiguous 1 KB LDS-DMA loads (the keys are read once,
@@ -40,9 +41,8 @@ using ixcore::kKeyTile;
 // ---------------------------------------------------------------------------
 // prefill: 8 query rows per workgroup (one per wave), keys staged through LDS in
 // chunks of 256 by LDS-DMA one chunk ahead (two buffers, one workgroup barrier
-// per 8 tiles, so the two waves of a SIMD drift apart and one wave's ReLU/weight
-// epilogue runs while the other's MFMAs occupy the matrix core).  LDS rows are unpadded; 16-byte pieces
-// are XOR-swizzled by the key so that the fragment reads are conflict-free.
+// per 8 tiles).  LDS rows are unpadded; 16-byte pieces are XOR-swizzled by the
+// key so that the fragment reads are conflict-free.
 // ---------------------------------------------------------------------------
 constexpr int kRowsPerBlock = 8;
 constexpr int kRowsThreads = kRowsPerBlock * kWave;

@@ -12,7 +12,7 @@
 // bf16 kernel: one workgroup = one query x 128 heads, 4 waves (one per SIMD)
 // of 32 heads each; or a slice of the query's selected keys when the key list
 // is split (few queries: decode).  A wave keeps its Q^T [576 x 32 heads] in 144
-// VGPRs and its O [32 heads x 512] in the 256 accumulation registers for the
+// VGPRs and its O^T [512 x 32 heads] in the 256 accumulation registers for the
 // whole query, so no partial result crosses waves.  Per tile of 32 selected
 // keys:
 //   gather    LDS-DMA (global_load_lds, 16 bytes per lane) of the 32 latent rows
@@ -27,10 +27,12 @@
 //             tile exceeds m_ref + 32, in which case the workgroup runs the
 //             query a second time with m_ref = the true max (known by then), so
 //             O is never rescaled inside the loop;
-//   O += P.V  the probabilities, rounded to bf16, are the A operand (heads on M,
-//             keys on K) in the order the S^T accumulator holds them; the B
-//             operand (keys x value columns) comes from the same row-major tile
-//             through ds_read_b64_tr_b16 (transposing LDS read).
+//   O += P.V  computed as O^T += V^T . P^T, so that each lane accumulates one
+//             head: the probabilities, rounded to bf16 in the order the S^T
+//             accumulator holds them (8 keys of one head per lane), are the B
+//             operand, and the V fragments (8 keys of one value column per
+//             lane, from the same row-major tile through ds_read_b64_tr_b16, a
+//             transposing LDS read) are the A operand.
 // The P.V of tile i-1 runs while the softmax of tile i is computed (its VALU
 // work sits between those MFMAs), and the gather of tile i+2 is issued between
 // the MFMAs of S(i).  The row sum adds the bf16-rounded probabilities, so the
@@ -257,8 +259,8 @@ __device__ __forceinline__ void wait_tile(bool next_in_flight) {
 }
 
 // V fragment m = 2n + ks (value tile n, key step ks) of the tile in buffer B (or
-// `buf` when B < 0): the B operand of the P.V MFMA (8 keys x 1 value column per
-// lane), read from the row-major tile with ds_read_b64_tr_b16: in each group of
+// `buf` when B < 0): the A operand of the V^T . P^T MFMA (8 keys x 1 value column
+// per lane), read from the row-major tile with ds_read_b64_tr_b16: in each group of
 // 16 lanes, lane 4m'+q reads 4 value columns of key row k0+m' and the transpose
 // hands lane i the 4 keys k0..k0+3 of column n0+i.  Lane half h needs keys
 // {4h..4h+3} (first read) and {8+4h..8+4h+3} (second read) of each 16-key step:
@@ -441,8 +443,8 @@ __device__ __forceinline__ void softmax_all(Softmax& sm, float scale2, float& m_
   for (int k = 0; k < kSmPieces; ++k) sm_piece(k, sm, scale2, m_ref, m_max, over, l_run);
 }
 
-// O += P . V for the tile in buffer B (B < 0: the buffer `buf` chosen at run
-// time).  The B operand comes from vfrag; on entry the ring holds V fragments
+// O^T += V^T . P^T for the tile in buffer B (B < 0: the buffer `buf` chosen at
+// run time).  The V operand comes from vfrag; on entry the ring holds V fragments
 // 0..3 (kFill: read them first).  With kSm, one softmax piece of the current
 // tile follows each MFMA from gap kSmFirstGap on.
 template <int B, bool kSm, bool kFill>
