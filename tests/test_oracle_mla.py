@@ -72,6 +72,23 @@ def test_special_cases():
     # empty selection
     o, l = mla.attend_row(q, kv, np.full(5, -1), 0.7, dv)
     assert np.all(o == 0) and np.all(np.isneginf(l))
-    # a shift of every logit by a constant does not change the output
-    o3, l3 = mla.attend_row(q, kv + 0.0, idx, 0.7, dv)
-    np.testing.assert_allclose(o3, o1)
+    # a shift of every logit by a constant: one more dim with kv = 1 on every row
+    # and q = c on every head adds c * sm_scale to each logit (the value dims are
+    # untouched); the output is unchanged and the lse moves by c * sm_scale
+    c = np.linspace(-40.0, 25.0, H)
+    q_ext = np.concatenate([q, c[:, None]], axis=1)
+    kv_ext = np.concatenate([kv, np.ones((N, 1))], axis=1)
+    o3, l3 = mla.attend_row(q_ext, kv_ext, idx, 0.7, dv)
+    np.testing.assert_allclose(o3, o1, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(l3, l1 + 0.7 * c, rtol=1e-13)
+    # a logit that grows by 200 across the selection: the largest key dominates,
+    # lse = its logit + log(1 + sum of the others' e^(l - l_max))
+    kv_big = kv.copy()
+    kv_big[:, 0] = np.arange(N) * 10.0
+    qb = np.zeros((1, dqk)); qb[0, 0] = 1.0
+    o4, l4 = mla.attend_row(qb, kv_big, np.array([29, 3, 28]), 1.0, dv)
+    np.testing.assert_allclose(l4[0], 290.0 + np.log1p(np.exp(-10.0) + np.exp(-260.0)), rtol=1e-15)
+    w29 = 1.0 / (1.0 + np.exp(-10.0) + np.exp(-260.0))
+    np.testing.assert_allclose(o4[0], w29 * kv_big[29, :dv] + (1 - w29) * kv_big[28, :dv]
+                               + np.exp(-260.0) * w29 * (kv_big[3, :dv] - kv_big[28, :dv]),
+                               rtol=1e-12, atol=1e-15)

@@ -135,3 +135,94 @@ def test_fp8_fold_equals_dequantised_definition():
     ref = indexer.score_row(deq_q[0], deq_k, w[0])
     got = indexer.score_row(p["q"][0], p["k"], p["w"][0], p["k_scale"])
     np.testing.assert_allclose(got, ref, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the composed preparation: LayerNorm -> RoPE -> rounding, positions per sample
+# ---------------------------------------------------------------------------
+def _prep_fixture():
+    rows = {l.split()[0]: [float(v) for v in l.split()[1:]]
+            for l in open(os.path.join(GOLD, "prep_hand.txt")) if l.strip() and not l.startswith("#")}
+    return rows
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prepare_composed_hand_fixture(dtype):
+    # norm, then rope (half-split pairs), then one rounding to the operand format:
+    # a rope applied before the norm, interleaved pairs, or a normed query fail it
+    f = _prep_fixture()
+    q_raw = np.array(f["q_raw"]).reshape(1, 1, 6)
+    k_raw = np.array(f["k_raw"]).reshape(1, 6)
+    w = np.array([f["w"]])
+    p = prep.prepare_indexer_inputs(q_raw, k_raw, w, np.array([int(f["q_pos"][0])]),
+                                    np.array([int(f["k_pos"][0])]), dtype, rope_dim=4,
+                                    rope_main_dim=4, theta=1e4, eps=1e-6)
+    want_k, want_q = np.array(f["k_out"]), np.array(f["q_out"])
+    if dtype == "f32":
+        np.testing.assert_allclose(p["k"][0], want_k, rtol=1.2e-7, atol=0)
+        np.testing.assert_allclose(p["q"][0, 0], want_q, rtol=1.2e-7, atol=0)
+    else:
+        to_bf16 = lambda x: torch.tensor(x, dtype=torch.float64).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(p["k"][0], to_bf16(want_k))
+        np.testing.assert_array_equal(p["q"][0, 0], to_bf16(want_q))
+    np.testing.assert_array_equal(p["w"], w)
+    assert p["k_scale"] is None
+
+
+def test_positions_restart_per_sample():
+    # review comment 1 of vime pull request #502 keeps per-sample positions and
+    # rebases only the indices; the rope angle uses the position inside the sample
+    import synth
+    lay = synth.layout_from_lengths([3, 2])
+    np.testing.assert_array_equal(lay.positions(), [0, 1, 2, 0, 1])
+    np.testing.assert_array_equal(lay.key_positions(), [0, 1, 2, 0, 1])
+    dec = synth.layout_from_lengths([5, 3], decode=True)       # the query is the last token
+    np.testing.assert_array_equal(dec.positions(), [4, 2])
+    # a sample that repeats the first tokens of another one gets identical operands
+    g = np.random.default_rng(9)
+    q_raw = g.standard_normal((5, 2, 8))
+    k_raw = g.standard_normal((5, 8))
+    q_raw[3:5], k_raw[3:5] = q_raw[0:2], k_raw[0:2]
+    w = g.random((5, 2))
+    p = prep.prepare_indexer_inputs(q_raw, k_raw, w, lay.positions(), lay.key_positions(), "f32",
+                                    rope_dim=4, rope_main_dim=4)
+    np.testing.assert_array_equal(p["q"][3:5], p["q"][0:2])
+    np.testing.assert_array_equal(p["k"][3:5], p["k"][0:2])
+    # and the first token of each sample is not rotated (position 0)
+    p0 = prep.prepare_indexer_inputs(q_raw, k_raw, w, lay.positions(), lay.key_positions(), "f32")
+    np.testing.assert_array_equal(p["q"][[0, 3]], p0["q"][[0, 3]])
+    np.testing.assert_array_equal(p["k"][[0, 3]], p0["k"][[0, 3]])
+    assert np.abs(p["q"][[1, 2, 4]] - p0["q"][[1, 2, 4]]).max() > 1e-3
+
+
+def test_same_position_pair_is_rope_invariant():
+    # q and k of one token are rotated by the same angle, so their dot product
+    # over the rotated dims is unchanged: the diagonal scores of a prefill and a
+    # decode query's score against its own cache entry equal the unrotated ones
+    # (up to the fp32 rounding of the operands).  Rotating q and k at different
+    # positions breaks this.
+    import synth
+    from oracle import indexer
+    g = np.random.default_rng(10)
+    for lay in (synth.layout_from_lengths([6, 4]), synth.layout_from_lengths([7, 3], decode=True)):
+        H, D = 3, 16
+        q_raw = g.standard_normal((lay.n_q, H, D)) * 3.0
+        k_raw = g.standard_normal((lay.n_k, D))
+        w = g.standard_normal((lay.n_q, H))
+        args = (q_raw, k_raw, w, lay.positions(), lay.key_positions(), "f32")
+        pr = prep.prepare_indexer_inputs(*args, rope_dim=8, rope_main_dim=8)
+        pn = prep.prepare_indexer_inputs(*args)
+        cu_q, cu_k = lay.cu_q, lay.cu_k
+        for b in range(len(lay.q_lens)):
+            for j in range(int(lay.q_lens[b])):
+                t = int(cu_q[b]) + j
+                s = int(cu_k[b + 1]) - int(lay.q_lens[b]) + j      # the query's own token
+                dr = pr["q"][t] @ pr["k"][s]
+                dn = pn["q"][t] @ pn["k"][s]
+                np.testing.assert_allclose(dr, dn, rtol=1e-5, atol=1e-5)
+                sr = indexer.score_row(pr["q"][t], pr["k"][s:s + 1], pr["w"][t])
+                sn = indexer.score_row(pn["q"][t], pn["k"][s:s + 1], pn["w"][t])
+                np.testing.assert_allclose(sr, sn, rtol=1e-5, atol=1e-5)
+        # an off-diagonal pair does change (the rope is not a no-op here)
+        t, s = lay.n_q - 1, 0
+        assert abs(pr["q"][t] @ pr["k"][s] - pn["q"][t] @ pn["k"][s]).max() > 1e-3
