@@ -22,10 +22,12 @@
  *     several host threads.
  *   - Every call returns DSA_OK (0) or a negative dsa_status.  Arguments are
  *     validated on the host before anything is enqueued; on error nothing is
- *     enqueued and no output is touched.  Device-side preconditions (windows
- *     inside [0, n_k], indices in range, no NaN scores in a window) are not
- *     checked; violating them gives unspecified output but stays inside the
- *     buffers described here, except where noted.
+ *     enqueued and no output is touched.
+ *   - Device-side values are never trusted for addressing: every kernel clamps
+ *     a window to [0, n_k] (a window that ends before it starts is empty), and
+ *     the attention skips an index outside [0, n_kv) exactly like -1.  A NaN
+ *     score inside a window is a precondition violation that gives an
+ *     unspecified selection, still inside the buffers described here.
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -165,7 +167,7 @@ int dsa_indexer_scores(const void* q, const void* k, const float* k_scale,
  *             (key, column) are merged: n_q * 16 * index_topk * 8 + n_q * 64
  *             bytes.  Its contents on entry do not matter.
  * Bit-exact: the result is a function of the fp32 score bits only.
- * Supported: 1 <= index_topk <= 65536; windows within [0, n_cols].
+ * Supported: 1 <= index_topk <= 65536.  Windows are clamped to [0, n_cols].
  */
 size_t dsa_topk_workspace_size(int64_t n_q, int64_t n_cols, int32_t index_topk);
 int dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_starts,
@@ -216,7 +218,8 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale,
  *
  *   q         [n_q, n_heads, d_qk] of dtype (F32 or BF16)
  *   kv        [n_kv, d_qk] of dtype; V = the first d_v columns of the same rows
- *   topk_idx  int32 [n_q, index_topk]; entries in [0, n_kv) or -1
+ *   topk_idx  int32 [n_q, index_topk]; entries in [0, n_kv) or -1 (an entry
+ *             outside [0, n_kv) is skipped like -1)
  *   out       [n_q, n_heads, d_v] of dtype;  lse f32 [n_q, n_heads] or NULL
  *   workspace at least dsa_sparse_mla_workspace_size(...) bytes (may be 0).
  *   For few queries (BF16) each row's keys are split over several workgroups;

@@ -102,6 +102,15 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream=None):
+    """Context in which outputs and workspaces are allocated: the stream the
+    kernels run on, so that torch's caching allocator does not hand a workspace
+    to another stream's allocation while the kernels still use it."""
+    import contextlib
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _check(status: int, what: str):
     if status != 0:
         msg = _lib.dsa_status_string(status).decode()
@@ -126,8 +135,9 @@ def dsa_row_windows(cu_seqlens_q, cu_seqlens_k, n_rows: int, causal: bool = True
     import torch
     lib = _lib_or_load()
     dev = cu_seqlens_q.device
-    rs = torch.empty(n_rows, dtype=torch.int32, device=dev) if row_starts is None else row_starts
-    re = torch.empty(n_rows, dtype=torch.int32, device=dev) if row_ends is None else row_ends
+    with _on(stream):
+        rs = torch.empty(n_rows, dtype=torch.int32, device=dev) if row_starts is None else row_starts
+        re = torch.empty(n_rows, dtype=torch.int32, device=dev) if row_ends is None else row_ends
     _check(lib.dsa_row_windows(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1,
                                n_rows, int(causal), _ptr(rs), _ptr(re), _stream(stream)),
            "dsa_row_windows")
@@ -143,11 +153,12 @@ def dsa_indexer_prep(q_raw, k_raw, w, pos_q=None, pos_k=None, out_dtype=None, ro
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     n_q, H, D = q_raw.shape
     n_k = k_raw.shape[0]
-    q = torch.empty((n_q, H, D), dtype=out_dtype, device=q_raw.device)
-    k = torch.empty((n_k, D), dtype=out_dtype, device=q_raw.device)
-    w_out = torch.empty((n_q, H), dtype=torch.float32, device=q_raw.device)
-    ks = torch.empty(n_k, dtype=torch.float32, device=q_raw.device) \
-        if out_dtype == torch.float8_e4m3fn else None
+    with _on(stream):
+        q = torch.empty((n_q, H, D), dtype=out_dtype, device=q_raw.device)
+        k = torch.empty((n_k, D), dtype=out_dtype, device=q_raw.device)
+        w_out = torch.empty((n_q, H), dtype=torch.float32, device=q_raw.device)
+        ks = torch.empty(n_k, dtype=torch.float32, device=q_raw.device) \
+            if out_dtype == torch.float8_e4m3fn else None
     _check(lib.dsa_indexer_prep(_ptr(q_raw), _ptr(k_raw), _ptr(w), _ptr(pos_q), _ptr(pos_k),
                                 n_q, n_k, H, D, rope_dim, rope_main_dim, rope_theta, eps,
                                 _dtype_code(q), _ptr(q), _ptr(k), _ptr(w_out), _ptr(ks),
@@ -164,7 +175,8 @@ def dsa_indexer_scores(q, k, w, row_starts, row_ends, k_scale=None, scores=None,
     n_k = k.shape[0]
     if scores is None:
         ld = n_k if ld is None else ld
-        scores = torch.full((n_q, ld), float("nan"), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            scores = torch.full((n_q, ld), float("nan"), dtype=torch.float32, device=q.device)
     ld = scores.shape[1]
     _check(lib.dsa_indexer_scores(_ptr(q), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(row_starts),
                                   _ptr(row_ends), n_q, n_k, H, D, _dtype_code(q), _ptr(scores), ld,
@@ -177,9 +189,11 @@ def dsa_topk(scores, row_starts, row_ends, index_topk: int, n_cols=None, out=Non
     lib = _lib_or_load()
     n_q, ld = scores.shape
     n_cols = ld if n_cols is None else n_cols
-    out = torch.empty((n_q, index_topk), dtype=torch.int32, device=scores.device) if out is None else out
     ws_bytes = lib.dsa_topk_workspace_size(n_q, n_cols, index_topk)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device) if ws_bytes else None
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n_q, index_topk), dtype=torch.int32, device=scores.device)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device) if ws_bytes else None
     _check(lib.dsa_topk(_ptr(scores), ld, _ptr(row_starts), _ptr(row_ends), n_q, n_cols,
                         index_topk, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)), "dsa_topk")
     return out
@@ -196,10 +210,12 @@ def dsa_indexer_topk(q, k, w, row_starts, row_ends, index_topk: int, k_scale=Non
     lib = _lib_or_load()
     n_q, H, D = q.shape
     n_k = k.shape[0]
-    out = torch.empty((n_q, index_topk), dtype=torch.int32, device=q.device) if out is None else out
     need = lib.dsa_indexer_topk_workspace_size(n_q, n_k, H, D, _dtype_code(q), index_topk)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n_q, index_topk), dtype=torch.int32, device=q.device)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_indexer_topk(_ptr(q), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(row_starts),
                                 _ptr(row_ends), n_q, n_k, H, D, _dtype_code(q), index_topk,
@@ -220,12 +236,14 @@ def dsa_sparse_mla_fwd(q, kv, topk_idx, sm_scale: float, d_v: int, out=None, lse
     n_q, H, d_qk = q.shape
     n_kv = kv.shape[0]
     K = topk_idx.shape[1]
-    out = torch.empty((n_q, H, d_v), dtype=q.dtype, device=q.device) if out is None else out
-    if lse is None and want_lse:
-        lse = torch.empty((n_q, H), dtype=torch.float32, device=q.device)
     need = lib.dsa_sparse_mla_workspace_size(n_q, H, d_qk, d_v, K, _dtype_code(q))
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n_q, H, d_v), dtype=q.dtype, device=q.device)
+        if lse is None and want_lse:
+            lse = torch.empty((n_q, H), dtype=torch.float32, device=q.device)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(topk_idx), n_q, n_kv, H, d_qk, d_v, K,
                                   sm_scale, _dtype_code(q), _ptr(out), _ptr(lse), _ptr(workspace),

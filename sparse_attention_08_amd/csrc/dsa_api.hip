@@ -163,7 +163,7 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const f
   hipStream_t s = as_stream(stream);
   if (dsa::indexer_topk_fused(n_q, dtype, index_topk))
     return launch_status(dsa::launch_indexer_topk_fused(q, k, k_scale, w, row_starts, row_ends,
-                                                        n_q, n_heads, dtype, index_topk,
+                                                        n_q, n_k, n_heads, dtype, index_topk,
                                                         topk_idx, workspace, s));
   float* scores = static_cast<float*>(workspace);
   hipError_t e = dsa::launch_indexer_scores(q, k, k_scale, w, row_starts, row_ends, n_q, n_k,

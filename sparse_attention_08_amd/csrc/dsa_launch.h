@@ -28,7 +28,8 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
 // Final phase of the split top-k: merge the per-chunk candidates in the
 // workspace (laid out as topksel::Candidates) into topk_idx.
 hipError_t launch_topk_merge(const int32_t* row_starts, const int32_t* row_ends, int64_t n_q,
-                             int32_t K, int32_t* out, void* workspace, hipStream_t stream);
+                             int64_t n_cols, int32_t K, int32_t* out, void* workspace,
+                             hipStream_t stream);
 
 hipError_t launch_indexer_scores(const void* q, const void* k, const float* k_scale,
                                  const float* w, const int32_t* row_starts,
@@ -42,7 +43,8 @@ bool indexer_topk_fused(int64_t n_q, int32_t dtype, int32_t K);
 size_t indexer_topk_fused_workspace_bytes(int64_t n_q, int32_t K);
 hipError_t launch_indexer_topk_fused(const void* q, const void* k, const float* k_scale,
                                      const float* w, const int32_t* row_starts,
-                                     const int32_t* row_ends, int64_t n_q, int32_t n_heads,
+                                     const int32_t* row_ends, int64_t n_q, int64_t n_k,
+                                     int32_t n_heads,
                                      int32_t dtype, int32_t K, int32_t* out, void* workspace,
                                      hipStream_t stream);
 

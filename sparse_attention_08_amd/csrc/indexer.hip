@@ -255,8 +255,9 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
     const int64_t t = t0 + tid;
     int a = 0, b = 0;
     if (t < n_q) {
-      a = row_starts[t];
-      b = row_ends[t];
+      // windows are clamped to the keys [0, n_k)
+      a = max(row_starts[t], 0);
+      b = min(row_ends[t], n_k);
       if (b < a) b = a;
     }
     win[tid] = a;
@@ -315,12 +316,12 @@ __global__ __launch_bounds__(kSplitThreads) void indexer_rowsplit_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const float* __restrict__ w,
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ row_ends, int H,
-    float* __restrict__ scores, int64_t ld, int nsplit) {
+    int n_k, float* __restrict__ scores, int64_t ld, int nsplit) {
   constexpr int kWaves = kSplitThreads / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int64_t t = blockIdx.x;
-  const int a = row_starts[t], b = row_ends[t];
+  const int a = max(row_starts[t], 0), b = min(row_ends[t], n_k);  // clamped to the keys
   if (b <= a) return;
   const int ntiles = (b - a + kKeyTile - 1) / kKeyTile;
   const int i0 = int(int64_t(ntiles) * blockIdx.y / nsplit);
@@ -349,10 +350,10 @@ __global__ __launch_bounds__(kSplitThreads) void indexer_rowsplit_kernel(
 __global__ __launch_bounds__(256) void indexer_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ w,
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ row_ends, int H,
-    int D, float* __restrict__ scores, int64_t ld) {
+    int D, int n_k, float* __restrict__ scores, int64_t ld) {
   extern __shared__ float sm[];  // q[t] (H*D) then w[t] (H)
   const int64_t t = blockIdx.x;
-  const int a = row_starts[t], b = row_ends[t];
+  const int a = max(row_starts[t], 0), b = min(row_ends[t], n_k);  // clamped to the keys
   const int s = a + int(blockIdx.y) * 256 + int(threadIdx.x);
   if (a + int(blockIdx.y) * 256 >= b) return;
   for (int i = threadIdx.x; i < H * D; i += 256) sm[i] = q[t * H * D + i];
@@ -388,7 +389,7 @@ hipError_t launch_mfma(const void* q, const void* k, const float* k_scale, const
     while (nsplit > 1 && int64_t(nsplit) * per_wave > max_tiles) nsplit >>= 1;
     hipLaunchKernelGGL((indexer_rowsplit_kernel<Op, MT>), dim3(unsigned(n_q), nsplit),
                        dim3(kSplitThreads), 0, stream, qb, kb, k_scale, w, rs, re, H,
-                       scores, ld, nsplit);
+                       int(n_k), scores, ld, nsplit);
   } else {
     const int64_t nrb = (n_q + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL((indexer_rows_kernel<Op, MT>), dim3(unsigned(nrb)), dim3(kRowsThreads), 0,
@@ -410,7 +411,7 @@ hipError_t launch_indexer_scores(const void* q, const void* k, const float* k_sc
     const size_t smem = size_t(n_heads) * (head_dim + 1) * sizeof(float);
     hipLaunchKernelGGL(indexer_f32_kernel, dim3(unsigned(n_q), gy), dim3(256), smem, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k), w,
-                       row_starts, row_ends, n_heads, head_dim, scores, ld);
+                       row_starts, row_ends, n_heads, head_dim, int(n_k), scores, ld);
     return hipGetLastError();
   }
   const bool one = n_heads <= 32;

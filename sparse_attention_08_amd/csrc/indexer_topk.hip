@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const float* __restrict__ w,
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ row_ends, int H,
-    int32_t K, int32_t* __restrict__ out, uint32_t* __restrict__ cand_key,
+    int n_k, int32_t K, int32_t* __restrict__ out, uint32_t* __restrict__ cand_key,
     int32_t* __restrict__ cand_col, int32_t* __restrict__ cand_cnt) {
   constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
   __shared__ FusedShared sh;
@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
   const int c = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
-  const int a = row_starts[t];
-  const int b = row_ends[t];
+  const int a = max(row_starts[t], 0);  // windows are clamped to the keys [0, n_k)
+  const int b = min(row_ends[t], n_k);
   const int n = b > a ? b - a : 0;
   const int clen = split_chunk_len(n);
   if (clen == 0 && c != 0) return;
@@ -155,16 +155,16 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
 
 template <class Op, int MT>
 hipError_t launch_fused(const void* q, const void* k, const float* k_scale, const float* w,
-                        const int32_t* rs, const int32_t* re, int64_t n_q, int H, int32_t K,
-                        int32_t* out, void* workspace, hipStream_t stream) {
+                        const int32_t* rs, const int32_t* re, int64_t n_q, int64_t n_k, int H,
+                        int32_t K, int32_t* out, void* workspace, hipStream_t stream) {
   const Candidates cd = Candidates::at(workspace, n_q, K);
   hipLaunchKernelGGL((indexer_topk_chunk_kernel<Op, MT>), dim3(unsigned(n_q), kMaxChunks),
                      dim3(kThreads), 0, stream, static_cast<const uint8_t*>(q),
-                     static_cast<const uint8_t*>(k), k_scale, w, rs, re, H, K, out, cd.key,
-                     cd.col, cd.cnt);
+                     static_cast<const uint8_t*>(k), k_scale, w, rs, re, H, int(n_k), K, out,
+                     cd.key, cd.col, cd.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_merge(rs, re, n_q, K, out, workspace, stream);
+  return launch_topk_merge(rs, re, n_q, n_k, K, out, workspace, stream);
 }
 
 }  // namespace
@@ -179,19 +179,19 @@ size_t indexer_topk_fused_workspace_bytes(int64_t n_q, int32_t K) {
 
 hipError_t launch_indexer_topk_fused(const void* q, const void* k, const float* k_scale,
                                      const float* w, const int32_t* row_starts,
-                                     const int32_t* row_ends, int64_t n_q, int32_t n_heads,
-                                     int32_t dtype, int32_t K, int32_t* out, void* workspace,
-                                     hipStream_t stream) {
+                                     const int32_t* row_ends, int64_t n_q, int64_t n_k,
+                                     int32_t n_heads, int32_t dtype, int32_t K, int32_t* out,
+                                     void* workspace, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
   const bool one = n_heads <= 32;
   if (dtype == 1)
-    return one ? launch_fused<OpBf16, 1>(q, k, nullptr, w, row_starts, row_ends, n_q, n_heads,
+    return one ? launch_fused<OpBf16, 1>(q, k, nullptr, w, row_starts, row_ends, n_q, n_k, n_heads,
                                          K, out, workspace, stream)
-               : launch_fused<OpBf16, 2>(q, k, nullptr, w, row_starts, row_ends, n_q, n_heads,
+               : launch_fused<OpBf16, 2>(q, k, nullptr, w, row_starts, row_ends, n_q, n_k, n_heads,
                                          K, out, workspace, stream);
-  return one ? launch_fused<OpFp8, 1>(q, k, k_scale, w, row_starts, row_ends, n_q, n_heads, K,
+  return one ? launch_fused<OpFp8, 1>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads, K,
                                       out, workspace, stream)
-             : launch_fused<OpFp8, 2>(q, k, k_scale, w, row_starts, row_ends, n_q, n_heads, K,
+             : launch_fused<OpFp8, 2>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads, K,
                                       out, workspace, stream);
 }
 

@@ -16,9 +16,11 @@
 // whole query, so no partial result crosses waves.  Per tile of 32 selected
 // keys:
 //   gather    LDS-DMA (global_load_lds, 16 bytes per lane) of the 32 latent rows
-//             into a row-major LDS tile whose rows are padded to 1168 bytes
-//             (conflict-free 16-byte fragment reads); four tile buffers, the
-//             gather of tile i+2 is issued while tile i is computed;
+//             into an LDS tile: the 512 latent dims of each key in a 1040-byte
+//             slot (slots permuted so that fragment and transposed reads are
+//             free of bank conflicts), the 64 rope dims of all keys piece-major
+//             after them; four tile buffers, the gather of tile i+2 is issued
+//             while tile i is computed;
 //   S^T=K.Q^T v_mfma_f32_32x32x16_bf16 with keys on M and the wave's 32 heads on
 //             N, 36 K-steps; lane l then holds 16 keys of head l%32;
 //   softmax   fp32 in base-2 units (sm_scale * log2 e folded into one multiply)
@@ -38,8 +40,9 @@
 // the MFMAs of S(i).  The row sum adds the bf16-rounded probabilities, so the
 // output is an exact convex combination of value rows up to fp32 accumulation.
 //
-// Split mode writes per-split (normalised output, lse) in fp32 to the workspace;
-// a combine kernel merges them with the log-sum-exp weights.
+// Split mode writes per-split partials to the workspace -- the normalised output
+// in bf16, the lse in fp32 -- and a combine kernel merges them with the
+// log-sum-exp weights.
 // The fp32 kernel (small head dims) is plain VALU code.
 #include <cfloat>
 #include <cmath>
@@ -510,7 +513,7 @@ __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const ui
 // registers per lane.
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
-    const int32_t* __restrict__ idx, int H, int K, float sm_scale,
+    const int32_t* __restrict__ idx, int n_kv, int H, int K, float sm_scale,
     __bf16* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_lse, int nsplit) {
   __shared__ __attribute__((aligned(16))) MlaShared sh;
@@ -558,15 +561,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   // Stage the index slice in LDS (padded with -1 to whole tiles, -1 stored as
   // row 0) with per-tile validity masks, and drop trailing tiles that hold only
   // -1 padding (top-k rows are -1 padded at the end); padding elsewhere is
-  // masked per key.
+  // masked per key.  An entry outside [0, n_kv) is treated as -1, so no gather
+  // reads outside kv.
   {
     int wl = -1;  // last valid position among this wave's loads (wave-uniform)
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int x = tid + u * kThreads;
-      if (x < nx) sh.idx[x] = rv[u] < 0 ? 0 : rv[u];
+      const bool ok = unsigned(rv[u]) < unsigned(n_kv);
+      if (x < nx) sh.idx[x] = ok ? rv[u] : 0;
       // x advances by whole waves: 2 tiles per ballot (the wave is uniform in x < nx)
-      const uint64_t b = __ballot(x < nx && rv[u] >= 0);
+      const uint64_t b = __ballot(x < nx && ok);
       if (x < nx && lane == 0) sh.vmask[x / kKT] = uint32_t(b);
       if (x < nx && lane == 32) sh.vmask[x / kKT] = uint32_t(b >> 32);
       if (b != 0ull) wl = u * kThreads + wave * kWave + 63 - __builtin_clzll(b);
@@ -741,8 +746,9 @@ __global__ __launch_bounds__(kCombineHeads * kWave) void mla_combine_kernel(
 // fp32 inputs: one workgroup per (query, head).
 __global__ __launch_bounds__(128) void mla_f32_kernel(const float* __restrict__ q,
                                                       const float* __restrict__ kv,
-                                                      const int32_t* __restrict__ idx, int H,
-                                                      int K, int dqk, int dv, float sm_scale,
+                                                      const int32_t* __restrict__ idx, int n_kv,
+                                                      int H, int K, int dqk, int dv,
+                                                      float sm_scale,
                                                       float* __restrict__ out,
                                                       float* __restrict__ lse) {
   extern __shared__ float sm[];  // q row [dqk], logits [K], reduction [4]
@@ -760,7 +766,7 @@ __global__ __launch_bounds__(128) void mla_f32_kernel(const float* __restrict__ 
   for (int j = tid; j < K; j += 128) {
     const int r = irow[j];
     float l = -INFINITY;
-    if (r >= 0) {
+    if (unsigned(r) < unsigned(n_kv)) {  // -1 and out-of-range entries are skipped
       const float* kr = kv + int64_t(r) * dqk;
       float dot = 0.0f;
       for (int d = 0; d < dqk; ++d) dot = fmaf(sq[d], kr[d], dot);
@@ -789,7 +795,7 @@ __global__ __launch_bounds__(128) void mla_f32_kernel(const float* __restrict__ 
     float acc = 0.0f;
     for (int j = 0; j < K; ++j) {
       const int r = irow[j];
-      if (r >= 0) acc = fmaf(sl[j], kv[int64_t(r) * dqk + d], acc);
+      if (unsigned(r) < unsigned(n_kv)) acc = fmaf(sl[j], kv[int64_t(r) * dqk + d], acc);
     }
     out[(t * H + h) * int64_t(dv) + d] = acc * inv;
   }
@@ -827,13 +833,12 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
                              int64_t n_kv, int32_t n_heads, int32_t d_qk, int32_t d_v,
                              int32_t K, float sm_scale, int32_t dtype, void* out, float* lse,
                              void* workspace, hipStream_t stream) {
-  (void)n_kv;
   if (n_q == 0) return hipSuccess;
   if (dtype == 0) {
     const size_t smem = (size_t(d_qk) + K + 4) * sizeof(float);
     hipLaunchKernelGGL(mla_f32_kernel, dim3(unsigned(n_q), n_heads), dim3(128), smem, stream,
                        static_cast<const float*>(q), static_cast<const float*>(kv), idx,
-                       n_heads, K, d_qk, d_v, sm_scale, static_cast<float*>(out), lse);
+                       int(n_kv), n_heads, K, d_qk, d_v, sm_scale, static_cast<float*>(out), lse);
     return hipGetLastError();
   }
   const int s = mla_splits(n_q, n_heads, K);
@@ -842,8 +847,8 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
   float* part_lse =
       s > 1 ? reinterpret_cast<float*>(part_o + size_t(n_q) * s * n_heads * d_v) : nullptr;
   hipLaunchKernelGGL(mla_bf16_kernel, dim3(unsigned(n_q), hb, s), dim3(kThreads), 0, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(kv), idx, n_heads,
-                     K, sm_scale, static_cast<__bf16*>(out), lse, part_o, part_lse, s);
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(kv), idx, int(n_kv),
+                     n_heads, K, sm_scale, static_cast<__bf16*>(out), lse, part_o, part_lse, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
   static_assert(kDv == 8 * kWave, "one wave per head row in the combine");

@@ -105,13 +105,13 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64
 template <int CAP>
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
-    const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out, int skip_long,
-    int skip_below) {
+    const int32_t* __restrict__ row_ends, int n_cols, int32_t K, int32_t* __restrict__ out,
+    int skip_long, int skip_below) {
   __shared__ uint32_t keys[CAP];
   __shared__ SelectShared<kThreads> sh;
   const int64_t row = blockIdx.x;
-  const int a = row_starts[row];
-  const int b = row_ends[row];
+  const int a = max(row_starts[row], 0);  // windows are clamped to the columns [0, n_cols)
+  const int b = min(row_ends[row], n_cols);
   const int n = b > a ? b - a : 0;
   if ((skip_long && n > CAP) || n <= skip_below) return;
   row_topk<CAP>(scores, ld, row, a, b, K, out, keys, sh);
@@ -120,15 +120,15 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
 // Split path, phase 1: workgroup (row, c) selects the top-k of chunk c.
 __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
-    const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out,
+    const int32_t* __restrict__ row_ends, int n_cols, int32_t K, int32_t* __restrict__ out,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col,
     int32_t* __restrict__ cand_cnt) {
   __shared__ uint32_t keys[kCap];
   __shared__ SelectShared<kThreads> sh;
   const int64_t row = blockIdx.x;
   const int c = blockIdx.y;
-  const int a = row_starts[row];
-  const int b = row_ends[row];
+  const int a = max(row_starts[row], 0);  // clamped to the columns
+  const int b = min(row_ends[row], n_cols);
   const int n = b > a ? b - a : 0;
   const int clen = split_chunk_len(n);
   if (clen == 0) {
@@ -161,16 +161,17 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
 // the row's top-k with its -1 padding.
 template <int kGroup, int kStride, bool kFinal>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
-    const int32_t* __restrict__ row_starts, const int32_t* __restrict__ row_ends, int32_t K,
-    int32_t* __restrict__ out, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col,
-    int32_t* __restrict__ cand_cnt) {
+    const int32_t* __restrict__ row_starts, const int32_t* __restrict__ row_ends, int n_cols,
+    int32_t K, int32_t* __restrict__ out, uint32_t* __restrict__ cand_key,
+    int32_t* __restrict__ cand_col, int32_t* __restrict__ cand_cnt) {
   __shared__ uint32_t keys[kGroup * kMaxSplitK];
   __shared__ int sel[kMaxSplitK];  // selected candidate positions, then (level 1) their columns
   __shared__ uint32_t skey[kFinal ? 1 : kMaxSplitK];
   __shared__ int off[kGroup + 1];
   __shared__ SelectShared<kMergeThreads> sh;
   const int64_t row = blockIdx.x;
-  const int n_win = row_ends[row] - row_starts[row];
+  // the window as phase 1 clamped it
+  const int n_win = max(min(row_ends[row], n_cols) - max(row_starts[row], 0), 0);
   if (split_chunk_len(n_win) == 0) return;  // written whole by phase 1
   const int64_t slot0 = row * kMaxChunks + int64_t(blockIdx.y) * kGroup * kStride;
   if (threadIdx.x == 0) {
@@ -283,15 +284,15 @@ struct StreamShared {
 
 __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
-    const int32_t* __restrict__ row_ends, int32_t K, int32_t* __restrict__ out) {
+    const int32_t* __restrict__ row_ends, int n_cols, int32_t K, int32_t* __restrict__ out) {
   __shared__ StreamShared sh;
   constexpr int kPer = kPiece / kThreads;  // keys per thread per piece
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int a = row_starts[row];
-  const int b = row_ends[row];
+  const int a = max(row_starts[row], 0);  // clamped to the columns
+  const int b = min(row_ends[row], n_cols);
   const int n = b > a ? b - a : 0;
   const float* src = scores + row * ld + a;
   int32_t* dst = out + row * int64_t(K);
@@ -455,40 +456,43 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
     // windows of at most 4096 keys: the 4096-key instance; longer ones up to
     // kCap (and, without the stream kernel, all longer ones): the kCap instance
     hipLaunchKernelGGL(topk_rows_kernel<4096>, dim3(unsigned(n_q)), dim3(kThreads), 0, stream,
-                       scores, ld, row_starts, row_ends, K, out, 1, -1);
+                       scores, ld, row_starts, row_ends, int(n_cols), K, out, 1, -1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (n_cols > 4096) {
       hipLaunchKernelGGL(topk_rows_kernel<kCap>, dim3(unsigned(n_q)), dim3(kThreads), 0, stream,
-                         scores, ld, row_starts, row_ends, K, out, int(stream_long), 4096);
+                         scores, ld, row_starts, row_ends, int(n_cols), K, out, int(stream_long),
+                         4096);
       e = hipGetLastError();
     }
     if (e != hipSuccess || !stream_long) return e;
     hipLaunchKernelGGL(topk_stream_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
-                       ld, row_starts, row_ends, K, out);
+                       ld, row_starts, row_ends, int(n_cols), K, out);
     return hipGetLastError();
   }
   const Candidates cd = Candidates::at(workspace, n_q, K);
   hipLaunchKernelGGL(topk_chunk_kernel, dim3(unsigned(n_q), kMaxChunks), dim3(kThreads), 0,
-                     stream, scores, ld, row_starts, row_ends, K, out, cd.key, cd.col, cd.cnt);
+                     stream, scores, ld, row_starts, row_ends, int(n_cols), K, out, cd.key, cd.col,
+                     cd.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_merge(row_starts, row_ends, n_q, K, out, workspace, stream);
+  return launch_topk_merge(row_starts, row_ends, n_q, n_cols, K, out, workspace, stream);
 }
 
 hipError_t launch_topk_merge(const int32_t* row_starts, const int32_t* row_ends, int64_t n_q,
-                             int32_t K, int32_t* out, void* workspace, hipStream_t stream) {
+                             int64_t n_cols, int32_t K, int32_t* out, void* workspace,
+                             hipStream_t stream) {
   const Candidates cd = Candidates::at(workspace, n_q, K);
   constexpr int kGroup = 4;  // slots per level-1 merge
   static_assert(kMaxChunks == kGroup * kGroup, "two levels of kGroup-way merges");
   hipLaunchKernelGGL((topk_merge_kernel<kGroup, 1, false>), dim3(unsigned(n_q), kGroup),
-                     dim3(kMergeThreads), 0, stream, row_starts, row_ends, K, out, cd.key, cd.col,
-                     cd.cnt);
+                     dim3(kMergeThreads), 0, stream, row_starts, row_ends, int(n_cols), K, out,
+                     cd.key, cd.col, cd.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((topk_merge_kernel<kGroup, kGroup, true>), dim3(unsigned(n_q), 1),
-                     dim3(kMergeThreads), 0, stream, row_starts, row_ends, K, out, cd.key, cd.col,
-                     cd.cnt);
+                     dim3(kMergeThreads), 0, stream, row_starts, row_ends, int(n_cols), K, out,
+                     cd.key, cd.col, cd.cnt);
   return hipGetLastError();
 }
 

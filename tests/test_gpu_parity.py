@@ -15,7 +15,7 @@ from oracle import mla as o_mla
 from oracle import prep as o_prep
 from oracle import topk as o_topk
 from oracle import windows as o_win
-from parity import check_mla, check_scores, check_topk_e2e, dev, host, i32, say
+from parity import check_mla, check_scores, check_topk_e2e, dev, host, i32, mla_lse_tol, say
 
 pytestmark = pytest.mark.gpu
 
@@ -393,14 +393,17 @@ def _random_topk_rows(g, n_q, n_kv, K, windows=None, holes=False):
     return out
 
 
-def _mla_case(dsa, q, kv, idx, sm, d_v, bf16, what, rows=None):
+def _mla_case(dsa, q, kv, idx, sm, d_v, bf16, what, rows=None, oracle_idx=None):
+    """oracle_idx: the selection the oracle reads (default idx); the kernel reads idx."""
     tdt = torch.bfloat16 if bf16 else torch.float32
     qd, kvd = dev(q, tdt), dev(kv, tdt)
     say(f"mla {what}: n_q={q.shape[0]} H={q.shape[1]} n_kv={kv.shape[0]} K={idx.shape[1]}")
     out, lse = dsa.dsa_sparse_mla_fwd(qd, kvd, i32(idx), sm, d_v)
-    rows = range(q.shape[0]) if rows is None else list(rows)
-    oo, ol = o_mla.sparse_mla(q, kv, idx, sm, d_v, rows=rows)
-    err = check_mla(host(out)[rows], oo, host(lse)[rows], ol, bf16, what)
+    rows = list(range(q.shape[0])) if rows is None else list(rows)
+    oidx = idx if oracle_idx is None else oracle_idx
+    oo, ol = o_mla.sparse_mla(q, kv, oidx, sm, d_v, rows=rows)
+    tol = mla_lse_tol(q[rows], kv, oidx[rows], sm, bf16, ol)
+    err = check_mla(host(out)[rows], oo, host(lse)[rows], ol, bf16, what, lse_tol=tol)
     say(f"  max abs err {err:.2e}")
 
 
@@ -436,9 +439,10 @@ def test_mla_bf16_peaky_and_split(dsa):
 
 def test_mla_bf16_large_logit_growth(dsa):
     # The logits rise by ~200 along the (ascending) key order while staying smooth
-    # near the top (noise std ~0.5): far beyond the slack over a first-tile
-    # reference max, so the affected (query, head group) slices take the exact
-    # recomputation path.  The trend lives in a rope dim, so values stay ~N(0, 0.01).
+    # near the top (noise std ~0.5): far beyond the 2^32 slack over the first
+    # tile's max that the softmax reference allows, so the workgroup runs its
+    # query a second time against the true max.  The trend lives in a rope dim,
+    # so values stay ~N(0, 0.01).
     g = np.random.default_rng(204)
     n_kv = 4096
     kv = synth.mla_kv(P4K, 0, n_kv)
@@ -451,6 +455,47 @@ def test_mla_bf16_large_logit_growth(dsa):
         idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk)
         _mla_case(dsa, q, kv, idx, P4K.sm_scale, P4K.d_v, True, f"bf16 logit growth {what}",
                   rows=range(0, n_q, 3))
+
+
+@pytest.mark.parametrize("n_q,what", [(12, "split"), (200, "one workgroup per query")])
+def test_mla_bf16_extreme_logits(dsa, n_q, what):
+    # Logits of several hundred to ~2000 natural units (q scaled by 8000, value
+    # rows scaled by 0.2 .. 3 along the cache): lse ~ 500 .. 1400, and a later
+    # tile's max far above the first tile's, on the split path (few queries) and
+    # on the one-workgroup-per-query launch.
+    g = np.random.default_rng(205)
+    n_kv = 4096
+    kv = synth.mla_kv(P4K, 0, n_kv) * np.linspace(0.2, 3.0, n_kv, dtype=np.float32)[:, None]
+    kv = o_prep.round_bf16(kv)
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q) * 8000.0)
+    idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk)
+    _mla_case(dsa, q, kv, idx, P4K.sm_scale, P4K.d_v, True, f"bf16 extreme logits {what}",
+              rows=range(0, n_q, 1 if n_q < 50 else 7))
+
+
+@pytest.mark.parametrize("n_q", [10, 300])
+def test_mla_out_of_range_indices_are_skipped(dsa, n_q):
+    # entries outside [0, n_kv) are skipped like -1: never gathered
+    g = np.random.default_rng(206)
+    n_kv = 900
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q))
+    kv = o_prep.round_bf16(synth.mla_kv(P4K, 0, n_kv))
+    idx = _random_topk_rows(g, n_q, n_kv, 512, holes=True)
+    bad = idx.copy()
+    pos = g.random(idx.shape) < 0.1
+    junk = g.choice(np.array([n_kv, n_kv + 1, 2 ** 31 - 1, -2, -(2 ** 31)], np.int64), idx.shape)
+    bad[pos] = junk[pos].astype(np.int32)
+    bad[0, :] = n_kv + 5                                  # nothing in range: out 0, lse -inf
+    oracle_idx = np.where((bad >= 0) & (bad < n_kv), bad, -1).astype(np.int32)
+    _mla_case(dsa, q, kv, bad, P4K.sm_scale, P4K.d_v, True, f"bf16 out-of-range n_q={n_q}",
+              oracle_idx=oracle_idx)
+    qf = o_prep.round_f32(synth.mla_q(TINY, 0, 40))
+    kvf = o_prep.round_f32(synth.mla_kv(TINY, 0, 50))
+    idf = _random_topk_rows(g, 40, 50, 16, holes=True)
+    idf[::3, 2] = 50
+    idf[1::3, 5] = -7
+    _mla_case(dsa, qf, kvf, idf, TINY.sm_scale, TINY.d_v, False, "f32 out-of-range",
+              oracle_idx=np.where((idf >= 0) & (idf < 50), idf, -1).astype(np.int32))
 
 
 def test_mla_bf16_fewer_heads(dsa):
@@ -503,3 +548,85 @@ def test_indexer_prep(dsa, dtype):
         assert np.mean(mism) < 0.01
         step = np.exp2(np.floor(np.log2(np.maximum(np.abs(p["k"]), 2.0 ** -6))) - 3)
         assert np.all(np.abs(gk - p["k"])[mism] <= step[mism] * 1.0001)
+
+
+# ---------------------------------------------------------------------------
+# windows outside the keys are clamped to [0, n_k]; a caller's stream is used
+# ---------------------------------------------------------------------------
+def _clamp(rs, re, n):
+    a = np.clip(rs, 0, None)
+    b = np.minimum(re, n)
+    return a.astype(np.int32), np.maximum(a, b).astype(np.int32)
+
+
+@pytest.mark.parametrize("n_q", [40, 600])
+def test_windows_clamped_to_keys(dsa, n_q):
+    # row-split (few rows) and row-block indexer kernels, the top-k rows and
+    # split paths, and the fused indexer + top-k: windows that start below 0 or
+    # end past the last key behave as their clamped windows
+    g = np.random.default_rng(301)
+    lay = synth.layout_from_lengths([1500] if n_q == 600 else [1500], decode=False)
+    p, _, _ = canonical_indexer(P4K, lay, "bf16", rope=False)
+    n_k = lay.n_k
+    p = dict(p, q=p["q"][:n_q], w=p["w"][:n_q])
+    rs = g.integers(-3000, n_k, n_q).astype(np.int32)
+    re = (rs + g.integers(0, 4000, n_q)).astype(np.int32)
+    rs[:4] = [-(2 ** 31), 0, n_k - 1, n_k + 7]
+    re[:4] = [2 ** 31 - 1, n_k + 1, n_k + 9000, n_k + 9]
+    ca, cb = _clamp(rs, re, n_k)
+    q, k, wt, _ = to_device_indexer(p, "bf16")
+    say(f"clamped windows n_q={n_q} n_k={n_k}")
+    G = host(dsa.dsa_indexer_scores(q, k, wt, i32(rs), i32(re)))
+    Gc = host(dsa.dsa_indexer_scores(q, k, wt, i32(ca), i32(cb)))
+    np.testing.assert_array_equal(np.isnan(G), np.isnan(Gc))
+    np.testing.assert_array_equal(G[~np.isnan(G)], Gc[~np.isnan(Gc)])
+    for t in range(0, n_q, 13):
+        a, b = int(ca[t]), int(cb[t])
+        if b > a:
+            o, c = o_idx.score_row(p["q"][t], p["k"][a:b], p["w"][t], with_cond=True)
+            check_scores(G[t, a:b], o, c, 2e-2, f"clamped row {t}")
+    S = np.where(np.isnan(Gc), np.float32(-1e4), Gc).astype(np.float32)
+    for K in (64, 2048):
+        got = host(dsa.dsa_topk(dev(S), i32(rs), i32(re), K))
+        np.testing.assert_array_equal(got, o_topk.topk(S, ca, cb, K))
+        fused = host(dsa.dsa_indexer_topk(q, k, wt, i32(rs), i32(re), K))
+        ref = host(dsa.dsa_indexer_topk(q, k, wt, i32(ca), i32(cb), K))
+        np.testing.assert_array_equal(fused, ref)
+    # the split path of dsa_topk (few rows over more than 8192 columns)
+    n = 20000
+    S2 = g.standard_normal((12, n)).astype(np.float32)
+    rs2 = np.array([-5, 0, 100, 19999, -100000, 5, 0, 0, 7, 8, 9, 10], np.int32)
+    re2 = np.array([n + 3, 9000, 30000, 40000, 2 ** 31 - 1, 4, 0, n, 8193, 8200, 200, 12000],
+                   np.int32)
+    a2, b2 = _clamp(rs2, re2, n)
+    assert dsa._lib_or_load().dsa_topk_workspace_size(12, n, 2048) > 0
+    np.testing.assert_array_equal(host(dsa.dsa_topk(dev(S2), i32(rs2), i32(re2), 2048)),
+                                  o_topk.topk(S2, a2, b2, 2048))
+
+
+def test_calls_on_a_caller_stream(dsa):
+    # every entry point enqueued on a non-default stream, with its workspace and
+    # outputs allocated by the binding for that stream; results match the
+    # default-stream calls
+    g = np.random.default_rng(302)
+    lay = synth.layout_from_lengths([20000], decode=True)
+    lay2 = synth.layout_from_lengths([700, 20000, 9000], decode=True)
+    p, rs, re = canonical_indexer(P4K, lay2, "bf16", rope=False)
+    q, k, wt, _ = to_device_indexer(p, "bf16")
+    mq = dev(o_prep.round_bf16(synth.mla_q(P4K, 0, 3)), torch.bfloat16)
+    mkv = dev(o_prep.round_bf16(synth.mla_kv(P4K, 0, lay2.n_k)), torch.bfloat16)
+    base_idx = dsa.dsa_indexer_topk(q, k, wt, i32(rs), i32(re), 2048)
+    base_out, base_lse = dsa.dsa_sparse_mla_fwd(mq, mkv, base_idx, P4K.sm_scale, P4K.d_v)
+    S = dsa.dsa_indexer_scores(q, k, wt, i32(rs), i32(re))
+    base_top = dsa.dsa_topk(S, i32(rs), i32(re), 2048)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    rsd, red = i32(rs), i32(re)
+    torch.cuda.synchronize()
+    idx = dsa.dsa_indexer_topk(q, k, wt, rsd, red, 2048, stream=s)
+    top = dsa.dsa_topk(S, rsd, red, 2048, stream=s)
+    out, lse = dsa.dsa_sparse_mla_fwd(mq, mkv, idx, P4K.sm_scale, P4K.d_v, stream=s)
+    s.synchronize()
+    assert torch.equal(idx, base_idx) and torch.equal(top, base_top)
+    assert torch.equal(out, base_out) and torch.equal(lse, base_lse)
+    del lay, g
