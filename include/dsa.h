@@ -203,6 +203,31 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_indexer_topk_noalloc -- dsa_indexer_topk without a workspace argument.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same operands,
+ * semantics and kernels as dsa_indexer_topk; the workspace that call would
+ * need comes from a device array inside the library, DSA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) on each GPU, held from library load until the process ends.  The
+ * call allocates nothing.
+ *   - The stream must belong to the current device (the array of that device
+ *     is used; its address is looked up on the first call on each device).
+ *   - Returns DSA_ERR_WORKSPACE, enqueueing nothing, when the workspace
+ *     dsa_indexer_topk_workspace_size(...) reports exceeds the array (e.g. more
+ *     than 255 rows of windows longer than 8192 keys at index_topk = 2048).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind (no call relies on them): calls that overlap in time on one GPU
+ *     (two streams, two threads) race and give undefined results.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dsa_indexer_topk_noalloc(const void* q, const void* k, const float* k_scale,
+                             const float* w, const int32_t* row_starts,
+                             const int32_t* row_ends, int64_t n_q, int64_t n_k,
+                             int32_t n_heads, int32_t head_dim, int32_t dtype,
+                             int32_t index_topk, int32_t* topk_idx, void* stream);
+
+/*
  * dsa_sparse_mla_fwd -- MLA attention over the selected latent rows only.
  *
  * Passage: the vLLM API page "vllm.models.kimi_k3.nvidia.dsa" (module text and

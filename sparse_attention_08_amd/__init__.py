@@ -67,6 +67,8 @@ def _declare(lib):
         "dsa_indexer_topk_workspace_size": (SZ, [I64, I64, I32, I32, I32, I32]),
         "dsa_indexer_topk": (ctypes.c_int, [P, P, P, P, P, P, I64, I64, I32, I32, I32, I32, P, P,
                                             SZ, P]),
+        "dsa_indexer_topk_noalloc": (ctypes.c_int, [P, P, P, P, P, P, I64, I64, I32, I32, I32,
+                                                    I32, P, P]),
         "dsa_sparse_mla_workspace_size": (SZ, [I64, I32, I32, I32, I32, I32]),
         "dsa_sparse_mla_fwd": (ctypes.c_int, [P, P, P, I64, I64, I32, I32, I32, I32, F32, I32, P, P,
                                               P, SZ, P]),
@@ -79,7 +81,7 @@ def _declare(lib):
 
 EXPORTS = ("dsa_status_string", "dsa_version", "dsa_row_windows", "dsa_indexer_prep",
            "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
-           "dsa_indexer_topk_workspace_size", "dsa_indexer_topk",
+           "dsa_indexer_topk_workspace_size", "dsa_indexer_topk", "dsa_indexer_topk_noalloc",
            "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd")
 
 
@@ -221,6 +223,24 @@ def dsa_indexer_topk(q, k, w, row_starts, row_ends, index_topk: int, k_scale=Non
                                 _ptr(row_ends), n_q, n_k, H, D, _dtype_code(q), index_topk,
                                 _ptr(out), _ptr(workspace), nbytes, _stream(stream)),
            "dsa_indexer_topk")
+    return out
+
+
+def dsa_indexer_topk_noalloc(q, k, w, row_starts, row_ends, index_topk: int, k_scale=None,
+                             out=None, stream=None):
+    """dsa_indexer_topk with the library's own scratch array as its workspace
+    (no device allocation by the library; out is allocated here unless given)."""
+    import torch
+    lib = _lib_or_load()
+    n_q, H, D = q.shape
+    n_k = k.shape[0]
+    if out is None:
+        with _on(stream):
+            out = torch.empty((n_q, index_topk), dtype=torch.int32, device=q.device)
+    _check(lib.dsa_indexer_topk_noalloc(_ptr(q), _ptr(k), _ptr(k_scale), _ptr(w),
+                                        _ptr(row_starts), _ptr(row_ends), n_q, n_k, H, D,
+                                        _dtype_code(q), index_topk, _ptr(out), _stream(stream)),
+           "dsa_indexer_topk_noalloc")
     return out
 
 

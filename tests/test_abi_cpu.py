@@ -134,3 +134,12 @@ def test_windows_and_prep_reject_bad_arguments(lib):
     assert lib.dsa_indexer_prep(*a) == INVALID                      # odd rope_dim
     a[9] = 64; a[13] = 2
     assert lib.dsa_indexer_prep(*a) == INVALID                      # fp8 needs k_scale_out
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_array(lib):
+    # 1000 decode rows over long windows need 1000 * 16 * 2048 * 8 + ... bytes of
+    # candidates, more than the 64 MiB array: refused before any device call
+    need = lib.dsa_indexer_topk_workspace_size(1000, 100000, 64, 128, 1, 2048)
+    assert need > (64 << 20)
+    assert lib.dsa_indexer_topk_noalloc(FAKE, FAKE, None, FAKE32, FAKE, FAKE, 1000, 100000, 64,
+                                        128, 1, 2048, FAKE, None) == WORKSPACE
