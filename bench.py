@@ -116,7 +116,7 @@ def stage_bench(args, dsa, synth, np, torch):
     and every standalone top-k) get a 1 GiB write between repetitions so that
     their inputs are not served from the 256 MB last-level cache."""
     dev = "cuda"
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[args.workload.replace("_stages", "")]
     lay = synth.layout(w)
     i32 = lambda x: torch.from_numpy(np.asarray(x, np.int32)).to(dev)
     inp = synth.device_inputs(w, dev, lay)
@@ -148,7 +148,7 @@ def stage_bench(args, dsa, synth, np, torch):
         "mla": lambda: dsa.dsa_sparse_mla_fwd(mq, mkv, idx, w.sm_scale, w.d_v, out=out, lse=lse,
                                               workspace=ws),
     }
-    fused = lay.n_q <= 1024          # decode shape: the fused indexer + top-k applies
+    fused = True                     # the fused indexer + top-k: decode and prefill kernels
     if fused:
         idx2 = torch.empty_like(idx)
         code = 1 if w.dtype == "bf16" else 2
@@ -156,7 +156,7 @@ def stage_bench(args, dsa, synth, np, torch):
                                                          code, K), 1), dtype=torch.uint8, device=dev)
         fns["indexer_topk"] = lambda: dsa.dsa_indexer_topk(q, k, wt, rs, re, K, k_scale=ks, out=idx2,
                                                            workspace=fws)
-        hbm_bound["indexer_topk"] = True
+        hbm_bound["indexer_topk"] = w.decode
     ms = {}
     for name in fns:
         f = fns[name]
@@ -206,16 +206,23 @@ def stage_bench(args, dsa, synth, np, torch):
         fb = idx_bytes - pairs * 4 + lay.n_q * K * 4       # q + k + w read, indices written
         comp["indexer_topk_fused"] = {"ms": ms["indexer_topk"],
                                       "pairs_per_s": pairs / t["indexer_topk"],
+                                      "tflops": idx_flop / t["indexer_topk"] / 1e12,
+                                      "frac_mfma_peak": idx_flop / t["indexer_topk"] / 1e12 / mfma_peak,
                                       "gbs": fb / t["indexer_topk"] / 1e9,
-                                      "frac_hbm": fb / t["indexer_topk"] / 1e9 / HBM_PEAK_GBS}
+                                      "frac_hbm": fb / t["indexer_topk"] / 1e9 / HBM_PEAK_GBS,
+                                      "vs_unfused": (ms["indexer"] + ms["topk"]) / ms["indexer_topk"]}
         ms_path = {"indexer_topk": ms["indexer_topk"], "mla": ms["mla"]}
     else:
         ms_path = {"indexer": ms["indexer"], "topk": ms["topk"], "mla": ms["mla"]}
     dom = max(ms_path, key=ms_path.get)
-    if dom == "indexer_topk":
+    if dom == "indexer_topk" and w.decode:
         ach = comp["indexer_topk_fused"]["gbs"]
         roof = {"kernel": "indexer_topk_chunk_kernel", "bound": "hbm", "achieved": ach,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    elif dom == "indexer_topk":
+        ach = comp["indexer_topk_fused"]["tflops"]
+        roof = {"kernel": "indexer_topk_rows_kernel", "bound": "mfma", "achieved": ach,
+                "peak": mfma_peak, "unit": "TFLOP/s", "frac": ach / mfma_peak, "traffic": None}
     elif dom == "indexer" and not w.decode:
         ach = comp["indexer"]["tflops"]
         roof = {"kernel": "indexer_rows_kernel", "bound": "mfma", "achieved": ach, "peak": mfma_peak,
@@ -257,7 +264,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="prefill4k", choices=["prefill4k", "thd", "decode", "fp8_64k"],
+    ap.add_argument("--workload", default="prefill4k",
+                    choices=["prefill4k", "prefill4k_stages", "thd", "decode", "fp8_64k"],
                     help="prefill4k: the benchmark step; the others time each stage on its own")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -185,12 +185,17 @@ int dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_starts,
  * not an output.  workspace: at least dsa_indexer_topk_workspace_size(...) bytes,
  * 256-byte aligned (NULL when that size is 0); its contents on entry do not
  * matter.
- *   Few rows (n_q <= 1024, bf16 or fp8, index_topk <= 2048; decode): fused --
- *   scores are computed into LDS per (row, key chunk) and reduced there to
- *   candidates, so they never reach memory; the workspace holds the candidates
- *   (n_q * 16 * index_topk * 8 + n_q * 64 bytes, 0 when n_k <= 8192).
- *   Otherwise the scores go through the workspace (n_q * n_k * 4 bytes, plus
- *   dsa_topk's workspace).
+ * The scores never reach memory for bf16 and fp8 with index_topk <= 2048:
+ *   More than 256 rows (prefill): fused, no workspace -- four rows per
+ *   workgroup share each chunk of keys, and each row keeps its candidates
+ *   (scores above a running floor, shrunk in place to their exact top k when
+ *   full) in LDS.
+ *   At most 256 rows (decode): fused -- scores are computed into LDS per (row,
+ *   key chunk) and reduced there to candidates; the workspace holds the
+ *   candidates (n_q * 16 * index_topk * 8 + n_q * 64 bytes, 0 when
+ *   n_k <= 8192).
+ * Otherwise (F32, or index_topk > 2048) the scores go through the workspace
+ * (n_q * n_k * 4 bytes, plus dsa_topk's workspace).
  */
 size_t dsa_indexer_topk_workspace_size(int64_t n_q, int64_t n_k, int32_t n_heads,
                                        int32_t head_dim, int32_t dtype,

@@ -16,8 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_api.hip", "topk.hip", "indexer.hip", "indexer_topk.hip", "mla.hip", "prep.hip",
-           "noalloc.hip"]
+SOURCES = ["dsa_api.hip", "topk.hip", "indexer.hip", "indexer_topk.hip", "indexer_topk_rows.hip",
+           "mla.hip", "prep.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON = [

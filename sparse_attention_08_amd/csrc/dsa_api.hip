@@ -52,6 +52,12 @@ int check_topk(const float* scores, int64_t ld, const int32_t* rs, const int32_t
   return DSA_OK;
 }
 
+// Many rows (prefill): four rows per workgroup share each key chunk and keep
+// their candidates in LDS; few rows (decode) split each window over workgroups.
+bool fused_rows(int64_t n_q, int32_t dtype, int32_t K) {
+  return n_q > 256 && dsa::indexer_topk_rows_applies(dtype, K);
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,6 +144,7 @@ size_t dsa_indexer_topk_workspace_size(int64_t n_q, int64_t n_k, int32_t n_heads
   (void)n_heads;
   (void)head_dim;
   if (n_q <= 0 || n_k <= 0 || index_topk < 1) return 0;
+  if (fused_rows(n_q, dtype, index_topk)) return 0;
   if (dsa::indexer_topk_fused(n_q, dtype, index_topk))
     return n_k > 8192 ? dsa::indexer_topk_fused_workspace_bytes(n_q, index_topk) : 0;
   // the score matrix, then the top-k's own workspace (256-byte aligned)
@@ -161,6 +168,10 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const f
     return DSA_ERR_WORKSPACE;
   if (n_q == 0) return DSA_OK;
   hipStream_t s = as_stream(stream);
+  if (fused_rows(n_q, dtype, index_topk))
+    return launch_status(dsa::launch_indexer_topk_rows(q, k, k_scale, w, row_starts, row_ends,
+                                                       n_q, n_k, n_heads, dtype, index_topk,
+                                                       topk_idx, s));
   if (dsa::indexer_topk_fused(n_q, dtype, index_topk))
     return launch_status(dsa::launch_indexer_topk_fused(q, k, k_scale, w, row_starts, row_ends,
                                                         n_q, n_k, n_heads, dtype, index_topk,

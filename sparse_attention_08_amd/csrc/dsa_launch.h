@@ -48,6 +48,15 @@ hipError_t launch_indexer_topk_fused(const void* q, const void* k, const float* 
                                      int32_t dtype, int32_t K, int32_t* out, void* workspace,
                                      hipStream_t stream);
 
+// Fused indexer + top-k for many rows (prefill): the rows' candidates stay in
+// LDS, no workspace.
+bool indexer_topk_rows_applies(int32_t dtype, int32_t K);
+hipError_t launch_indexer_topk_rows(const void* q, const void* k, const float* k_scale,
+                                    const float* w, const int32_t* row_starts,
+                                    const int32_t* row_ends, int64_t n_q, int64_t n_k,
+                                    int32_t n_heads, int32_t dtype, int32_t K, int32_t* out,
+                                    hipStream_t stream);
+
 size_t mla_workspace_bytes(int64_t n_q, int32_t n_heads, int32_t d_qk, int32_t d_v,
                            int32_t index_topk, int32_t dtype);
 

@@ -35,6 +35,7 @@ namespace {
 
 using ixcore::OpBf16;
 using ixcore::OpFp8;
+using ixcore::PendingTile;
 using ixcore::QueryRow;
 using ixcore::kKeyTile;
 
@@ -48,89 +49,8 @@ constexpr int kRowsPerBlock = 8;
 constexpr int kRowsThreads = kRowsPerBlock * kWave;
 constexpr int kChunkKeys = 256;
 constexpr int kChunkTiles = kChunkKeys / kKeyTile;
-
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// LDS position (in 16-byte pieces) of piece cc of local key kl.
 template <class Op>
-__device__ __forceinline__ int swz(int kl, int cc) {
-  return Op::kRowBytes == 256 ? (cc ^ (kl & 15)) : (cc ^ ((kl >> 1) & 7));
-}
-
-// Chunk DMA.  Wave w issues the 1 KB loads j = w, w + 8, ...; load j covers the
-// kKeysPerLoad keys from j * kKeysPerLoad, and lane l moves piece l % kPieces of
-// key l / kPieces into LDS slot j * 64 + l.  The piece's source position in the
-// key row (the swizzle) depends on the key only through key & 15 (bf16) or
-// (key >> 1) & 7 (fp8), which for every load of a wave is the same per lane, so
-// the lane part of the source address is one fixed offset and each load only
-// moves a wave-uniform base (global_load_lds with an SGPR base).
-template <class Op>
-struct ChunkDma {
-  static constexpr int kPieces = Op::kRowBytes / 16;      // per key
-  static constexpr int kKeysPerLoad = kWave / kPieces;    // keys per 1 KB wave load
-  static constexpr int kLoads = kChunkKeys / kKeysPerLoad;  // wave loads per chunk
-  static_assert(kLoads % kRowsPerBlock == 0, "every wave issues the same loads");
-  int lane_off;  // byte offset of this lane's piece from the load's first key row
-
-  __device__ __forceinline__ ChunkDma(int wave, int lane) {
-    const int kl = wave * kKeysPerLoad + lane / kPieces;  // local key of load j = wave
-    lane_off = (lane / kPieces) * Op::kRowBytes + swz<Op>(kl, lane % kPieces) * 16;
-  }
-
-  __device__ __forceinline__ void issue(uint8_t* buf, const uint8_t* __restrict__ k, int key0,
-                                        int n_k, int wave, int lane) const {
-    if (key0 + kChunkKeys <= n_k) {
-#pragma unroll
-      for (int u = 0; u < kLoads / kRowsPerBlock; ++u) {
-        const int j = wave + kRowsPerBlock * u;
-        const uint8_t* base = k + (int64_t(key0) + j * kKeysPerLoad) * Op::kRowBytes;
-        // asm: a compiler-issued LDS-DMA would turn every later LDS wait into a
-        // full drain; the chunk's only wait is the explicit one in rows_chunk
-        asm volatile("global_load_lds_dwordx4 %0, %1 offset:0"
-                     :
-                     : "v"(lane_off), "s"(base), "{m0}"(ixcore::lds_addr(buf + j * kWave * 16))
-                     : "memory");
-      }
-      return;
-    }
-    // the last chunk runs past the keys: lanes past the end read the last key
-    // (lane laundered so that none of this is hoisted out of the chunk loop)
-    asm volatile("" : "+v"(lane));
-#pragma unroll
-    for (int u = 0; u < kLoads / kRowsPerBlock; ++u) {
-      const int j = wave + kRowsPerBlock * u;
-      const int kl = j * kKeysPerLoad + lane / kPieces;
-      int key = key0 + kl;
-      key = key < n_k ? key : n_k - 1;
-      const uint8_t* src = k + int64_t(key) * Op::kRowBytes + swz<Op>(kl, lane % kPieces) * 16;
-      asm volatile("global_load_lds_dwordx4 %0, off"
-                   :
-                   : "v"(src), "{m0}"(ixcore::lds_addr(buf + j * kWave * 16))
-                   : "memory");
-    }
-  }
-};
-
-// K fragments of one 32-key tile (local keys kt*32 .. +32) from a chunk buffer.
-template <class Op>
-__device__ __forceinline__ void load_kfrags(const uint8_t* buf, int kt, int lane,
-                                            typename Op::frag_t (&kb)[Op::kSteps]) {
-  const int kl = kt * kKeyTile + (lane & 31);
-  const uint8_t* row = buf + kl * Op::kRowBytes;
-  constexpr int kFragPieces = Op::kFragBytes / 16;
-#pragma unroll
-  for (int st = 0; st < Op::kSteps; ++st) {
-    const int cc = (2 * st + (lane >> 5)) * kFragPieces;
-    if constexpr (kFragPieces == 1) {
-      kb[st] = *reinterpret_cast<const typename Op::frag_t*>(row + swz<Op>(kl, cc) * 16);
-    } else {
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + swz<Op>(kl, cc) * 16);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(row + swz<Op>(kl, cc + 1) * 16);
-      kb[st] = __builtin_bit_cast(typename Op::frag_t,
-                                  __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  }
-}
+using RowsDma = ixcore::ChunkDma<Op, kRowsPerBlock, kChunkKeys>;
 
 // Two chunk buffers as separate LDS objects, so that the compiler can tell the
 // in-flight LDS-DMA target apart from the buffer being read (it then inserts no
@@ -156,36 +76,6 @@ __device__ __forceinline__ void store_scores(__amdgpu_buffer_rsrc_t row, int a, 
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p), row, off, 0, 0);
 }
 
-// A wave's tiles go through its matrix core in pairs (A, B), with one tile
-// pending across pairs: the MFMAs of A run beside the ReLU / weight epilogue of
-// the pending tile, the MFMAs of B beside that of A, and B is left pending.  So
-// one wave keeps both the matrix core and the VALU busy instead of leaving the
-// overlap to the other wave of its SIMD.  The pending logits always sit in the
-// same registers between pairs.
-template <class Op, int MT>
-struct PendingTile {
-  f32x16_t acc[MT];
-  int s0 = 0;         // first key of the tile
-  float ksc = 1.0f;   // the lane's key scale (fp8)
-  bool live = false;
-};
-
-// Order of one pair half: each MFMA followed by kV VALU operations of the other
-// tile's epilogue.  With kDsStep > 0, the kDsStep fragment reads of step st of
-// the second tile follow the last MFMA that uses step st of the first (MFMA i
-// is step i / MT), so the second tile's fragments can take the first's
-// registers.
-template <int kMf, int kV, int MT, int kDsStep, int I = 0>
-__device__ __forceinline__ void sched_mfma_valu() {
-  if constexpr (I < kMf) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);  // kV VALU
-    if constexpr (kDsStep > 0 && I % MT == MT - 1)
-      __builtin_amdgcn_sched_group_barrier(0x100, kDsStep, 0);  // DS reads
-    sched_mfma_valu<kMf, kV, MT, kDsStep, I + 1>();
-  }
-}
-
 // Scores of one wave's row over chunk c (keys key0 .. key0+255), which sits in
 // buffer kCur; the DMA of chunk c+1 goes to the other buffer kNn.
 template <class Op, int MT, int kCur, int kNn>
@@ -194,46 +84,15 @@ __device__ __forceinline__ void rows_chunk(int c, int nchunks, int key0, int hi,
                                            const float* __restrict__ k_scale,
                                            const QueryRow<Op, MT>& qr, bool active, int a, int b,
                                            __amdgpu_buffer_rsrc_t srow, int wave, int lane,
-                                           const ChunkDma<Op>& dma, PendingTile<Op, MT>& pd) {
-  constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
-  // per-lane key scales of this chunk, read before the next DMA is issued so that
-  // waiting for them never waits for that DMA
+                                           const RowsDma<Op>& dma, PendingTile<Op, MT>& pd) {
   float ksc[kChunkTiles];
-#pragma unroll
-  for (int kt = 0; kt < kChunkTiles; ++kt) {
-    const int s = key0 + kt * kKeyTile + (lane & 31);
-    ksc[kt] = (kScaled && k_scale != nullptr && s < hi) ? k_scale[s] : 1.0f;
-  }
+  ixcore::chunk_key_scales<Op, kChunkKeys>(k_scale, key0, hi, lane, ksc);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA pieces of chunk c landed
   __syncthreads();                // ... everyone's; all waves are done with chunk c-1
   if (c + 1 < nchunks) dma.issue(kbuf<kNn>(), k, key0 + kChunkKeys, n_k, wave, lane);
   if (!active || key0 >= b || key0 + kChunkKeys <= a) return;
-  constexpr int kMf = Op::kSteps * MT;                   // MFMAs per tile
-  constexpr int kDs = Op::kSteps * (Op::kFragBytes / 16);  // fragment reads per tile
-  constexpr int kV = (32 * MT + kMf - 1) / kMf;          // epilogue VALU per MFMA
   auto put = [&](int s0, float p, float ks) { store_scores(srow, a, s0, lane, p * ks); };
-#pragma unroll
-  for (int pr = 0; pr < kChunkTiles / 2; ++pr) {
-    const int sA = key0 + 2 * pr * kKeyTile;
-    if (sA >= b || sA + 2 * kKeyTile <= a) continue;
-    typename Op::frag_t kA[Op::kSteps], kB[Op::kSteps];
-    load_kfrags<Op>(kbuf<kCur>(), 2 * pr, lane, kA);
-    load_kfrags<Op>(kbuf<kCur>(), 2 * pr + 1, lane, kB);
-    f32x16_t acc1[MT];
-    qr.mma(kA, acc1);
-    const float pP = qr.epilogue(pd.acc);
-    __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // tile A's fragments
-    __builtin_amdgcn_sched_group_barrier(0x002, 2 * kV, 0);
-    sched_mfma_valu<kMf, kV, MT, kDs / Op::kSteps>();
-    if (pd.live) put(pd.s0, pP, pd.ksc);
-    qr.mma(kB, pd.acc);
-    const float pA = qr.epilogue(acc1);
-    sched_mfma_valu<kMf, kV, MT, 0>();
-    put(sA, pA, ksc[2 * pr]);
-    pd.s0 = sA + kKeyTile;
-    pd.ksc = ksc[2 * pr + 1];
-    pd.live = true;
-  }
+  ixcore::chunk_tile_pairs<Op, MT, kChunkKeys>(kbuf<kCur>(), key0, a, b, qr, lane, ksc, pd, put);
 }
 
 template <class Op, int MT>
@@ -279,7 +138,7 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
   const int hi = __builtin_amdgcn_readfirstlane(span[1]);
   if (hi <= lo) return;
   const int nchunks = (hi - lo + kChunkKeys - 1) / kChunkKeys;
-  const ChunkDma<Op> dma(wave, lane);
+  const RowsDma<Op> dma(wave, lane);
   dma.issue(kbuf<0>(), k, lo, n_k, wave, lane);
 
   const int64_t t = t0 + wave;

@@ -85,18 +85,19 @@ def test_indexer_rejects_bad_arguments(lib):
 
 def test_indexer_topk_workspace_is_checked(lib):
     # few rows over more than 8192 keys (fused: candidate workspace) and many
-    # rows (scores go through the workspace)
-    for n_q, n_k in ((4, 10000), (2000, 8)):
-        need = lib.dsa_indexer_topk_workspace_size(n_q, n_k, 64, 128, 1, 4)
+    # rows with index_topk above 2048 (scores go through the workspace)
+    for n_q, n_k, K in ((4, 10000, 4), (2000, 8, 3000)):
+        need = lib.dsa_indexer_topk_workspace_size(n_q, n_k, 64, 128, 1, K)
         assert need > 0
-        st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, n_q, n_k, 64, 128, 1, 4,
+        st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, n_q, n_k, 64, 128, 1, K,
                                   FAKE, None, 0, None)
         assert st == WORKSPACE
-        st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, n_q, n_k, 64, 128, 1, 4,
+        st = lib.dsa_indexer_topk(FAKE32, FAKE32, None, FAKE, FAKE, FAKE, n_q, n_k, 64, 128, 1, K,
                                   FAKE, FAKE32, need - 1, None)
         assert st == WORKSPACE
-    # fused with every window inside 8192 keys needs none
+    # fused with every window inside 8192 keys needs none, nor does prefill
     assert lib.dsa_indexer_topk_workspace_size(4, 8192, 64, 128, 1, 4) == 0
+    assert lib.dsa_indexer_topk_workspace_size(2000, 100000, 64, 128, 1, 2048) == 0
 
 
 def test_topk_workspace_is_checked(lib):
@@ -137,9 +138,12 @@ def test_windows_and_prep_reject_bad_arguments(lib):
 
 
 def test_noalloc_rejects_a_workspace_beyond_its_array(lib):
-    # 1000 decode rows over long windows need 1000 * 16 * 2048 * 8 + ... bytes of
+    # 256 decode rows over long windows need 256 * (16 * 2048 * 8 + 64) bytes of
     # candidates, more than the 64 MiB array: refused before any device call
-    need = lib.dsa_indexer_topk_workspace_size(1000, 100000, 64, 128, 1, 2048)
+    need = lib.dsa_indexer_topk_workspace_size(256, 100000, 64, 128, 1, 2048)
     assert need > (64 << 20)
-    assert lib.dsa_indexer_topk_noalloc(FAKE, FAKE, None, FAKE32, FAKE, FAKE, 1000, 100000, 64,
+    assert lib.dsa_indexer_topk_noalloc(FAKE, FAKE, None, FAKE32, FAKE, FAKE, 256, 100000, 64,
                                         128, 1, 2048, FAKE, None) == WORKSPACE
+    # prefill rows keep their candidates on chip: no workspace at all
+    assert lib.dsa_indexer_topk_workspace_size(65536, 65536, 64, 128, 2, 2048) == 0
+    assert lib.dsa_indexer_topk_workspace_size(257, 1 << 20, 64, 128, 1, 2048) == 0

@@ -11,7 +11,8 @@ Checks per sampled row:
   * dsa_topk on the oracle's fp32 scores is bit-identical to the oracle's top-k;
   * the GPU's end-to-end selection differs from the oracle's only in columns
     whose score is within tolerance of the k-th (T3);
-  * the fused indexer + top-k call returns the unfused call's indices;
+  * the fused indexer + top-k call returns the unfused call's indices (every
+    row);
   * sparse MLA over the oracle's selection matches the oracle (T4), and the
     full-size MLA output matches it on rows whose selections are identical.
 
@@ -75,7 +76,9 @@ def _run_workload(dsa, name, n_random=96):
     ors, ore = o_win.row_windows(lay.cu_q, lay.cu_k)
     assert np.array_equal(host(rs), ors) and np.array_equal(host(re), ore)
     g_idx = host(idx[rt])
-    assert np.array_equal(g_idx, host(idx_fused[rt])), "fused and unfused indices differ"
+    bad = torch.nonzero((idx_fused != idx).any(dim=1)).flatten()
+    assert bad.numel() == 0, f"[{name}] fused and unfused indices differ on {bad.numel()} rows"
+    say(f"[{name}] fused indexer + top-k equals scores + top-k on all {lay.n_q} rows")
     q_raw_s = host(inp["q_raw"][rt])
     w_s = host(inp["w"][rt])
     pos_q = lay.positions()

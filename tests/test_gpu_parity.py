@@ -630,3 +630,74 @@ def test_calls_on_a_caller_stream(dsa):
     assert torch.equal(idx, base_idx) and torch.equal(top, base_top)
     assert torch.equal(out, base_out) and torch.equal(lse, base_lse)
     del lay, g
+
+
+# ---------------------------------------------------------------------------
+# fused prefill indexer + top-k (more than 256 rows): candidates held in LDS
+# ---------------------------------------------------------------------------
+def _fused_vs_unfused(dsa, q, k, wt, ks, rs, re, K, what):
+    S = dsa.dsa_indexer_scores(q, k, wt, rs, re, k_scale=ks)
+    ref = dsa.dsa_topk(S, rs, re, K)
+    need = dsa._lib_or_load().dsa_indexer_topk_workspace_size(q.shape[0], k.shape[0], q.shape[1],
+                                                               q.shape[2], dsa._dtype_code(q), K)
+    assert need == 0, f"{what}: the prefill path needs no workspace"
+    got = dsa.dsa_indexer_topk(q, k, wt, rs, re, K, k_scale=ks)
+    torch.cuda.synchronize()
+    bad = torch.nonzero((got != ref).any(dim=1)).flatten().cpu().numpy()
+    assert bad.size == 0, (f"{what}: fused differs on {bad.size} rows, first {bad[:5]}: "
+                           f"{host(got[bad[0]])[:10]} vs {host(ref[bad[0]])[:10]}")
+    return S, ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_topk_prefill_matches_unfused(dsa, dtype):
+    # causal prefill and packed samples; windows from empty to 20000 keys (the
+    # held candidates are shrunk several times per row); k from 1 to 2048
+    w = P4K if dtype == "bf16" else synth.WORKLOADS["fp8_64k"]
+    rope = dtype == "bf16"
+    for lens, Ks in (([3000], (2048, 300)), ([700, 20000, 33, 1, 4100], (2048, 1, 777))):
+        lay = synth.layout_from_lengths(lens)
+        p, rs, re = canonical_indexer(w, lay, dtype, rope=rope)
+        q, k, wt, ks = to_device_indexer(p, dtype)
+        say(f"fused prefill {dtype} lens={lens}: n_q={lay.n_q}")
+        for K in Ks:
+            S, ref = _fused_vs_unfused(dsa, q, k, wt, ks, i32(rs), i32(re), K, f"{dtype} {lens} K={K}")
+        # and the unfused selection is the oracle's on those fp32 scores (sampled rows)
+        Sh = host(S)
+        for t in list(range(0, lay.n_q, 997)) + [lay.n_q - 1]:
+            np.testing.assert_array_equal(host(ref[t]), o_topk.topk_row(Sh[t], rs[t], re[t], Ks[-1]))
+
+
+def test_indexer_topk_prefill_ties_and_signs(dsa):
+    # rows whose weights are 0 (every score exactly 0: the first k columns win)
+    # or negative (scores <= 0, with -0.0 == +0.0), and random windows inside
+    # one block of four rows
+    lay = synth.layout_from_lengths([6000])
+    p, _, _ = canonical_indexer(P4K, lay, "bf16", signed=True)
+    g = np.random.default_rng(303)
+    n_q = 1500
+    p = dict(p, q=p["q"][:n_q], w=p["w"][:n_q].copy())
+    p["w"][0::5] = 0.0
+    p["w"][1::5] = -np.abs(p["w"][1::5])
+    rs = g.integers(0, 6000, n_q).astype(np.int32)
+    re = np.minimum(6000, rs + g.integers(0, 6000, n_q)).astype(np.int32)
+    rs[:8] = [0, 0, 5, 100, 0, 2999, 6000, 0]
+    re[:8] = [6000, 1, 5, 2148, 2048, 5999, 6000, 2049]
+    q, k, wt, _ = to_device_indexer(p, "bf16")
+    for K in (2048, 64):
+        _fused_vs_unfused(dsa, q, k, wt, None, i32(rs), i32(re), K, f"ties K={K}")
+
+
+def test_indexer_topk_prefill_wide_columns(dsa):
+    # more than 65536 keys: the held columns are 32-bit
+    g = np.random.default_rng(304)
+    n_k, n_q = 70000, 300
+    lay = synth.layout_from_lengths([n_k])
+    p, _, _ = canonical_indexer(P4K, lay, "bf16", rope=False)
+    p = dict(p, q=p["q"][:n_q], w=p["w"][:n_q])
+    rs = g.integers(0, 10000, n_q).astype(np.int32)
+    re = np.minimum(n_k, rs + g.integers(1, n_k, n_q)).astype(np.int32)
+    rs[:3], re[:3] = [0, 0, 4], [n_k, 65537, 65541]
+    q, k, wt, _ = to_device_indexer(p, "bf16")
+    say(f"fused prefill wide: n_q={n_q} n_k={n_k}")
+    _fused_vs_unfused(dsa, q, k, wt, None, i32(rs), i32(re), 2048, "wide")

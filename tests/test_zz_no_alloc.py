@@ -53,8 +53,10 @@ def test_noalloc_matches_workspace_call(dsa):
 
 
 def test_noalloc_rejects_more_than_the_array(dsa):
-    q, k, w, ks, rs, re = _operands([20000] * 300, "bf16")     # 300 rows x 262208 B > 64 MiB
-    out = torch.full((300, 2048), -7, dtype=torch.int32, device="cuda")
+    # 256 decode rows over windows of more than 8192 keys: 256 x 262208 B > 64 MiB
+    # (more rows take the prefill kernel, which needs no workspace)
+    q, k, w, ks, rs, re = _operands([9000] * 256, "bf16")
+    out = torch.full((256, 2048), -7, dtype=torch.int32, device="cuda")
     with pytest.raises(dsa.DSAError, match="workspace"):
         dsa.dsa_indexer_topk_noalloc(q, k, w, rs, re, 2048, out=out)
     torch.cuda.synchronize()
