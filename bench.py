@@ -18,6 +18,7 @@ workload on this host.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -116,15 +117,35 @@ def stage_bench(args, dsa, synth, np, torch):
     and every standalone top-k) get a 1 GiB write between repetitions so that
     their inputs are not served from the 256 MB last-level cache."""
     dev = "cuda"
-    w = synth.WORKLOADS[args.workload.replace("_stages", "")]
+    fp8_cache = args.workload == "decode_fp8"
+    w = synth.WORKLOADS["decode" if fp8_cache else args.workload.replace("_stages", "")]
     lay = synth.layout(w)
     i32 = lambda x: torch.from_numpy(np.asarray(x, np.int32)).to(dev)
     inp = synth.device_inputs(w, dev, lay)
     tdt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
     rs, re = dsa.dsa_row_windows(i32(lay.cu_q), i32(lay.cu_k), lay.n_q)
-    q, k, wt, ks = dsa.dsa_indexer_prep(inp["q_raw"], inp["k_raw"], inp["w"], i32(lay.positions()),
-                                        i32(lay.key_positions()), tdt, w.rope_dim, w.rope_main_dim,
-                                        w.rope_theta)
+    insert_ms = None
+    if fp8_cache:
+        # the index-key cache in e4m3 + power-of-two scales, written by the fused
+        # norm -> quant -> insert from the bf16 key projections (timed once)
+        w = dataclasses.replace(w, dtype="fp8")
+        k_in = inp["k_raw"].to(torch.bfloat16)
+        slots = torch.arange(lay.n_k, dtype=torch.int64, device=dev)
+        k = torch.empty((lay.n_k, w.head_dim), dtype=torch.float8_e4m3fn, device=dev)
+        ks = torch.empty(lay.n_k, dtype=torch.float32, device=dev)
+        dsa.dsa_indexer_k_insert(k_in, slots, k, ks)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dsa.dsa_indexer_k_insert(k_in, slots, k, ks)
+        e1.record()
+        torch.cuda.synchronize()
+        insert_ms = e0.elapsed_time(e1)
+        del k_in
+        q, _, wt, _ = dsa.dsa_indexer_prep(inp["q_raw"], None, inp["w"], out_dtype=torch.float8_e4m3fn)
+    else:
+        q, k, wt, ks = dsa.dsa_indexer_prep(inp["q_raw"], inp["k_raw"], inp["w"],
+                                            i32(lay.positions()), i32(lay.key_positions()), tdt,
+                                            w.rope_dim, w.rope_main_dim, w.rope_theta)
     mq = inp["mla_q"].to(torch.bfloat16)
     mkv = inp["mla_kv"].to(torch.bfloat16)
     del inp
@@ -179,7 +200,8 @@ def stage_bench(args, dsa, synth, np, torch):
     hd = w.n_heads * w.head_dim
     elt = 1 if w.dtype == "fp8" else 2
     idx_flop = pairs * 2 * hd
-    idx_bytes = lay.n_q * hd * elt + lay.n_k * w.head_dim * elt + lay.n_q * w.n_heads * 4 + pairs * 4
+    key_bytes = lay.n_k * (w.head_dim * elt + (4 if w.dtype == "fp8" else 0))  # codes + scale
+    idx_bytes = lay.n_q * hd * elt + key_bytes + lay.n_q * w.n_heads * 4 + pairs * 4
     topk_bytes = pairs * 4 + lay.n_q * K * 4
     mla_flop = sel * MLA_FLOP_PER_PAIR
     gather = sel * w.d_qk * 2
@@ -202,6 +224,11 @@ def stage_bench(args, dsa, synth, np, torch):
                 "gather_gbs": (gather + mla_compulsory) / t["mla"] / 1e9,
                 "frac_hbm": (gather + mla_compulsory) / t["mla"] / 1e9 / HBM_PEAK_GBS},
     }
+    if insert_ms is not None:
+        ib = lay.n_k * (w.head_dim * 2 + 8 + w.head_dim + 4)  # bf16 keys + slot in, codes + scale out
+        comp["k_insert"] = {"ms": insert_ms, "keys_per_s": lay.n_k / (insert_ms * 1e-3),
+                            "gbs": ib / (insert_ms * 1e-3) / 1e9,
+                            "frac_hbm": ib / (insert_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if fused:
         fb = idx_bytes - pairs * 4 + lay.n_q * K * 4       # q + k + w read, indices written
         comp["indexer_topk_fused"] = {"ms": ms["indexer_topk"],
@@ -251,7 +278,7 @@ def stage_bench(args, dsa, synth, np, torch):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": total,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: n_q={lay.n_q} n_k={lay.n_k} index {w.n_heads}x{w.head_dim} "
+        "config": {"workload": f"{args.workload}: n_q={lay.n_q} n_k={lay.n_k} index {w.n_heads}x{w.head_dim} "
                                f"{w.dtype}, index_topk {K}, sparse MLA {w.mla_heads} heads "
                                f"{w.d_qk}/{w.d_v} bf16", "valid_pairs": pairs, "selected_pairs": sel,
                    "parallelism": "none (1 GPU)"},
@@ -265,7 +292,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill4k",
-                    choices=["prefill4k", "prefill4k_stages", "thd", "decode", "fp8_64k"],
+                    choices=["prefill4k", "prefill4k_stages", "thd", "decode", "decode_fp8",
+                             "fp8_64k"],
                     help="prefill4k: the benchmark step; the others time each stage on its own")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -123,6 +123,37 @@ int dsa_indexer_prep(const float* q_raw, const float* k_raw, const float* w,
                      void* stream);
 
 /*
+ * dsa_indexer_k_insert -- write new index keys into the fp8 index-key cache.
+ *
+ * Passage: KimiK3DSAIndexer._fused_k_insert and KimiK3DSAIndexer.__init__ on the
+ * vLLM API page "vllm.models.kimi_k3.nvidia.dsa": the new tokens' index keys go
+ * through the key LayerNorm (the norm's weight, bias and eps; this fused path
+ * is the one used without index rope), are quantised to fp8 with one
+ * power-of-two ("ue8m0", rounded at write) scale per index_head_dim block, and
+ * are written to the cache at the tokens' slots.
+ *
+ *   k_raw          [n_tokens, head_dim] of k_dtype (F32 or BF16): the key
+ *                  projection before the norm
+ *   norm_weight    f32 [head_dim] or NULL (1);  norm_bias f32 [head_dim] or NULL (0)
+ *   slot_mapping   int64 [n_tokens]: the cache row of each token; a negative
+ *                  slot (padding) or one >= n_slots writes nothing
+ *   k_cache        OCP e4m3fn [n_slots, head_dim] (uint8): row `slot` gets the
+ *                  codes; k_scale_cache f32 [n_slots]: row `slot` gets the scale.
+ *                  Together they are the k / k_scale operands of
+ *                  dsa_indexer_scores and dsa_indexer_topk with FP8_E4M3 (132
+ *                  bytes read per key), so a decode step scores the cache in place.
+ * Other slots are left untouched.  Two tokens must not share a slot.  Scale
+ * rule as dsa_indexer_prep: the smallest power of two s with amax <= 448 * s
+ * (1 for an all-zero row), codes = round-to-nearest-even(y / s); the norm is
+ * computed in fp32.  Supported: even head_dim <= 128, or a multiple of 4 up to
+ * 256.
+ */
+int dsa_indexer_k_insert(const void* k_raw, int32_t k_dtype, const float* norm_weight,
+                         const float* norm_bias, float eps, const int64_t* slot_mapping,
+                         int64_t n_tokens, int32_t head_dim, uint8_t* k_cache,
+                         float* k_scale_cache, int64_t n_slots, void* stream);
+
+/*
  * dsa_indexer_scores -- lightning-indexer scores over each row's window.
  *
  * Passage: the operands KimiK3DSAIndexer.forward and .score build on the vLLM API

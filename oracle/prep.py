@@ -71,6 +71,17 @@ def layer_norm(x, eps: float = 1e-6) -> np.ndarray:
     return d / np.sqrt(var + eps)
 
 
+def layer_norm_affine(x, weight=None, bias=None, eps: float = 1e-6) -> np.ndarray:
+    """LayerNorm over the last axis followed by the per-dim weight and bias
+    (KimiK3DSAIndexerKNorm holds both; weight None = 1, bias None = 0)."""
+    y = layer_norm(x, eps)
+    if weight is not None:
+        y = y * np.asarray(weight, np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)
+    return y
+
+
 # ----------------------------------------------------------------------------
 # RoPE on the leading dims, half-split pairing (_apply_index_rope)
 # ----------------------------------------------------------------------------
@@ -164,3 +175,28 @@ def prepare_indexer_inputs(q_raw, k_raw, w, positions_q, positions_k, dtype: str
         wf = round_f32(fold_q_scale(w, sq[..., 0]))
         return dict(q=q8, k=k8, w=wf, k_scale=sk[:, 0])
     raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# the fp8 index-key cache and its fused insert
+# ----------------------------------------------------------------------------
+def k_norm_quant_insert(k_raw, weight, bias, eps, slot_mapping, cache_codes, cache_scales):
+    """The index-key cache insert of KimiK3DSAIndexer._fused_k_insert (vLLM API
+    page "vllm.models.kimi_k3.nvidia.dsa"): each new key row goes through the
+    key LayerNorm (with the norm's weight and bias; the fused insert is used
+    only without index rope), is quantised to e4m3 with one power-of-two
+    ("ue8m0") scale for its index_head_dim block, and is written to the cache
+    slot slot_mapping[i].
+
+    Readings: a negative slot is a padding token and writes nothing; so does a
+    slot past the cache (the insert never writes outside it); every other slot
+    keeps its contents; two tokens never share a slot.  cache_codes [n_slots, D]
+    (e4m3 values as float64) and cache_scales [n_slots] are updated in place
+    and returned."""
+    y = layer_norm_affine(k_raw, weight, bias, eps)
+    codes, s = quant_e4m3_blocks(y, y.shape[-1])
+    slots = np.asarray(slot_mapping, np.int64)
+    ok = (slots >= 0) & (slots < cache_codes.shape[0])
+    cache_codes[slots[ok]] = codes[ok]
+    cache_scales[slots[ok]] = s[ok, 0]
+    return cache_codes, cache_scales

@@ -5,8 +5,9 @@ kernels.  Tensors are torch CUDA (HIP) tensors; each call is enqueued on the
 current torch stream.  The entry points carry the names of the C ABI in
 ``include/dsa.h``:
 
-    dsa_row_windows, dsa_indexer_prep, dsa_indexer_scores, dsa_topk,
-    dsa_indexer_topk, dsa_sparse_mla_fwd (+ workspace-size queries)
+    dsa_row_windows, dsa_indexer_prep, dsa_indexer_k_insert, dsa_indexer_scores,
+    dsa_topk, dsa_indexer_topk, dsa_indexer_topk_noalloc, dsa_sparse_mla_fwd
+    (+ workspace-size queries)
 
 A nonzero status raises ``DSAError``.  Importing this package does not load
 the library; ``load()`` does, and fails loudly when it is missing.
@@ -61,6 +62,7 @@ def _declare(lib):
         "dsa_row_windows": (ctypes.c_int, [P, P, I32, I64, I32, P, P, P]),
         "dsa_indexer_prep": (ctypes.c_int, [P, P, P, P, P, I64, I64, I32, I32, I32, I32, F32, F32,
                                             I32, P, P, P, P, P]),
+        "dsa_indexer_k_insert": (ctypes.c_int, [P, I32, P, P, F32, P, I64, I32, P, P, I64, P]),
         "dsa_indexer_scores": (ctypes.c_int, [P, P, P, P, P, P, I64, I64, I32, I32, I32, P, I64, P]),
         "dsa_topk_workspace_size": (SZ, [I64, I64, I32]),
         "dsa_topk": (ctypes.c_int, [P, I64, P, P, I64, I64, I32, P, P, SZ, P]),
@@ -80,7 +82,7 @@ def _declare(lib):
 
 
 EXPORTS = ("dsa_status_string", "dsa_version", "dsa_row_windows", "dsa_indexer_prep",
-           "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
+           "dsa_indexer_k_insert", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
            "dsa_indexer_topk_workspace_size", "dsa_indexer_topk", "dsa_indexer_topk_noalloc",
            "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd")
 
@@ -149,23 +151,39 @@ def dsa_row_windows(cu_seqlens_q, cu_seqlens_k, n_rows: int, causal: bool = True
 def dsa_indexer_prep(q_raw, k_raw, w, pos_q=None, pos_k=None, out_dtype=None, rope_dim: int = 0,
                      rope_main_dim: int = 0, rope_theta: float = 1e4, eps: float = 1e-6,
                      stream=None):
-    """Returns (q, k, w_out, k_scale) in out_dtype (k_scale is None unless fp8)."""
+    """Returns (q, k, w_out, k_scale) in out_dtype (k_scale is None unless fp8;
+    k and k_scale are None when k_raw is None: queries only, e.g. a decode step
+    over a key cache)."""
     import torch
     lib = _lib_or_load()
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     n_q, H, D = q_raw.shape
-    n_k = k_raw.shape[0]
+    n_k = 0 if k_raw is None else k_raw.shape[0]
     with _on(stream):
         q = torch.empty((n_q, H, D), dtype=out_dtype, device=q_raw.device)
-        k = torch.empty((n_k, D), dtype=out_dtype, device=q_raw.device)
+        k = None if k_raw is None else torch.empty((n_k, D), dtype=out_dtype, device=q_raw.device)
         w_out = torch.empty((n_q, H), dtype=torch.float32, device=q_raw.device)
         ks = torch.empty(n_k, dtype=torch.float32, device=q_raw.device) \
-            if out_dtype == torch.float8_e4m3fn else None
+            if out_dtype == torch.float8_e4m3fn and k_raw is not None else None
     _check(lib.dsa_indexer_prep(_ptr(q_raw), _ptr(k_raw), _ptr(w), _ptr(pos_q), _ptr(pos_k),
                                 n_q, n_k, H, D, rope_dim, rope_main_dim, rope_theta, eps,
                                 _dtype_code(q), _ptr(q), _ptr(k), _ptr(w_out), _ptr(ks),
                                 _stream(stream)), "dsa_indexer_prep")
     return q, k, w_out, ks
+
+
+def dsa_indexer_k_insert(k_raw, slot_mapping, k_cache, k_scale_cache, norm_weight=None,
+                         norm_bias=None, eps: float = 1e-6, stream=None):
+    """LayerNorm -> e4m3 + power-of-two scale -> cache rows slot_mapping[i]
+    (k_cache uint8 / float8_e4m3fn [n_slots, D], k_scale_cache f32 [n_slots],
+    updated in place; negative slots are skipped)."""
+    lib = _lib_or_load()
+    n_tok, D = k_raw.shape
+    _check(lib.dsa_indexer_k_insert(_ptr(k_raw), _dtype_code(k_raw), _ptr(norm_weight),
+                                    _ptr(norm_bias), eps, _ptr(slot_mapping), n_tok, D,
+                                    _ptr(k_cache), _ptr(k_scale_cache), k_cache.shape[0],
+                                    _stream(stream)), "dsa_indexer_k_insert")
+    return k_cache, k_scale_cache
 
 
 def dsa_indexer_scores(q, k, w, row_starts, row_ends, k_scale=None, scores=None, ld=None,

@@ -109,6 +109,25 @@ int dsa_indexer_prep(const float* q_raw, const float* k_raw, const float* w,
                                                 as_stream(stream)));
 }
 
+int dsa_indexer_k_insert(const void* k_raw, int32_t k_dtype, const float* norm_weight,
+                         const float* norm_bias, float eps, const int64_t* slot_mapping,
+                         int64_t n_tokens, int32_t head_dim, uint8_t* k_cache,
+                         float* k_scale_cache, int64_t n_slots, void* stream) {
+  if (n_tokens < 0 || n_slots < 0 || head_dim < 1) return DSA_ERR_INVALID_ARG;
+  if (k_dtype != DSA_DTYPE_F32 && k_dtype != DSA_DTYPE_BF16) {
+    if (k_dtype == DSA_DTYPE_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+    return DSA_ERR_INVALID_ARG;
+  }
+  if (!(eps >= 0.0f)) return DSA_ERR_INVALID_ARG;
+  if (n_tokens > 0 && (!k_raw || !slot_mapping)) return DSA_ERR_INVALID_ARG;
+  if (n_slots > 0 && (!k_cache || !k_scale_cache)) return DSA_ERR_INVALID_ARG;
+  if (head_dim > 256 || (head_dim > 128 ? head_dim % 4 : head_dim % 2) != 0)
+    return DSA_ERR_UNSUPPORTED;
+  return launch_status(dsa::launch_indexer_k_insert(k_raw, k_dtype, norm_weight, norm_bias, eps,
+                                                    slot_mapping, n_tokens, head_dim, k_cache,
+                                                    k_scale_cache, n_slots, as_stream(stream)));
+}
+
 int dsa_indexer_scores(const void* q, const void* k, const float* k_scale, const float* w,
                        const int32_t* row_starts, const int32_t* row_ends, int64_t n_q,
                        int64_t n_k, int32_t n_heads, int32_t head_dim, int32_t dtype,

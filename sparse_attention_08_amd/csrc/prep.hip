@@ -51,6 +51,30 @@ __device__ __forceinline__ float pow2_scale(float amax) {
   return s;
 }
 
+// LayerNorm of one row held by one wave (x[j] = element lane + 64 j, zero past
+// D): fp32, biased variance.
+__device__ __forceinline__ void wave_layer_norm(float (&x)[kMaxD / kWave], int D, float eps,
+                                                int lane) {
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxD / kWave; ++j) s += x[j];
+  const float mean = wave_sum(s) / float(D);
+  float v = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxD / kWave; ++j) {
+    const int e = lane + kWave * j;
+    const float d = e < D ? x[j] - mean : 0.0f;
+    v = fmaf(d, d, v);
+  }
+  const float var = wave_sum(v) / float(D);
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int j = 0; j < kMaxD / kWave; ++j) {
+    const int e = lane + kWave * j;
+    x[j] = e < D ? (x[j] - mean) * rstd : 0.0f;
+  }
+}
+
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void prep_kernel(
     const float* __restrict__ q_raw, const float* __restrict__ k_raw,
     const float* __restrict__ w, const int32_t* __restrict__ pos_q,
@@ -73,26 +97,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void prep_kernel(
     const int e = lane + kWave * j;
     x[j] = (live && e < D) ? src[e] : 0.0f;
   }
-  if (is_key) {  // LayerNorm, fp32, biased variance
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxD / kWave; ++j) s += x[j];
-    const float mean = wave_sum(s) / float(D);
-    float v = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxD / kWave; ++j) {
-      const int e = lane + kWave * j;
-      const float d = e < D ? x[j] - mean : 0.0f;
-      v = fmaf(d, d, v);
-    }
-    const float var = wave_sum(v) / float(D);
-    const float rstd = 1.0f / sqrtf(var + eps);
-#pragma unroll
-    for (int j = 0; j < kMaxD / kWave; ++j) {
-      const int e = lane + kWave * j;
-      x[j] = e < D ? (x[j] - mean) * rstd : 0.0f;
-    }
-  }
+  if (is_key) wave_layer_norm(x, D, eps, lane);  // LayerNorm, fp32, biased variance
   if (rope_dim > 0) {
 #pragma unroll
     for (int j = 0; j < kMaxD / kWave; ++j) buf[wave][lane + kWave * j] = x[j];
@@ -145,6 +150,165 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void prep_kernel(
   if (!is_key && lane == 0 && w_out) w_out[r] = w[r];
 }
 
+// The fused insert into the fp8 index-key cache (KimiK3DSAIndexer._fused_k_insert
+// on the vLLM API page "vllm.models.kimi_k3.nvidia.dsa"): one wave per new key
+// row -- LayerNorm with the norm's weight and bias, one power-of-two scale for
+// the row, e4m3 codes -- written to its cache slot.  A negative slot (padding)
+// or one past the cache writes nothing.  Lane l holds the kPer consecutive
+// elements kPer*l .. (the row is read and written with one vector access per
+// lane; the norm's sums and the max do not depend on the order), and a wave
+// issues the loads of kInsRows rows before it works on any of them.
+constexpr int kInsRows = 4;  // rows per wave, their loads issued together
+
+template <bool kBf16In, int kPer>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void k_insert_kernel(
+    const void* __restrict__ k_raw, const float* __restrict__ weight,
+    const float* __restrict__ bias, float eps, const int64_t* __restrict__ slots,
+    int64_t n_tok, int64_t n_slots, int D, uint8_t* __restrict__ cache,
+    float* __restrict__ cache_scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row0 = (int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave) * kInsRows;
+  const int e0 = kPer * lane;
+  const bool on = e0 < D;  // D is a multiple of kPer
+  float wg[kPer], bs[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    wg[j] = (on && weight) ? weight[e0 + j] : 1.0f;
+    bs[j] = (on && bias) ? bias[e0 + j] : 0.0f;
+  }
+  float x[kInsRows][kPer];
+  int64_t slot[kInsRows];
+#pragma unroll
+  for (int r = 0; r < kInsRows; ++r) {
+    const int64_t row = row0 + r;
+    const bool live = row < n_tok;
+    slot[r] = live ? slots[row] : -1;
+    const int64_t rr = live ? row : 0;
+    if constexpr (kBf16In) {
+      const uint16_t* src = static_cast<const uint16_t*>(k_raw) + rr * D + e0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) x[r][j] = on ? bf16_bits_to_f32(src[j]) : 0.0f;
+    } else {
+      const float* src = static_cast<const float*>(k_raw) + rr * D + e0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) x[r][j] = on ? src[j] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kInsRows; ++r) {
+    if (slot[r] < 0 || slot[r] >= n_slots) continue;  // padding or past the cache (wave-uniform)
+    // LayerNorm, fp32, biased variance, then the norm's weight and bias
+    float sm = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) sm += x[r][j];
+    const float mean = wave_sum(sm) / float(D);
+    float v = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float d = on ? x[r][j] - mean : 0.0f;
+      v = fmaf(d, d, v);
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(v) / float(D) + eps);
+    float y[kPer];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      y[j] = fmaf((x[r][j] - mean) * rstd, wg[j], bs[j]);
+      amax = on ? fmaxf(amax, fabsf(y[j])) : amax;
+    }
+    amax = wave_max(amax);
+    const float s = pow2_scale(amax);
+    if (on) {
+      uint8_t c[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) c[j] = encode_e4m3(y[j] / s);
+      uint8_t* dst = cache + slot[r] * D + e0;
+      if constexpr (kPer == 2) {
+        *reinterpret_cast<uint16_t*>(dst) = uint16_t(c[0] | (c[1] << 8));
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) =
+            uint32_t(c[0]) | (uint32_t(c[1]) << 8) | (uint32_t(c[2]) << 16) | (uint32_t(c[3]) << 24);
+      }
+    }
+    if (lane == 0) cache_scale[slot[r]] = s;
+  }
+}
+
+// head_dim 128: 16 lanes per row, four rows per wave, eight consecutive
+// elements per lane (one 16- or 32-byte load, one 8-byte store of codes); the
+// row sums and max reduce over the 16 lanes of the row.
+template <int O>
+__device__ __forceinline__ float xor16_sum(float v) {
+  if constexpr (O > 0) return xor16_sum<O / 2>(v + __shfl_xor(v, O));
+  return v;
+}
+template <int O>
+__device__ __forceinline__ float xor16_max(float v) {
+  if constexpr (O > 0) return xor16_max<O / 2>(fmaxf(v, __shfl_xor(v, O)));
+  return v;
+}
+
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void k_insert128_kernel(
+    const void* __restrict__ k_raw, const float* __restrict__ weight,
+    const float* __restrict__ bias, float eps, const int64_t* __restrict__ slots,
+    int64_t n_tok, int64_t n_slots, uint8_t* __restrict__ cache,
+    float* __restrict__ cache_scale) {
+  constexpr int D = 128;
+  const int sub = threadIdx.x & 15;
+  const int64_t row = (int64_t(blockIdx.x) * 256 + threadIdx.x) / 16;
+  const int e0 = 8 * sub;
+  float x[8], wg[8], bs[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    wg[j] = weight ? weight[e0 + j] : 1.0f;
+    bs[j] = bias ? bias[e0 + j] : 0.0f;
+  }
+  const int64_t rr = row < n_tok ? row : n_tok - 1;
+  const int64_t slot = slots[rr];
+  if constexpr (kBf16In) {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k_raw) + rr * D + e0);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_bits_to_f32(uint16_t(w4[j] & 0xFFFFu));
+      x[2 * j + 1] = bf16_bits_to_f32(uint16_t(w4[j] >> 16));
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(k_raw) + rr * D + e0);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(k_raw) + rr * D + e0 + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  float sm = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sm += x[j];
+  const float mean = xor16_sum<8>(sm) / float(D);
+  float v = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float d = x[j] - mean;
+    v = fmaf(d, d, v);
+  }
+  const float rstd = 1.0f / sqrtf(xor16_sum<8>(v) / float(D) + eps);
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = fmaf((x[j] - mean) * rstd, wg[j], bs[j]);
+    amax = fmaxf(amax, fabsf(x[j]));
+  }
+  const float s = pow2_scale(xor16_max<8>(amax));
+  if (row >= n_tok || slot < 0 || slot >= n_slots) return;
+  uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo |= uint32_t(encode_e4m3(x[j] / s)) << (8 * j);
+    hi |= uint32_t(encode_e4m3(x[4 + j] / s)) << (8 * j);
+  }
+  *reinterpret_cast<uint2*>(cache + slot * D + e0) = make_uint2(lo, hi);
+  if (sub == 0) cache_scale[slot] = s;
+}
+
 __global__ __launch_bounds__(256) void row_windows_kernel(const int32_t* __restrict__ cu_q,
                                                           const int32_t* __restrict__ cu_k,
                                                           int n_seqs, int64_t n_rows, int causal,
@@ -186,6 +350,52 @@ hipError_t launch_indexer_prep(const float* q_raw, const float* k_raw, const flo
   hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(kRowsPerBlock * kWave), 0, stream, q_raw,
                      k_raw, w, pos_q, pos_k, n_q, n_k, n_heads, head_dim, rope_dim,
                      rope_main_dim, theta, eps, dtype, q_out, k_out, w_out, k_scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_k_insert(const void* k_raw, int32_t k_dtype, const float* weight,
+                                   const float* bias, float eps, const int64_t* slot_mapping,
+                                   int64_t n_tokens, int32_t head_dim, uint8_t* k_cache,
+                                   float* k_scale_cache, int64_t n_slots, hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  if (head_dim == 128) {
+    const unsigned g128 = unsigned((n_tokens + 15) / 16);
+    if (k_dtype == 1)
+      hipLaunchKernelGGL(k_insert128_kernel<true>, dim3(g128), dim3(256), 0, stream, k_raw,
+                         weight, bias, eps, slot_mapping, n_tokens, n_slots, k_cache,
+                         k_scale_cache);
+    else
+      hipLaunchKernelGGL(k_insert128_kernel<false>, dim3(g128), dim3(256), 0, stream, k_raw,
+                         weight, bias, eps, slot_mapping, n_tokens, n_slots, k_cache,
+                         k_scale_cache);
+    return hipGetLastError();
+  }
+  const int64_t per_block = int64_t(kRowsPerBlock) * kInsRows;
+  const unsigned grid = unsigned((n_tokens + per_block - 1) / per_block);
+  const dim3 blk(kRowsPerBlock * kWave);
+  // two elements per lane up to 128 dims, four up to 256 (the C ABI admits
+  // only those head dims)
+  if (head_dim <= 128 && head_dim % 2 == 0) {
+    if (k_dtype == 1)
+      hipLaunchKernelGGL((k_insert_kernel<true, 2>), dim3(grid), blk, 0, stream, k_raw, weight,
+                         bias, eps, slot_mapping, n_tokens, n_slots, head_dim, k_cache,
+                         k_scale_cache);
+    else
+      hipLaunchKernelGGL((k_insert_kernel<false, 2>), dim3(grid), blk, 0, stream, k_raw, weight,
+                         bias, eps, slot_mapping, n_tokens, n_slots, head_dim, k_cache,
+                         k_scale_cache);
+  } else if (head_dim % 4 == 0) {
+    if (k_dtype == 1)
+      hipLaunchKernelGGL((k_insert_kernel<true, 4>), dim3(grid), blk, 0, stream, k_raw, weight,
+                         bias, eps, slot_mapping, n_tokens, n_slots, head_dim, k_cache,
+                         k_scale_cache);
+    else
+      hipLaunchKernelGGL((k_insert_kernel<false, 4>), dim3(grid), blk, 0, stream, k_raw, weight,
+                         bias, eps, slot_mapping, n_tokens, n_slots, head_dim, k_cache,
+                         k_scale_cache);
+  } else {
+    return hipErrorInvalidValue;  // rejected by the C ABI before this point
+  }
   return hipGetLastError();
 }
 

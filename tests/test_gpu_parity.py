@@ -701,3 +701,106 @@ def test_indexer_topk_prefill_wide_columns(dsa):
     q, k, wt, _ = to_device_indexer(p, "bf16")
     say(f"fused prefill wide: n_q={n_q} n_k={n_k}")
     _fused_vs_unfused(dsa, q, k, wt, None, i32(rs), i32(re), 2048, "wide")
+
+
+# ---------------------------------------------------------------------------
+# fp8 index-key cache: fused norm -> quant -> insert, and decode scoring from it
+# ---------------------------------------------------------------------------
+def _e4m3_step(o):
+    a = np.abs(o)
+    return np.where(a < 2.0 ** -6, 2.0 ** -9, np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+
+
+def _check_cache(g_codes, g_scales, o_codes, o_scales, rows, what):
+    np.testing.assert_array_equal(g_scales[rows], o_scales[rows], err_msg=f"{what}: scales")
+    d = np.abs(g_codes[rows] - o_codes[rows])
+    assert np.all(d <= _e4m3_step(o_codes[rows]) * 1.0001), f"{what}: a code off by more than one step"
+    frac = np.mean(d > 0)
+    assert frac < 0.01, f"{what}: {frac:.3%} of the codes differ"
+    return frac
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_k_cache_insert(dsa, in_dtype):
+    g = np.random.default_rng(401)
+    n_tok, n_slots, D = 2000, 2600, 128
+    k_raw = synth.index_k_raw(P4K, 0, n_tok) * 3.0 + 0.5
+    if in_dtype == "bf16":
+        k_raw = o_prep.round_bf16(k_raw)
+    wgt = o_prep.round_f32(1.0 + 0.3 * g.standard_normal(D))
+    bias = o_prep.round_f32(0.1 * g.standard_normal(D))
+    slots = g.permutation(n_slots)[:n_tok].astype(np.int64)
+    slots[::37] = -1                                      # padding tokens
+    slots[5] = n_slots + 3                                # past the cache: ignored
+    k_raw[7] = 0.0                                        # an all-zero row
+    sentinel = 0x7E                                       # e4m3 448
+    cache = torch.full((n_slots, D), sentinel, dtype=torch.uint8, device="cuda")
+    scales = torch.full((n_slots,), -1.0, dtype=torch.float32, device="cuda")
+    tdt = torch.float32 if in_dtype == "f32" else torch.bfloat16
+    say(f"k cache insert {in_dtype}: {n_tok} tokens into {n_slots} slots")
+    dsa.dsa_indexer_k_insert(dev(k_raw, tdt), dev(slots, torch.int64), cache, scales,
+                             norm_weight=dev(wgt), norm_bias=dev(bias), eps=1e-6)
+    g_codes = cache.view(torch.float8_e4m3fn).float().cpu().numpy().astype(np.float64)
+    g_scales = host(scales).astype(np.float64)
+    o_codes = np.full((n_slots, D), 448.0)
+    o_scales = np.full(n_slots, -1.0)
+    o_prep.k_norm_quant_insert(k_raw, wgt, bias, 1e-6, slots, o_codes, o_scales)
+    written = np.zeros(n_slots, bool)
+    written[slots[(slots >= 0) & (slots < n_slots)]] = True
+    assert np.all(host(cache)[~written] == sentinel) and np.all(g_scales[~written] == -1.0)
+    frac = _check_cache(g_codes, g_scales, o_codes, o_scales, written, f"insert {in_dtype}")
+    # an all-zero raw key normalises to 0: what is written is the bias
+    np.testing.assert_array_equal(g_codes[slots[7]] * g_scales[slots[7]],
+                                  o_codes[slots[7]] * o_scales[slots[7]])
+    say(f"  {frac:.4%} of the codes one e4m3 step from the oracle's")
+
+
+def test_decode_scores_from_fp8_key_cache(dsa):
+    # a decode step over caches filled by two inserts (the prompt, then each
+    # sequence's newest token), scored and selected straight from the cache
+    w8 = synth.WORKLOADS["fp8_64k"]
+    lens = [20000, 9000, 70000, 300, 8193]
+    lay = synth.layout_from_lengths(lens, decode=True)
+    k_raw = o_prep.round_bf16(synth.index_k_raw(w8, 0, lay.n_k))
+    q_raw = synth.index_q_raw(w8, 0, lay.n_q)
+    wt = synth.index_weights(w8, 0, lay.n_q)
+    g = np.random.default_rng(402)
+    wgt = o_prep.round_f32(1.0 + 0.2 * g.standard_normal(128))
+    bias = o_prep.round_f32(0.05 * g.standard_normal(128))
+    last = lay.cu_k[1:] - 1
+    first = np.setdiff1d(np.arange(lay.n_k), last)
+    batches = [first, np.concatenate([last, [-1, -1]])]   # the step batch has two padding tokens
+    cache = torch.zeros((lay.n_k, 128), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(lay.n_k, dtype=torch.float32, device="cuda")
+    o_codes, o_scales = np.zeros((lay.n_k, 128)), np.zeros(lay.n_k)
+    for bt in batches:
+        rows = np.where(bt >= 0, bt, 0)
+        kb = k_raw[rows]
+        dsa.dsa_indexer_k_insert(dev(kb, torch.bfloat16), dev(bt.astype(np.int64), torch.int64),
+                                 cache, scales, norm_weight=dev(wgt), norm_bias=dev(bias))
+        o_prep.k_norm_quant_insert(kb, wgt, bias, 1e-6, bt, o_codes, o_scales)
+    torch.cuda.synchronize()
+    g_codes = cache.view(torch.float8_e4m3fn).float().cpu().numpy().astype(np.float64)
+    _check_cache(g_codes, host(scales).astype(np.float64), o_codes, o_scales,
+                 np.ones(lay.n_k, bool), "decode cache")
+    # fp8 queries with the query scale folded into the weights (no keys to prepare)
+    q8, _, w_f, _ = dsa.dsa_indexer_prep(dev(q_raw), None, dev(wt), out_dtype=torch.float8_e4m3fn)
+    pq = o_prep.prepare_indexer_inputs(q_raw, np.zeros((1, 128)), wt, np.zeros(lay.n_q),
+                                       np.zeros(1), "fp8")
+    rs, re = o_win.row_windows(lay.cu_q, lay.cu_k)
+    kc = cache.view(torch.float8_e4m3fn)
+    say(f"decode from the fp8 cache: n_k={lay.n_k}")
+    G = host(dsa.dsa_indexer_scores(q8, kc, w_f, i32(rs), i32(re), k_scale=scales))
+    idx = host(dsa.dsa_indexer_topk(q8, kc, w_f, i32(rs), i32(re), 2048, k_scale=scales))
+    ndiff = 0
+    for t in range(lay.n_q):
+        a, b = int(rs[t]), int(re[t])
+        o, c = o_idx.score_row(pq["q"][t], o_codes[a:b], pq["w"][t], o_scales[a:b], with_cond=True)
+        check_scores(G[t, a:b], o, c, 2e-2, f"fp8 cache row {t}")
+        full = np.full(lay.n_k, -np.inf)
+        full[a:b] = o
+        tau = np.zeros(lay.n_k)
+        tau[a:b] = 2e-2 * np.maximum(np.abs(o), c / 128)
+        oi = o_topk.topk_row(full.astype(np.float32), a, b, 2048)
+        ndiff += check_topk_e2e(idx[t], oi, full, tau, f"fp8 cache row {t}")
+    say(f"  selection differs from the oracle's in {ndiff} columns (within tolerance)")

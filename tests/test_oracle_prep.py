@@ -226,3 +226,46 @@ def test_same_position_pair_is_rope_invariant():
         # an off-diagonal pair does change (the rope is not a no-op here)
         t, s = lay.n_q - 1, 0
         assert abs(pr["q"][t] @ pr["k"][s] - pn["q"][t] @ pn["k"][s]).max() > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# the fp8 index-key cache insert (norm -> quant -> slot)
+# ---------------------------------------------------------------------------
+def test_layer_norm_affine_vs_torch():
+    g = np.random.default_rng(20)
+    x = g.standard_normal((16, 128)) * 2 + 0.3
+    wgt, b = g.standard_normal(128), g.standard_normal(128)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (128,), torch.from_numpy(wgt),
+                                         torch.from_numpy(b), eps=1e-6).numpy()
+    np.testing.assert_allclose(prep.layer_norm_affine(x, wgt, b, 1e-6), ref, rtol=1e-12, atol=1e-12)
+    # weight 1 and bias 0 (the defaults) are the plain norm
+    np.testing.assert_array_equal(prep.layer_norm_affine(x, None, None), prep.layer_norm(x))
+
+
+def test_k_insert_slots_and_quantisation():
+    g = np.random.default_rng(21)
+    n_slots, D = 12, 128
+    codes = np.full((n_slots, D), 7.0)
+    scales = np.full(n_slots, 3.0)
+    k = g.standard_normal((5, D)) * np.array([1.0, 50.0, 1e-3, 0.0, 2.0])[:, None]
+    slots = np.array([3, -1, 11, 0, 12])          # a padding token and a slot past the cache
+    prep.k_norm_quant_insert(k, None, None, 1e-6, slots, codes, scales)
+    untouched = [i for i in range(n_slots) if i not in (3, 11, 0)]
+    assert np.all(codes[untouched] == 7.0) and np.all(scales[untouched] == 3.0)
+    # a zero row normalises to zero: codes 0 with scale 1
+    assert np.all(codes[0] == 0.0) and scales[0] == 1.0
+    for src, dst in ((0, 3), (2, 11)):
+        y = prep.layer_norm(k[src])
+        s = scales[dst]
+        m, _ = np.frexp(s)
+        assert m == 0.5 and np.abs(y).max() <= 448 * s < 2 * np.abs(y).max()
+        # the codes are e4m3 values and each is the nearest one to y / s
+        np.testing.assert_array_equal(prep.round_e4m3(codes[dst]), codes[dst])
+        ref = torch.from_numpy(y / s).to(torch.float8_e4m3fn).double().numpy()
+        np.testing.assert_array_equal(codes[dst], ref)
+    # the norm makes the insert invariant to an affine change of the raw key
+    c2, s2 = np.zeros((1, D)), np.zeros(1)
+    prep.k_norm_quant_insert(k[2:3] * 1e4 + 5.0, None, None, 0.0, [0], c2, s2)
+    c3, s3 = np.zeros((1, D)), np.zeros(1)
+    prep.k_norm_quant_insert(k[2:3], None, None, 0.0, [0], c3, s3)
+    np.testing.assert_array_equal(c2 * s2[:, None], c3 * s3[:, None])
