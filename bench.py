@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
 MLA_FLOP_PER_PAIR = 2 * 128 * (576 + 512)   # 278,528
 
 
@@ -118,11 +119,15 @@ def stage_bench(args, dsa, synth, np, torch):
     their inputs are not served from the 256 MB last-level cache."""
     dev = "cuda"
     fp8_cache = args.workload == "decode_fp8"
-    w = synth.WORKLOADS["decode" if fp8_cache else args.workload.replace("_stages", "")]
+    mx = args.workload == "mxfp4_64k"
+    base = "decode" if fp8_cache else ("fp8_64k" if mx else args.workload.replace("_stages", ""))
+    w = synth.WORKLOADS[base]
+    if mx:  # the 64K prefill with MXFP4 indexer operands (no index rope)
+        w = dataclasses.replace(w, dtype="mxfp4")
     lay = synth.layout(w)
     i32 = lambda x: torch.from_numpy(np.asarray(x, np.int32)).to(dev)
     inp = synth.device_inputs(w, dev, lay)
-    tdt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
+    tdt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "mxfp4": "mxfp4"}[w.dtype]
     rs, re = dsa.dsa_row_windows(i32(lay.cu_q), i32(lay.cu_k), lay.n_q)
     insert_ms = None
     if fp8_cache:
@@ -172,7 +177,7 @@ def stage_bench(args, dsa, synth, np, torch):
     fused = True                     # the fused indexer + top-k: decode and prefill kernels
     if fused:
         idx2 = torch.empty_like(idx)
-        code = 1 if w.dtype == "bf16" else 2
+        code = {"bf16": 1, "fp8": 2, "mxfp4": 3}[w.dtype]
         fws = torch.empty(max(dsa.indexer_topk_workspace(lay.n_q, lay.n_k, w.n_heads, w.head_dim,
                                                          code, K), 1), dtype=torch.uint8, device=dev)
         fns["indexer_topk"] = lambda: dsa.dsa_indexer_topk(q, k, wt, rs, re, K, k_scale=ks, out=idx2,
@@ -198,15 +203,15 @@ def stage_bench(args, dsa, synth, np, torch):
     pairs = int((re_h - rs_h).sum())
     sel = int((idx >= 0).sum().item())
     hd = w.n_heads * w.head_dim
-    elt = 1 if w.dtype == "fp8" else 2
+    elt = {"bf16": 2.0, "fp8": 1.0, "mxfp4": 0.5 + 1 / 32}[w.dtype]   # bytes per element (+ scales)
     idx_flop = pairs * 2 * hd
-    key_bytes = lay.n_k * (w.head_dim * elt + (4 if w.dtype == "fp8" else 0))  # codes + scale
-    idx_bytes = lay.n_q * hd * elt + key_bytes + lay.n_q * w.n_heads * 4 + pairs * 4
+    key_bytes = int(lay.n_k * (w.head_dim * elt + (4 if w.dtype == "fp8" else 0)))  # codes + scale
+    idx_bytes = int(lay.n_q * hd * elt) + key_bytes + lay.n_q * w.n_heads * 4 + pairs * 4
     topk_bytes = pairs * 4 + lay.n_q * K * 4
     mla_flop = sel * MLA_FLOP_PER_PAIR
     gather = sel * w.d_qk * 2
     mla_compulsory = mq.numel() * 2 + out.numel() * 2 + lse.numel() * 4 + idx.numel() * 4
-    mfma_peak = FP8_PEAK_TFLOPS if w.dtype == "fp8" else BF16_PEAK_TFLOPS
+    mfma_peak = {"bf16": BF16_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS, "mxfp4": FP4_PEAK_TFLOPS}[w.dtype]
     t = {n: v * 1e-3 for n, v in ms.items()}
     if fused:
         assert torch.equal(idx, idx2), "fused and unfused indexer + top-k disagree"
@@ -293,7 +298,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill4k",
                     choices=["prefill4k", "prefill4k_stages", "thd", "decode", "decode_fp8",
-                             "fp8_64k"],
+                             "fp8_64k", "mxfp4_64k"],
                     help="prefill4k: the benchmark step; the others time each stage on its own")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -51,6 +51,9 @@ typedef enum dsa_dtype {
   DSA_DTYPE_F32 = 0,      /* float32                                    */
   DSA_DTYPE_BF16 = 1,     /* bfloat16                                   */
   DSA_DTYPE_FP8_E4M3 = 2, /* OCP float8 e4m3fn (max 448), one byte each */
+  DSA_DTYPE_MXFP4 = 3,    /* OCP MXFP4: e2m1 values, two per byte (even
+                             element in the low nibble), one E8M0 scale
+                             byte (2^(byte - 127)) per 32 values       */
 } dsa_dtype;
 
 /* Human-readable name of a status code (static string). */
@@ -106,12 +109,22 @@ int dsa_row_windows(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
  *   q_raw   f32 [n_q, n_heads, head_dim]   k_raw f32 [n_k, head_dim]
  *   w       f32 [n_q, n_heads]             pos_q int32 [n_q], pos_k int32 [n_k]
  *           (positions inside each sequence; ignored when rope_dim == 0, may be NULL then)
- *   dtype   output type of q_out / k_out: F32, BF16 or FP8_E4M3.
+ *   dtype   output type of q_out / k_out: F32, BF16, FP8_E4M3 or MXFP4.
  *   q_out   [n_q, n_heads, head_dim] of dtype;  k_out [n_k, head_dim] of dtype.
- *   w_out   f32 [n_q, n_heads]: w (F32/BF16) or w * q_scale (FP8_E4M3).
- *   k_scale_out  f32 [n_k]: the key scale for FP8_E4M3, else ignored (may be NULL).
+ *   w_out   f32 [n_q, n_heads]: w (F32/BF16/MXFP4) or w * q_scale (FP8_E4M3).
+ *   k_scale_out  f32 [n_k]: the key scale for FP8_E4M3; for MXFP4 the E8M0
+ *           scale bytes [n_k, head_dim / 32]; else ignored (may be NULL).
  * Scale rule (FP8_E4M3): s = the smallest power of two with amax <= 448 * s
  * (s = 1 for an all-zero block); codes = round-to-nearest-even(x / s).
+ * MXFP4 (the "MXFP4 keys with MXFP4 queries" indexer of KimiK3DSAIndexer.__init__,
+ * scales not foldable into the per-head weights): the OCP microscaling
+ * conversion per 32 values -- X = 2^(floor(log2 amax) - 2), codes =
+ * round-to-nearest-even(x / X) on the e2m1 grid, saturating at 6; q_out holds,
+ * per token, the n_heads rows of head_dim / 2 code bytes followed by the
+ * n_heads scale groups of head_dim / 32 bytes; k_out [n_k, head_dim / 2] code
+ * bytes.  MXFP4 requires rope_dim == 0 (on the page the fp4 keys need the
+ * fused key insert, which runs without index rope) and head_dim % 64 == 0.
+ * n_k may be 0 (queries only, e.g. a decode step over a key cache).
  * Supported: head_dim <= 256 and even; rope_dim even and <= head_dim.
  */
 int dsa_indexer_prep(const float* q_raw, const float* k_raw, const float* w,
@@ -163,15 +176,21 @@ int dsa_indexer_k_insert(const void* k_raw, int32_t k_dtype, const float* norm_w
  *     score[t, s] = k_scale[s] * sum_h w[t, h] * max(0, q[t, h, :] . k[s, :])
  * for row_starts[t] <= s < row_ends[t].
  *
- *   q        [n_q, n_heads, head_dim] of dtype
- *   k        [n_k, head_dim] of dtype
- *   k_scale  f32 [n_k] (FP8_E4M3 only; must be NULL otherwise)
+ *   q        [n_q, n_heads, head_dim] of dtype (MXFP4: the layout of
+ *            dsa_indexer_prep's q_out, n_heads * (head_dim / 2 + head_dim / 32)
+ *            bytes per token)
+ *   k        [n_k, head_dim] of dtype (MXFP4: head_dim / 2 code bytes per key)
+ *   k_scale  f32 [n_k] (FP8_E4M3), or the E8M0 bytes [n_k, head_dim / 32]
+ *            (MXFP4, 4-byte aligned); must be NULL otherwise
  *   w        f32 [n_q, n_heads]
+ * MXFP4: score = sum_h w * max(0, sum over the 32-value blocks b of
+ * 2^(sq_b - 127) 2^(sk_b - 127) sum_{d in b} q4 k4) -- the matrix core applies
+ * both block scales (v_mfma_scale_f32_32x32x64_f8f6f4 with e2m1 operands).
  *   scores   f32 [n_q, ld_scores], ld_scores >= n_k.  ONLY in-window entries are
  *            written; everything else is left untouched (it may hold garbage).
- * Accumulation is fp32.  Supported: BF16 and FP8_E4M3 with head_dim == 128 and
- * 1 <= n_heads <= 64 (matrix-core path); F32 with head_dim <= 256, n_heads <= 64
- * and n_heads * head_dim <= 8192.
+ * Accumulation is fp32.  Supported: BF16, FP8_E4M3 and MXFP4 with head_dim ==
+ * 128 and 1 <= n_heads <= 64 (MXFP4: n_heads % 4 == 0) (matrix-core path); F32
+ * with head_dim <= 256, n_heads <= 64 and n_heads * head_dim <= 8192.
  */
 int dsa_indexer_scores(const void* q, const void* k, const float* k_scale,
                        const float* w, const int32_t* row_starts,
@@ -216,7 +235,7 @@ int dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_starts,
  * not an output.  workspace: at least dsa_indexer_topk_workspace_size(...) bytes,
  * 256-byte aligned (NULL when that size is 0); its contents on entry do not
  * matter.
- * The scores never reach memory for bf16 and fp8 with index_topk <= 2048:
+ * The scores never reach memory for bf16, fp8 and MXFP4 with index_topk <= 2048:
  *   More than 256 rows (prefill): fused, no workspace -- four rows per
  *   workgroup share each chunk of keys, and each row keeps its candidates
  *   (scores above a running floor, shrunk in place to their exact top k when

@@ -52,6 +52,14 @@ def round_f32(x) -> np.ndarray:
     return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
 
 
+def round_e2m1(x) -> np.ndarray:
+    """OCP FP4 E2M1 (the MXFP4 element type): 1 mantissa bit, min normal 1,
+    subnormal step 0.5, max 6; values are clamped to +-6 before rounding
+    (the MX conversion saturates)."""
+    x = np.clip(np.asarray(x, np.float64), -6.0, 6.0)
+    return _round_format(x, 1, 0)
+
+
 def round_e4m3(x) -> np.ndarray:
     """OCP E4M3FN: 3 mantissa bits, min normal 2**-6, subnormal step 2**-9,
     max 448.  Values are clamped to +-448 before rounding."""
@@ -140,6 +148,28 @@ def quant_e4m3_blocks(x, block: int):
     return codes.reshape(x.shape), s
 
 
+def mx_scale_exponent(amax) -> np.ndarray:
+    """MXFP4 shared scale (OCP Microscaling format, block of 32): X = 2^e with
+    e = floor(log2 amax) - 2 (2 = the largest exponent of E2M1); amax = 0 gives
+    e = 0.  The E8M0 byte is e + 127."""
+    amax = np.asarray(amax, np.float64)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))   # amax = m 2^e, 0.5 <= m < 1
+    return np.where(amax > 0, (e - 1) - 2, 0).astype(np.int64)
+
+
+def quant_mxfp4_blocks(x, block: int = 32):
+    """MXFP4 along the last axis: returns (codes, scale_exp) with codes the E2M1
+    values (float64) and scale_exp [..., D/block] the scale exponents;
+    x ~= codes * 2^scale_exp per block (values of |x| / 2^e in [6, 8) saturate)."""
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    assert D % block == 0
+    xb = x.reshape(x.shape[:-1] + (D // block, block))
+    e = mx_scale_exponent(np.abs(xb).max(axis=-1))
+    codes = round_e2m1(xb / np.exp2(e)[..., None].astype(np.float64))
+    return codes.reshape(x.shape), e
+
+
 def fold_q_scale(w, q_scale) -> np.ndarray:
     """score() folds the per-(token, head) query scale into the head weights."""
     return np.asarray(w, np.float64) * np.asarray(q_scale, np.float64)
@@ -174,6 +204,16 @@ def prepare_indexer_inputs(q_raw, k_raw, w, positions_q, positions_k, dtype: str
         k8, sk = quant_e4m3_blocks(k, D)          # sk [Nk, 1]
         wf = round_f32(fold_q_scale(w, sq[..., 0]))
         return dict(q=q8, k=k8, w=wf, k_scale=sk[:, 0])
+    if dtype == "mxfp4":
+        # block scales per 32 dims on both sides (not foldable into per-head
+        # weights): the operands are handed over dequantised, with the codes
+        # and scale exponents alongside
+        q4, eq = quant_mxfp4_blocks(q)            # eq [Nq, H, D/32]
+        k4, ek = quant_mxfp4_blocks(k)            # ek [Nk, D/32]
+        qd = q4 * np.repeat(np.exp2(eq.astype(np.float64)), 32, axis=-1)
+        kd = k4 * np.repeat(np.exp2(ek.astype(np.float64)), 32, axis=-1)
+        return dict(q=qd, k=kd, w=round_f32(w), k_scale=None, q_codes=q4, q_exp=eq,
+                    k_codes=k4, k_exp=ek)
     raise ValueError(dtype)
 
 

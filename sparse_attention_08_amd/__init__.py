@@ -20,7 +20,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa.so")
 
-DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3, DTYPE_MXFP4 = 0, 1, 2, 3
 
 _lib = None
 
@@ -122,9 +122,19 @@ def _check(status: int, what: str):
 
 
 def _dtype_code(t) -> int:
+    """Operand format of a tensor; MXFP4 operands are uint8 buffers."""
     import torch
     return {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16,
-            torch.float8_e4m3fn: DTYPE_FP8_E4M3}[t.dtype]
+            torch.float8_e4m3fn: DTYPE_FP8_E4M3, torch.uint8: DTYPE_MXFP4}[t.dtype]
+
+
+def _indexer_dims(q, k, w):
+    """(n_q, n_heads, head_dim): from q [n_q, H, D], or for MXFP4 (uint8 q of
+    H * (D/2 + D/32) bytes per token) from w [n_q, H] and k [n_k, D/2]."""
+    import torch
+    if q.dtype == torch.uint8:
+        return q.shape[0], w.shape[1], k.shape[1] * 2
+    return q.shape
 
 
 def _lib_or_load():
@@ -151,23 +161,32 @@ def dsa_row_windows(cu_seqlens_q, cu_seqlens_k, n_rows: int, causal: bool = True
 def dsa_indexer_prep(q_raw, k_raw, w, pos_q=None, pos_k=None, out_dtype=None, rope_dim: int = 0,
                      rope_main_dim: int = 0, rope_theta: float = 1e4, eps: float = 1e-6,
                      stream=None):
-    """Returns (q, k, w_out, k_scale) in out_dtype (k_scale is None unless fp8;
-    k and k_scale are None when k_raw is None: queries only, e.g. a decode step
-    over a key cache)."""
+    """Returns (q, k, w_out, k_scale) in out_dtype (k_scale is None unless fp8 or
+    mxfp4; k and k_scale are None when k_raw is None: queries only, e.g. a
+    decode step over a key cache).  out_dtype "mxfp4": q uint8 [n_q, H*(D/2+D/32)],
+    k uint8 [n_k, D/2], k_scale uint8 [n_k, D/32] (E8M0)."""
     import torch
     lib = _lib_or_load()
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     n_q, H, D = q_raw.shape
     n_k = 0 if k_raw is None else k_raw.shape[0]
+    dev_ = q_raw.device
     with _on(stream):
-        q = torch.empty((n_q, H, D), dtype=out_dtype, device=q_raw.device)
-        k = None if k_raw is None else torch.empty((n_k, D), dtype=out_dtype, device=q_raw.device)
-        w_out = torch.empty((n_q, H), dtype=torch.float32, device=q_raw.device)
-        ks = torch.empty(n_k, dtype=torch.float32, device=q_raw.device) \
-            if out_dtype == torch.float8_e4m3fn and k_raw is not None else None
+        if out_dtype == "mxfp4":
+            code = DTYPE_MXFP4
+            q = torch.empty((n_q, H * (D // 2 + D // 32)), dtype=torch.uint8, device=dev_)
+            k = None if k_raw is None else torch.empty((n_k, D // 2), dtype=torch.uint8, device=dev_)
+            ks = None if k_raw is None else torch.empty((n_k, D // 32), dtype=torch.uint8, device=dev_)
+        else:
+            q = torch.empty((n_q, H, D), dtype=out_dtype, device=dev_)
+            code = _dtype_code(q)
+            k = None if k_raw is None else torch.empty((n_k, D), dtype=out_dtype, device=dev_)
+            ks = torch.empty(n_k, dtype=torch.float32, device=dev_) \
+                if out_dtype == torch.float8_e4m3fn and k_raw is not None else None
+        w_out = torch.empty((n_q, H), dtype=torch.float32, device=dev_)
     _check(lib.dsa_indexer_prep(_ptr(q_raw), _ptr(k_raw), _ptr(w), _ptr(pos_q), _ptr(pos_k),
                                 n_q, n_k, H, D, rope_dim, rope_main_dim, rope_theta, eps,
-                                _dtype_code(q), _ptr(q), _ptr(k), _ptr(w_out), _ptr(ks),
+                                code, _ptr(q), _ptr(k), _ptr(w_out), _ptr(ks),
                                 _stream(stream)), "dsa_indexer_prep")
     return q, k, w_out, ks
 
@@ -191,7 +210,7 @@ def dsa_indexer_scores(q, k, w, row_starts, row_ends, k_scale=None, scores=None,
     """scores [n_q, ld] fp32; only in-window entries are written."""
     import torch
     lib = _lib_or_load()
-    n_q, H, D = q.shape
+    n_q, H, D = _indexer_dims(q, k, w)
     n_k = k.shape[0]
     if scores is None:
         ld = n_k if ld is None else ld
@@ -228,7 +247,7 @@ def dsa_indexer_topk(q, k, w, row_starts, row_ends, index_topk: int, k_scale=Non
                      workspace=None, stream=None):
     import torch
     lib = _lib_or_load()
-    n_q, H, D = q.shape
+    n_q, H, D = _indexer_dims(q, k, w)
     n_k = k.shape[0]
     need = lib.dsa_indexer_topk_workspace_size(n_q, n_k, H, D, _dtype_code(q), index_topk)
     with _on(stream):
@@ -250,7 +269,7 @@ def dsa_indexer_topk_noalloc(q, k, w, row_starts, row_ends, index_topk: int, k_s
     (no device allocation by the library; out is allocated here unless given)."""
     import torch
     lib = _lib_or_load()
-    n_q, H, D = q.shape
+    n_q, H, D = _indexer_dims(q, k, w)
     n_k = k.shape[0]
     if out is None:
         with _on(stream):

@@ -22,11 +22,11 @@ int check_indexer(const void* q, const void* k, const float* k_scale, const floa
                   const int32_t* rs, const int32_t* re, int64_t n_q, int64_t n_k,
                   int32_t n_heads, int32_t head_dim, int32_t dtype) {
   if (n_q < 0 || n_k < 0 || n_k > INT32_MAX || n_q > INT32_MAX) return DSA_ERR_INVALID_ARG;
-  if (dtype < DSA_DTYPE_F32 || dtype > DSA_DTYPE_FP8_E4M3) return DSA_ERR_INVALID_ARG;
+  if (dtype < DSA_DTYPE_F32 || dtype > DSA_DTYPE_MXFP4) return DSA_ERR_INVALID_ARG;
   if (n_heads < 1 || head_dim < 1) return DSA_ERR_INVALID_ARG;
   if (n_q > 0 && (!q || !w || !rs || !re)) return DSA_ERR_INVALID_ARG;
   if (n_q > 0 && n_k > 0 && !k) return DSA_ERR_INVALID_ARG;
-  if (dtype == DSA_DTYPE_FP8_E4M3) {
+  if (dtype == DSA_DTYPE_FP8_E4M3 || dtype == DSA_DTYPE_MXFP4) {
     if (n_q > 0 && n_k > 0 && !k_scale) return DSA_ERR_INVALID_ARG;
   } else if (k_scale) {
     return DSA_ERR_INVALID_ARG;
@@ -36,8 +36,11 @@ int check_indexer(const void* q, const void* k, const float* k_scale, const floa
     if (head_dim > 256 || int64_t(n_heads) * head_dim > 8192) return DSA_ERR_UNSUPPORTED;
   } else {
     if (head_dim != 128) return DSA_ERR_UNSUPPORTED;
+    // MXFP4 tokens are n_heads * 68 bytes: 16-byte fragments need n_heads % 4 == 0
+    if (dtype == DSA_DTYPE_MXFP4 && (n_heads % 4) != 0) return DSA_ERR_UNSUPPORTED;
     const uintptr_t al = dtype == DSA_DTYPE_FP8_E4M3 ? 32 : 16;
     if (!aligned(q, al) || !aligned(k, al)) return DSA_ERR_UNSUPPORTED;
+    if (dtype == DSA_DTYPE_MXFP4 && !aligned(k_scale, 4)) return DSA_ERR_UNSUPPORTED;
   }
   return DSA_OK;
 }
@@ -92,10 +95,14 @@ int dsa_indexer_prep(const float* q_raw, const float* k_raw, const float* w,
                      float rope_theta, float eps, int32_t dtype, void* q_out, void* k_out,
                      float* w_out, float* k_scale_out, void* stream) {
   if (n_q < 0 || n_k < 0 || n_heads < 1 || head_dim < 1) return DSA_ERR_INVALID_ARG;
-  if (dtype < DSA_DTYPE_F32 || dtype > DSA_DTYPE_FP8_E4M3) return DSA_ERR_INVALID_ARG;
+  if (dtype < DSA_DTYPE_F32 || dtype > DSA_DTYPE_MXFP4) return DSA_ERR_INVALID_ARG;
   if (n_q > 0 && (!q_raw || !w || !q_out || !w_out)) return DSA_ERR_INVALID_ARG;
   if (n_k > 0 && (!k_raw || !k_out)) return DSA_ERR_INVALID_ARG;
-  if (dtype == DSA_DTYPE_FP8_E4M3 && n_k > 0 && !k_scale_out) return DSA_ERR_INVALID_ARG;
+  if ((dtype == DSA_DTYPE_FP8_E4M3 || dtype == DSA_DTYPE_MXFP4) && n_k > 0 && !k_scale_out)
+    return DSA_ERR_INVALID_ARG;
+  // MXFP4 keys go through the fused insert path of the pages, which has no index rope
+  if (dtype == DSA_DTYPE_MXFP4 && (rope_dim != 0 || head_dim % 64 != 0))
+    return DSA_ERR_UNSUPPORTED;
   if (rope_dim < 0 || (rope_dim & 1) || rope_dim > head_dim) return DSA_ERR_INVALID_ARG;
   if (rope_dim > 0) {
     if (rope_main_dim < rope_dim || !(rope_theta > 0.0f)) return DSA_ERR_INVALID_ARG;

@@ -34,6 +34,7 @@ namespace dsa {
 namespace {
 
 using ixcore::OpBf16;
+using ixcore::OpFp4;
 using ixcore::OpFp8;
 using ixcore::PendingTile;
 using ixcore::QueryRow;
@@ -85,13 +86,13 @@ __device__ __forceinline__ void rows_chunk(int c, int nchunks, int key0, int hi,
                                            const QueryRow<Op, MT>& qr, bool active, int a, int b,
                                            __amdgpu_buffer_rsrc_t srow, int wave, int lane,
                                            const RowsDma<Op>& dma, PendingTile<Op, MT>& pd) {
-  float ksc[kChunkTiles];
+  typename Op::kscale_t ksc[kChunkTiles];
   ixcore::chunk_key_scales<Op, kChunkKeys>(k_scale, key0, hi, lane, ksc);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA pieces of chunk c landed
   __syncthreads();                // ... everyone's; all waves are done with chunk c-1
   if (c + 1 < nchunks) dma.issue(kbuf<kNn>(), k, key0 + kChunkKeys, n_k, wave, lane);
   if (!active || key0 >= b || key0 + kChunkKeys <= a) return;
-  auto put = [&](int s0, float p, float ks) { store_scores(srow, a, s0, lane, p * ks); };
+  auto put = [&](int s0, float p) { store_scores(srow, a, s0, lane, p); };
   ixcore::chunk_tile_pairs<Op, MT, kChunkKeys>(kbuf<kCur>(), key0, a, b, qr, lane, ksc, pd, put);
 }
 
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(
     rows_chunk<Op, MT, 1, 0>(c + 1, nchunks, lo + (c + 1) * kChunkKeys, hi, n_k, k, k_scale, qr,
                              active, a, b, srow, wave, lane, dma, pd);
   }
-  if (pd.live) store_scores(srow, a, pd.s0, lane, qr.epilogue(pd.acc) * pd.ksc);
+  if (pd.live) store_scores(srow, a, pd.s0, lane, qr.epilogue(pd.acc) * Op::post(pd.ksc));
 }
 
 // ---------------------------------------------------------------------------
@@ -189,13 +190,10 @@ __global__ __launch_bounds__(kSplitThreads) void indexer_rowsplit_kernel(
 
   QueryRow<Op, MT> qr;
   qr.load(q, w, t, H, lane);
-  constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
-  auto put = [&](int i, float p, float ks) {
+  constexpr bool kScaled = Op::kKeyScale;  // fp8 / fp4 keys carry a scale
+  auto put = [&](int i, float p) {
     const int s = a + i * kKeyTile + (lane & 31);
-    if (lane < 32 && s < b && i < i1) {
-      if constexpr (kScaled) p *= ks;
-      scores[t * ld + s] = p;
-    }
+    if (lane < 32 && s < b && i < i1) scores[t * ld + s] = p;
   };
   typedef ixcore::LdsTile<Op, kScaled> T;
   __shared__ __attribute__((aligned(16))) uint8_t tbuf[kWaves][kSplitBufs * T::kBytes];
@@ -279,6 +277,11 @@ hipError_t launch_indexer_scores(const void* q, const void* k, const float* k_sc
                                         n_heads, scores, ld, stream)
                : launch_mfma<OpBf16, 2>(q, k, nullptr, w, row_starts, row_ends, n_q, n_k,
                                         n_heads, scores, ld, stream);
+  if (dtype == 3)
+    return one ? launch_mfma<OpFp4, 1>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k,
+                                       n_heads, scores, ld, stream)
+               : launch_mfma<OpFp4, 2>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k,
+                                       n_heads, scores, ld, stream);
   return one ? launch_mfma<OpFp8, 1>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k,
                                      n_heads, scores, ld, stream)
              : launch_mfma<OpFp8, 2>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k,

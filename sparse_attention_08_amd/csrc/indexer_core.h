@@ -17,50 +17,103 @@
 namespace dsa {
 namespace ixcore {
 
+// Operand traits.  Keys of the fp8 and fp4 paths carry a 4-byte scale per key
+// (kscale_t): fp8 one fp32 power of two that multiplies the score (post), fp4
+// the four E8M0 bytes of its 32-dim blocks, which the matrix core applies
+// itself (kMx: scaled MFMA with a per-lane scale on each operand).
 struct OpBf16 {
   typedef bf16x8_t frag_t;
+  typedef float kscale_t;
   static constexpr int kRowBytes = 256;  // 128 bf16
   static constexpr int kFragBytes = 16;  // 8 bf16 per lane per K-step of 16
   static constexpr int kSteps = 8;
-  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c) {
+  static constexpr bool kKeyScale = false, kMx = false;
+  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c, int, int) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  __device__ static __forceinline__ kscale_t kscale_one() { return 1.0f; }
+  __device__ static __forceinline__ kscale_t load_kscale(const float*, int64_t) { return 1.0f; }
+  __device__ static __forceinline__ float post(kscale_t) { return 1.0f; }
 };
 
 struct OpFp8 {
   typedef i32x8_t frag_t;
+  typedef float kscale_t;
   static constexpr int kRowBytes = 128;  // 128 e4m3
   static constexpr int kFragBytes = 32;  // 32 e4m3 per lane per K-step of 64
   static constexpr int kSteps = 2;
-  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c) {
+  static constexpr bool kKeyScale = true, kMx = false;
+  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c, int, int) {
     // format 0 = e4m3 for both operands; block scales 127 = 2^0 (no scaling)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
   }
+  __device__ static __forceinline__ kscale_t kscale_one() { return 1.0f; }
+  __device__ static __forceinline__ kscale_t load_kscale(const float* p, int64_t i) { return p[i]; }
+  __device__ static __forceinline__ float post(kscale_t ks) { return ks; }
+};
+
+// MXFP4 (OCP microscaling): 128 packed E2M1 values per row (64 bytes), one E8M0
+// scale per 32 dims.  A K-step of the 32x32x64 MFMA gives each lane 32 values
+// -- exactly one block -- of its row (lanes 0-31: dims 64 st .. +32, lanes
+// 32-63: the next 32), so the block scale is the lane's scale operand.
+struct OpFp4 {
+  typedef i32x4_t frag_t;  // 32 e2m1 per lane per K-step of 64
+  typedef uint32_t kscale_t;
+  static constexpr int kRowBytes = 64;
+  static constexpr int kFragBytes = 16;
+  static constexpr int kSteps = 2;
+  static constexpr bool kKeyScale = true, kMx = true;
+  __device__ static __forceinline__ f32x16_t mfma(frag_t a, frag_t b, f32x16_t c, int sa,
+                                                  int sb) {
+    // format 4 = e2m1 for both operands (the instruction reads four registers
+    // of each: the upper half of the 8-register operand is not used)
+    const i32x8_t a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3);
+    const i32x8_t b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+  }
+  __device__ static __forceinline__ kscale_t kscale_one() { return 0x7F7F7F7Fu; }  // 2^0 x 4
+  __device__ static __forceinline__ kscale_t load_kscale(const float* p, int64_t i) {
+    return reinterpret_cast<const uint32_t*>(p)[i];
+  }
+  __device__ static __forceinline__ float post(kscale_t) { return 1.0f; }
 };
 
 constexpr int kKeyTile = 32;
 
 // q[t] fragments and the matching head weights of one query row, per lane.
+// MXFP4 queries: token t's H code rows (64 bytes each) are followed by its H
+// scale quads (4 E8M0 bytes each), so a token takes H * 68 bytes.
 template <class Op, int MT>
 struct QueryRow {
   typename Op::frag_t qa[MT][Op::kSteps];
   float wv[MT][16];
+  int qs[Op::kMx ? MT : 1][Op::kSteps];  // MXFP4: the lane's block scale per (tile, step)
+  int kshift;                            // MXFP4: bit offset of the lane's key scale in step 0
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ q,
                                        const float* __restrict__ w, int64_t t, int H,
                                        int lane) {
     const int half = lane >> 5;
+    constexpr int64_t kTok = Op::kMx ? int64_t(Op::kRowBytes + Op::kSteps * 2) : Op::kRowBytes;
+    kshift = 8 * half;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int h = mt * 32 + (lane & 31);
       const bool ok = h < H;
-      const uint8_t* base =
-          q + (t * H + (ok ? h : 0)) * int64_t(Op::kRowBytes) + half * Op::kFragBytes;
+      const uint8_t* base = Op::kMx ? q + t * H * kTok + (ok ? h : 0) * Op::kRowBytes +
+                                          half * Op::kFragBytes
+                                    : q + (t * H + (ok ? h : 0)) * int64_t(Op::kRowBytes) +
+                                          half * Op::kFragBytes;
 #pragma unroll
       for (int st = 0; st < Op::kSteps; ++st) {
         typename Op::frag_t v = *reinterpret_cast<const typename Op::frag_t*>(
             base + st * 2 * Op::kFragBytes);
         qa[mt][st] = ok ? v : typename Op::frag_t{};
+        if constexpr (Op::kMx) {
+          const uint8_t* sc = q + t * H * kTok + int64_t(H) * Op::kRowBytes +
+                              (ok ? h : 0) * (Op::kSteps * 2) + 2 * st + half;
+          qs[mt][st] = ok ? int(*sc) : 127;
+        }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -70,15 +123,20 @@ struct QueryRow {
     }
   }
 
-  // Logits of the 32 keys whose fragments are in kb (heads on M, keys on N).
+  // Logits of the 32 keys whose fragments are in kb (heads on M, keys on N);
+  // ks: the lane's key scale (MXFP4: its four block scales).
   __device__ __forceinline__ void mma(const typename Op::frag_t (&kb)[Op::kSteps],
-                                      f32x16_t (&acc)[MT]) const {
+                                      typename Op::kscale_t ks, f32x16_t (&acc)[MT]) const {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
 #pragma unroll
-    for (int st = 0; st < Op::kSteps; ++st)
+    for (int st = 0; st < Op::kSteps; ++st) {
+      int sb = 0;
+      if constexpr (Op::kMx) sb = int((uint32_t(ks) >> (kshift + 16 * st)) & 0xFFu);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mfma(qa[mt][st], kb[st], acc[mt]);
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = Op::mfma(qa[mt][st], kb[st], acc[mt], Op::kMx ? qs[Op::kMx ? mt : 0][st] : 0, sb);
+    }
   }
 
   // ReLU, head weights and the head sum; lanes l and l^32 both end with the
@@ -99,10 +157,12 @@ struct QueryRow {
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
 
-  __device__ __forceinline__ float score(const typename Op::frag_t (&kb)[Op::kSteps]) const {
+  // The tile's scores: epilogue times the key's post scale (fp8).
+  __device__ __forceinline__ float score(const typename Op::frag_t (&kb)[Op::kSteps],
+                                         typename Op::kscale_t ks) const {
     f32x16_t acc[MT];
-    mma(kb, acc);
-    return epilogue(acc);
+    mma(kb, ks, acc);
+    return epilogue(acc) * Op::post(ks);
   }
 };
 
@@ -121,18 +181,18 @@ __device__ __forceinline__ void load_key_tile(const uint8_t* __restrict__ k, int
     kb[st] = *reinterpret_cast<const typename Op::frag_t*>(src + st * 2 * Op::kFragBytes);
 }
 
-// A 32-key tile and, for fp8 keys, the scale of the lane's key.
+// A 32-key tile and the scale of the lane's key.
 template <class Op, bool kScaled>
 struct KeyTile {
   typename Op::frag_t kb[Op::kSteps];
-  float ks;
+  typename Op::kscale_t ks = Op::kscale_one();
   __device__ __forceinline__ void load(const uint8_t* __restrict__ k,
                                        const float* __restrict__ k_scale, int s0, int b,
                                        int lane) {
     load_key_tile<Op>(k, s0, b, lane, kb);
     if constexpr (kScaled) {
       const int s = s0 + (lane & 31);
-      ks = k_scale[s < b ? s : s0];
+      ks = Op::load_kscale(k_scale, s < b ? s : s0);
     }
   }
 };
@@ -143,8 +203,8 @@ struct KeyTile {
 // unconditionally (past the last tile the last tile is reloaded and its score
 // dropped), so each loop iteration has the same loads in the same order and
 // the compiler's memory-counter waits stay exact instead of draining the
-// prefetch.  put(i, score, scale) receives each tile's scores (lanes l and l^32
-// both hold key l%32).
+// prefetch.  put(i, score) receives each tile's scores, key scale applied
+// (lanes l and l^32 both hold key l%32).
 template <class Op, int MT, bool kScaled, class Put>
 __device__ __forceinline__ void stream_tiles(const QueryRow<Op, MT>& qr,
                                              const uint8_t* __restrict__ k,
@@ -156,15 +216,13 @@ __device__ __forceinline__ void stream_tiles(const QueryRow<Op, MT>& qr,
   ta.load(k, k_scale, key0(first), b, lane);
   tb.load(k, k_scale, key0(first + step), b, lane);
   for (int i = first;; i += 2 * step) {
-    const float pa = qr.score(ta.kb);
-    const float ka = ta.ks;
+    const float pa = qr.score(ta.kb, ta.ks);
     ta.load(k, k_scale, key0(i + 2 * step), b, lane);
-    put(i, pa, ka);
+    put(i, pa);
     if (i + step >= nt) break;
-    const float pb = qr.score(tb.kb);
-    const float kbs = tb.ks;
+    const float pb = qr.score(tb.kb, tb.ks);
     tb.load(k, k_scale, key0(i + 3 * step), b, lane);
-    put(i + step, pb, kbs);
+    put(i + step, pb);
     if (i + 2 * step >= nt) break;
   }
 }
@@ -195,7 +253,9 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // LDS slot (in 16-byte pieces) of piece cc of tile-local key kl (an involution).
 template <class Op>
 __device__ __forceinline__ int kswz(int kl, int cc) {
-  return Op::kRowBytes == 256 ? (cc ^ (kl & 15)) : (cc ^ ((kl >> 1) & 7));
+  return Op::kRowBytes == 256   ? (cc ^ (kl & 15))
+         : Op::kRowBytes == 128 ? (cc ^ ((kl >> 1) & 7))
+                                : (cc ^ ((kl >> 2) & 3));
 }
 
 template <class Op, bool kScaled>
@@ -235,7 +295,7 @@ struct LdsTile {
   // MFMA fragments (and the scale) of the lane's key l % 32
   __device__ static __forceinline__ void read(const uint8_t* buf, int lane,
                                               typename Op::frag_t (&kb)[Op::kSteps],
-                                              float& ks) {
+                                              typename Op::kscale_t& ks) {
     const int kl = lane & 31;
     const uint8_t* row = buf + kl * Op::kRowBytes;
     constexpr int kFragPieces = Op::kFragBytes / 16;
@@ -251,7 +311,8 @@ struct LdsTile {
                                     __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
-    if constexpr (kScaled) ks = reinterpret_cast<const float*>(buf + kKeyBytes)[kl];
+    if constexpr (kScaled)
+      ks = reinterpret_cast<const typename Op::kscale_t*>(buf + kKeyBytes)[kl];
   }
 };
 
@@ -267,8 +328,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // wave's sequence goes to buffer j % NB; the DMA into a buffer is issued after
 // the MFMAs of the tile it held, so its reads are done.  Past the last tile the
 // last tile is fetched again (every iteration issues the same loads, so the wait
-// count is fixed), and everything is drained before return.  put(i, score,
-// scale) receives each tile's scores (lanes l and l^32 both hold key l%32).
+// count is fixed), and everything is drained before return.  put(i, score)
+// receives each tile's scores, key scale applied (lanes l and l^32 both hold
+// key l%32).
 template <class Op, int MT, bool kScaled, int NB, class Put>
 __device__ __forceinline__ void stream_tiles_lds(const QueryRow<Op, MT>& qr,
                                                  const uint8_t* __restrict__ k,
@@ -286,9 +348,9 @@ __device__ __forceinline__ void stream_tiles_lds(const QueryRow<Op, MT>& qr,
     T::issue(wbuf + nxt * T::kBytes, k, k_scale, key0(i + (NB - 1) * step), b, lane);
     wait_vmcnt<(NB - 1) * T::kLoads>();
     typename Op::frag_t kb[Op::kSteps];
-    float ks = 1.0f;
+    typename Op::kscale_t ks = Op::kscale_one();
     T::read(wbuf + cur * T::kBytes, lane, kb, ks);
-    put(i, qr.score(kb), ks);
+    put(i, qr.score(kb, ks));
     cur = cur + 1 == NB ? 0 : cur + 1;
   }
   wait_vmcnt<0>();
@@ -389,8 +451,8 @@ __device__ __forceinline__ void load_kfrags(const uint8_t* buf, int kt, int lane
 template <class Op, int MT>
 struct PendingTile {
   f32x16_t acc[MT];
-  int s0 = 0;         // first key of the tile
-  float ksc = 1.0f;   // the lane's key scale (fp8)
+  int s0 = 0;                                        // first key of the tile
+  typename Op::kscale_t ksc = Op::kscale_one();      // the lane's key scale
   bool live = false;
 };
 
@@ -415,23 +477,24 @@ __device__ __forceinline__ void sched_mfma_valu() {
 // issued after it.
 template <class Op, int CK>
 __device__ __forceinline__ void chunk_key_scales(const float* __restrict__ k_scale, int key0,
-                                                 int hi, int lane, float (&ksc)[CK / kKeyTile]) {
-  constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
+                                                 int hi, int lane,
+                                                 typename Op::kscale_t (&ksc)[CK / kKeyTile]) {
 #pragma unroll
   for (int kt = 0; kt < CK / kKeyTile; ++kt) {
     const int s = key0 + kt * kKeyTile + (lane & 31);
-    ksc[kt] = (kScaled && k_scale != nullptr && s < hi) ? k_scale[s] : 1.0f;
+    ksc[kt] = (Op::kKeyScale && k_scale != nullptr && s < hi) ? Op::load_kscale(k_scale, s)
+                                                                : Op::kscale_one();
   }
 }
 
 // Scores of one wave's row over the chunk in `buf` (keys key0 .. key0+CK-1),
-// tile pairs skipped outside the window [a, b).  put(s0, score, scale) gets each
-// finished tile (lanes l and l^32 both hold key s0 + l%32); the chunk's last
-// tile is left pending in pd.
+// tile pairs skipped outside the window [a, b).  put(s0, score) gets each
+// finished tile, key scale applied (lanes l and l^32 both hold key s0 + l%32);
+// the chunk's last tile is left pending in pd.
 template <class Op, int MT, int CK, class Put>
 __device__ __forceinline__ void chunk_tile_pairs(const uint8_t* buf, int key0, int a, int b,
                                                  const QueryRow<Op, MT>& qr, int lane,
-                                                 const float (&ksc)[CK / kKeyTile],
+                                                 const typename Op::kscale_t (&ksc)[CK / kKeyTile],
                                                  PendingTile<Op, MT>& pd, Put put) {
   constexpr int kTiles = CK / kKeyTile;
   constexpr int kMf = Op::kSteps * MT;                     // MFMAs per tile
@@ -445,16 +508,16 @@ __device__ __forceinline__ void chunk_tile_pairs(const uint8_t* buf, int key0, i
     load_kfrags<Op>(buf, 2 * pr, lane, kA);
     load_kfrags<Op>(buf, 2 * pr + 1, lane, kB);
     f32x16_t acc1[MT];
-    qr.mma(kA, acc1);
+    qr.mma(kA, ksc[2 * pr], acc1);
     const float pP = qr.epilogue(pd.acc);
     __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // tile A's fragments
     __builtin_amdgcn_sched_group_barrier(0x002, 2 * kV, 0);
     sched_mfma_valu<kMf, kV, MT, kDs / Op::kSteps>();
-    if (pd.live) put(pd.s0, pP, pd.ksc);
-    qr.mma(kB, pd.acc);
+    if (pd.live) put(pd.s0, pP * Op::post(pd.ksc));
+    qr.mma(kB, ksc[2 * pr + 1], pd.acc);
     const float pA = qr.epilogue(acc1);
     sched_mfma_valu<kMf, kV, MT, 0>();
-    put(sA, pA, ksc[2 * pr]);
+    put(sA, pA * Op::post(ksc[2 * pr]));
     pd.s0 = sA + kKeyTile;
     pd.ksc = ksc[2 * pr + 1];
     pd.live = true;

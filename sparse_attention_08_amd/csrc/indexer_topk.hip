@@ -31,6 +31,7 @@ namespace {
 using namespace topksel;
 using ixcore::kKeyTile;
 using ixcore::OpBf16;
+using ixcore::OpFp4;
 using ixcore::OpFp8;
 using ixcore::QueryRow;
 
@@ -55,10 +56,9 @@ __device__ __forceinline__ uint32_t score_range(const QueryRow<Op, MT>& qr,
   const int nt = (m + kKeyTile - 1) / kKeyTile;
   const int hi = s_lo + m;
   uint32_t cnt = 0u;
-  auto put = [&](int i, float p, float ks) {
+  auto put = [&](int i, float p) {
     const int j = i * kKeyTile + (lane & 31);
     if (lane < 32 && j < m) {
-      if constexpr (kScaled) p *= ks;
       const uint32_t key = score_key(p);
       out[j] = key;
       if (key != 0u) {
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ row_ends, int H,
     int n_k, int32_t K, int32_t* __restrict__ out, uint32_t* __restrict__ cand_key,
     int32_t* __restrict__ cand_col, int32_t* __restrict__ cand_cnt) {
-  constexpr bool kScaled = Op::kRowBytes == 128;  // fp8 keys carry a scale
+  constexpr bool kScaled = Op::kKeyScale;  // fp8 / fp4 keys carry a scale
   __shared__ FusedShared sh;
   const int64_t t = blockIdx.x;
   const int c = blockIdx.y;
@@ -189,6 +189,11 @@ hipError_t launch_indexer_topk_fused(const void* q, const void* k, const float* 
                                          K, out, workspace, stream)
                : launch_fused<OpBf16, 2>(q, k, nullptr, w, row_starts, row_ends, n_q, n_k, n_heads,
                                          K, out, workspace, stream);
+  if (dtype == 3)
+    return one ? launch_fused<OpFp4, 1>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads,
+                                        K, out, workspace, stream)
+               : launch_fused<OpFp4, 2>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads,
+                                        K, out, workspace, stream);
   return one ? launch_fused<OpFp8, 1>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads, K,
                                       out, workspace, stream)
              : launch_fused<OpFp8, 2>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads, K,

@@ -37,6 +37,7 @@ namespace {
 
 using ixcore::kKeyTile;
 using ixcore::OpBf16;
+using ixcore::OpFp4;
 using ixcore::OpFp8;
 using ixcore::PendingTile;
 using ixcore::QueryRow;
@@ -49,7 +50,7 @@ constexpr int kFMaxK = 2048;
 
 template <class Op>
 constexpr int chunk_keys() {
-  return kFChunkBytes / Op::kRowBytes;  // 128 (bf16), 256 (fp8)
+  return kFChunkBytes / Op::kRowBytes < 256 ? kFChunkBytes / Op::kRowBytes : 256;  // 128 bf16, 256 fp8 / fp4
 }
 
 // One row's state in LDS: the radix histogram, the ring of scores (the chunk
@@ -193,13 +194,13 @@ __global__ __launch_bounds__(kFThreads) void indexer_topk_rows_kernel(
     for (int mt = 0; mt < MT; ++mt) pd.acc[mt] = f32x16_t{};
     // lanes l and l + 32 both hold key s0 + l % 32 and store the same value to
     // the same slot
-    auto put = [&](int s0, float p, float ks) {
-      hd.stage[(s0 - lo + (lane & 31)) & (kStage - 1)] = p * ks;
+    auto put = [&](int s0, float p) {
+      hd.stage[(s0 - lo + (lane & 31)) & (kStage - 1)] = p;
     };
     auto chunk = [&](int c, auto cur, auto nn) {
       constexpr int kCur = decltype(cur)::value, kNn = decltype(nn)::value;
       const int key0 = lo + c * CK;
-      float ksc[CK / kKeyTile];
+      typename Op::kscale_t ksc[CK / kKeyTile];
       ixcore::chunk_key_scales<Op, CK>(k_scale, key0, hi, lane, ksc);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA pieces of chunk c landed
       __syncthreads();                // ... everyone's; chunk c-1 and its ring slots are free
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kFThreads) void indexer_topk_rows_kernel(
       chunk(c + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
     }
     __syncthreads();  // the selecting wave has filtered everything before the pending tile
-    if (pd.live) put(pd.s0, qr.epilogue(pd.acc), pd.ksc);
+    if (pd.live) put(pd.s0, qr.epilogue(pd.acc) * Op::post(pd.ksc));
     wsel::wave_fence();
     if (lane == 0) scored[row] = b;
     __syncthreads();  // the row's last scores are in the ring
@@ -280,6 +281,11 @@ hipError_t launch_indexer_topk_rows(const void* q, const void* k, const float* k
                                         K, out, stream)
                : launch_rows<OpBf16, 2>(q, k, nullptr, w, row_starts, row_ends, n_q, n_k, n_heads,
                                         K, out, stream);
+  if (dtype == 3)
+    return one ? launch_rows<OpFp4, 1>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads,
+                                       K, out, stream)
+               : launch_rows<OpFp4, 2>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads,
+                                       K, out, stream);
   return one ? launch_rows<OpFp8, 1>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads, K,
                                      out, stream)
              : launch_rows<OpFp8, 2>(q, k, k_scale, w, row_starts, row_ends, n_q, n_k, n_heads, K,

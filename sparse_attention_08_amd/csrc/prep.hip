@@ -41,6 +41,24 @@ __device__ __forceinline__ uint8_t encode_e4m3(float x) {
   return uint8_t(sign | (uint32_t(e + 7) << 3) | (qv - 8u));
 }
 
+// OCP FP4 E2M1 code of x (round to nearest even on the grid 0, .5, 1, 1.5, 2,
+// 3, 4, 6; beyond 6 saturates): sign in bit 3.
+__device__ __forceinline__ uint32_t encode_e2m1(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  const float a = fabsf(x);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f  ? 4u : a < 3.5f  ? 5u : a <= 5.0f  ? 6u : 7u;
+  return sign | c;
+}
+
+// MXFP4 block scale exponent: floor(log2 amax) - 2 (0 for amax == 0), within
+// the E8M0 range.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int e = ilogbf(amax) - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // Smallest power of two s with amax <= 448 * s (1 for amax == 0).
 __device__ __forceinline__ float pow2_scale(float amax) {
   if (!(amax > 0.0f)) return 1.0f;
@@ -120,6 +138,36 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void prep_kernel(
   }
   if (!live) return;
 
+  if (dtype == 3) {
+    // MXFP4: element e = lane + 64 j sits in block e / 32, i.e. the lane half
+    // of slot j; the block max reduces over those 32 lanes
+    const int half = lane >> 5;
+    uint8_t* codes;
+    uint8_t* scales;
+    if (is_key) {
+      codes = static_cast<uint8_t*>(k_out) + r * (D / 2);
+      scales = reinterpret_cast<uint8_t*>(k_scale_out) + r * (D / 32);
+    } else {
+      const int64_t t = r / H, h = r % H;
+      uint8_t* tok = static_cast<uint8_t*>(q_out) + t * H * int64_t(D / 2 + D / 32);
+      codes = tok + h * (D / 2);
+      scales = tok + int64_t(H) * (D / 2) + h * (D / 32);
+      if (lane == 0) w_out[r] = w[r];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxD / kWave; ++j) {
+      if (kWave * j >= D) break;
+      float amax = fabsf(x[j]);
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const int ex = mx_exponent(amax);
+      const uint32_t c = encode_e2m1(ldexpf(x[j], -ex));
+      const uint32_t nb = uint32_t(__shfl_down(int(c), 1));  // the next element's code
+      if ((lane & 1) == 0) codes[(lane + kWave * j) / 2] = uint8_t(c | (nb << 4));
+      if ((lane & 31) == 0) scales[2 * j + half] = uint8_t(ex + 127);
+    }
+    return;
+  }
   if (dtype == 0) {
     float* dst = (is_key ? static_cast<float*>(k_out) : static_cast<float*>(q_out)) + r * D;
 #pragma unroll

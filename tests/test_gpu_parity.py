@@ -804,3 +804,112 @@ def test_decode_scores_from_fp8_key_cache(dsa):
         oi = o_topk.topk_row(full.astype(np.float32), a, b, 2048)
         ndiff += check_topk_e2e(idx[t], oi, full, tau, f"fp8 cache row {t}")
     say(f"  selection differs from the oracle's in {ndiff} columns (within tolerance)")
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 indexer (e2m1 values, E8M0 scale per 32 dims, scaled MFMA)
+# ---------------------------------------------------------------------------
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _e2m1_codes(v):
+    """e2m1 values -> 4-bit codes (sign in bit 3)."""
+    v = np.asarray(v, np.float64)
+    mag = np.searchsorted(_E2M1, np.abs(v))
+    assert np.all(_E2M1[mag] == np.abs(v)), "not an e2m1 value"
+    return (mag | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def _e2m1_values(c):
+    c = np.asarray(c, np.uint8)
+    return np.where(c & 8, -1.0, 1.0) * _E2M1[c & 7]
+
+
+def _pack_rows(codes):  # [..., D] e2m1 values -> [..., D/2] bytes, even element low
+    c = _e2m1_codes(codes)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _unpack_rows(b):
+    b = np.asarray(b, np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.float64)
+    out[..., 0::2] = _e2m1_values(b & 15)
+    out[..., 1::2] = _e2m1_values(b >> 4)
+    return out
+
+
+def mxfp4_device(p):
+    """The oracle's MXFP4 operands in the library's layout: q per token = its H
+    code rows then its H scale groups; k codes; k E8M0 bytes."""
+    n_q, H, D = p["q_codes"].shape
+    qb = _pack_rows(p["q_codes"]).reshape(n_q, H * D // 2)
+    qs = (p["q_exp"] + 127).astype(np.uint8).reshape(n_q, H * D // 32)
+    q = np.concatenate([qb, qs], axis=1)
+    k = _pack_rows(p["k_codes"])
+    ks = (p["k_exp"] + 127).astype(np.uint8)
+    u8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return u8(q), u8(k), dev(p["w"]), u8(ks)
+
+
+def test_indexer_prep_mxfp4(dsa):
+    lay = synth.layout_from_lengths([300, 1000])
+    w = synth.WORKLOADS["fp8_64k"]
+    q_raw = synth.index_q_raw(w, 0, lay.n_q)
+    k_raw = synth.index_k_raw(w, 0, lay.n_k)
+    wt = synth.index_weights(w, 0, lay.n_q)
+    say("prep mxfp4")
+    q, k, wo, ks = dsa.dsa_indexer_prep(dev(q_raw), dev(k_raw), dev(wt), out_dtype="mxfp4")
+    p = o_prep.prepare_indexer_inputs(q_raw, k_raw, wt, np.zeros(lay.n_q), np.zeros(lay.n_k),
+                                      "mxfp4")
+    H, D = w.n_heads, w.head_dim
+    gq = host(q).reshape(lay.n_q, -1)
+    np.testing.assert_array_equal(_unpack_rows(gq[:, :H * D // 2].reshape(lay.n_q, H, D // 2)),
+                                  p["q_codes"])                     # no norm: codes identical
+    np.testing.assert_array_equal(gq[:, H * D // 2:].reshape(lay.n_q, H, D // 32).astype(int) - 127,
+                                  p["q_exp"])
+    np.testing.assert_array_equal(host(wo), p["w"])
+    gk = _unpack_rows(host(k))
+    ge = host(ks).astype(int) - 127
+    same_e = ge == p["k_exp"]
+    assert np.mean(same_e) > 0.999                                   # fp32 vs fp64 norm
+    mism = gk != p["k_codes"]
+    assert np.mean(mism) < 0.01
+    rows_ok = same_e.all(axis=1)
+    # a differing code is the neighbour on the e2m1 grid
+    idx = lambda v: np.searchsorted(_E2M1, np.abs(v)) * np.sign(v + 0.0)
+    assert np.all(np.abs(idx(gk[rows_ok]) - idx(p["k_codes"][rows_ok]))[mism[rows_ok]] <= 1)
+
+
+@pytest.mark.parametrize("lens,decode", [([777], False), ([5000, 33, 12000, 20001], True)])
+def test_indexer_scores_mxfp4(dsa, lens, decode):
+    # the oracle's canonical MXFP4 operands on the GPU (row-block and row-split
+    # kernels) against the oracle's scores on the dequantised values
+    w = synth.WORKLOADS["fp8_64k"]
+    lay = synth.layout_from_lengths(lens, decode=decode)
+    p, rs, re = canonical_indexer(w, lay, "mxfp4", signed=True, rope=False)
+    q, k, wt, ks = mxfp4_device(p)
+    say(f"indexer mxfp4 lens={lens}: n_q={lay.n_q} n_k={lay.n_k}")
+    G = host(dsa.dsa_indexer_scores(q, k, wt, i32(rs), i32(re), k_scale=ks))
+    worst = 0.0
+    for t in range(0, lay.n_q, 1 if decode else 7):
+        a, b = rs[t], re[t]
+        o, c = o_idx.score_row(p["q"][t], p["k"][a:b], p["w"][t], with_cond=True)
+        worst = max(worst, check_scores(G[t, a:b], o, c, 2e-2, f"mxfp4 row {t}"))
+        assert np.isnan(G[t, :a]).all() and np.isnan(G[t, b:]).all()
+    say(f"  max rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("lens,decode", [([3000, 700], False), ([70000, 9000, 300], True)])
+def test_indexer_topk_mxfp4(dsa, lens, decode):
+    w = synth.WORKLOADS["fp8_64k"]
+    lay = synth.layout_from_lengths(lens, decode=decode)
+    p, rs, re = canonical_indexer(w, lay, "mxfp4", rope=False)
+    q, k, wt, ks = mxfp4_device(p)
+    for K in (2048, 100):
+        S = dsa.dsa_indexer_scores(q, k, wt, i32(rs), i32(re), k_scale=ks)
+        ref = host(dsa.dsa_topk(S, i32(rs), i32(re), K))
+        got = host(dsa.dsa_indexer_topk(q, k, wt, i32(rs), i32(re), K, k_scale=ks))
+        assert np.array_equal(got, ref), f"mxfp4 fused differs (K={K})"
+        Sh = host(S)
+        for t in list(range(0, lay.n_q, 251)) + [lay.n_q - 1]:
+            np.testing.assert_array_equal(ref[t], o_topk.topk_row(Sh[t], rs[t], re[t], K))

@@ -269,3 +269,64 @@ def test_k_insert_slots_and_quantisation():
     c3, s3 = np.zeros((1, D)), np.zeros(1)
     prep.k_norm_quant_insert(k[2:3], None, None, 0.0, [0], c3, s3)
     np.testing.assert_array_equal(c2 * s2[:, None], c3 * s3[:, None])
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (OCP microscaling: E2M1 elements, E8M0 scale per 32)
+# ---------------------------------------------------------------------------
+def test_round_e2m1_grid_and_ties():
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    np.testing.assert_array_equal(prep.round_e2m1(grid), grid)
+    np.testing.assert_array_equal(prep.round_e2m1(-grid), -grid)
+    # ties go to the even mantissa bit (0.5 = 0.1b: odd; 1, 2, 4: even)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    np.testing.assert_array_equal(prep.round_e2m1(ties), [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0])
+    np.testing.assert_array_equal(prep.round_e2m1([0.26, 0.74, 1.26, 2.6, 5.01, 6.5, 7.99, 1e9]),
+                                  [0.5, 0.5, 1.5, 3.0, 6.0, 6.0, 6.0, 6.0])   # saturates at 6
+    # every value rounds to a nearest grid point
+    g = np.random.default_rng(30)
+    x = g.uniform(-6, 6, 20000)
+    r = prep.round_e2m1(x)
+    full = np.concatenate([-grid[::-1], grid])
+    best = np.abs(x[:, None] - full[None, :]).min(axis=1)
+    np.testing.assert_allclose(np.abs(x - r), best, rtol=0, atol=1e-15)
+
+
+def test_mxfp4_block_scales():
+    g = np.random.default_rng(31)
+    x = g.standard_normal((20, 4, 128)) * 10.0 ** g.integers(-4, 4, (20, 4, 1))
+    x[0, 0, :32] = 0.0                          # an all-zero block: exponent 0
+    codes, e = prep.quant_mxfp4_blocks(x)
+    assert e.shape == (20, 4, 4) and e[0, 0, 0] == 0 and np.all(codes[0, 0, :32] == 0)
+    amax = np.abs(x.reshape(20, 4, 4, 32)).max(-1)
+    nz = amax > 0
+    # 2^e <= amax / 4 < 2^(e+1): the largest element lands in [4, 8) before saturation
+    assert np.all(np.exp2(e[nz] + 2.0) <= amax[nz]) and np.all(amax[nz] < np.exp2(e[nz] + 3.0))
+    np.testing.assert_array_equal(prep.round_e2m1(codes), codes)
+    deq = codes * np.repeat(np.exp2(e.astype(float)), 32, axis=-1)
+    # error: within half a grid step of the element's binade, or the saturation
+    # (at most 2 steps of 2^e below 8 2^e)
+    ok = np.abs(deq - x) <= np.maximum(0.25, 0.5 * np.exp2(np.floor(np.log2(np.maximum(
+        np.abs(x) / np.repeat(np.exp2(e.astype(float)), 32, -1), 1.0))) - 1)) \
+        * np.repeat(np.exp2(e.astype(float)), 32, -1) + 1e-300
+    sat = np.abs(x) >= 6 * np.repeat(np.exp2(e.astype(float)), 32, -1)
+    assert np.all(ok | sat)
+    assert np.all(np.abs(deq[sat]) == 6 * np.repeat(np.exp2(e.astype(float)), 32, -1)[sat])
+
+
+def test_mxfp4_prepared_operands_score_as_dequantised():
+    from oracle import indexer
+    g = np.random.default_rng(32)
+    q = g.standard_normal((3, 4, 128))
+    k = g.standard_normal((9, 128))
+    w = g.random((3, 4)).astype(np.float32).astype(np.float64)
+    p = prep.prepare_indexer_inputs(q, k, w, np.zeros(3), np.zeros(9), "mxfp4")
+    kn = prep.layer_norm(k)
+    k4, ek = prep.quant_mxfp4_blocks(kn)
+    np.testing.assert_array_equal(p["k_codes"], k4)
+    np.testing.assert_array_equal(p["k"], k4 * np.repeat(np.exp2(ek.astype(float)), 32, axis=-1))
+    # the score is the definition on the dequantised operands (no key scale)
+    ref = indexer.score_row(p["q"][1], p["k"], w[1])
+    manual = np.array([sum(w[1, h] * max(0.0, float(p["q"][1, h] @ p["k"][s])) for h in range(4))
+                       for s in range(9)])
+    np.testing.assert_allclose(ref, manual, rtol=1e-13)
