@@ -154,6 +154,19 @@ def stage_bench(args, dsa, synth, np, torch):
     mq = inp["mla_q"].to(torch.bfloat16)
     mkv = inp["mla_kv"].to(torch.bfloat16)
     del inp
+    mla_insert_ms, mcache = None, None
+    if fp8_cache:
+        # the latent cache in fp8 (656-byte rows), written from the bf16 rows (timed once)
+        slots = torch.arange(lay.n_k, dtype=torch.int64, device=dev)
+        mcache = torch.empty((lay.n_k, dsa.MLA_FP8_ROW_BYTES), dtype=torch.uint8, device=dev)
+        dsa.dsa_mla_kv_insert(mkv, slots, mcache)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dsa.dsa_mla_kv_insert(mkv, slots, mcache)
+        e1.record()
+        torch.cuda.synchronize()
+        mla_insert_ms = e0.elapsed_time(e1)
+        del slots
     K = w.index_topk
     scores = torch.full((lay.n_q, lay.n_k), float("-inf"), dtype=torch.float32, device=dev)
     idx = torch.empty((lay.n_q, K), dtype=torch.int32, device=dev)
@@ -171,9 +184,14 @@ def stage_bench(args, dsa, synth, np, torch):
     fns = {
         "indexer": lambda: dsa.dsa_indexer_scores(q, k, wt, rs, re, k_scale=ks, scores=scores),
         "topk": lambda: dsa.dsa_topk(scores, rs, re, K, out=idx),
-        "mla": lambda: dsa.dsa_sparse_mla_fwd(mq, mkv, idx, w.sm_scale, w.d_v, out=out, lse=lse,
-                                              workspace=ws),
+        "mla": lambda: dsa.dsa_sparse_mla_fwd(mq, mkv if mcache is None else mcache, idx,
+                                              w.sm_scale, w.d_v, out=out, lse=lse, workspace=ws),
     }
+    if mcache is not None:   # the same attention over the bf16 rows, for comparison
+        out_b = torch.empty_like(out)
+        fns["mla_bf16_kv"] = lambda: dsa.dsa_sparse_mla_fwd(mq, mkv, idx, w.sm_scale, w.d_v,
+                                                            out=out_b, lse=lse, workspace=ws)
+        hbm_bound["mla_bf16_kv"] = True
     fused = True                     # the fused indexer + top-k: decode and prefill kernels
     if fused:
         idx2 = torch.empty_like(idx)
@@ -209,7 +227,8 @@ def stage_bench(args, dsa, synth, np, torch):
     idx_bytes = int(lay.n_q * hd * elt) + key_bytes + lay.n_q * w.n_heads * 4 + pairs * 4
     topk_bytes = pairs * 4 + lay.n_q * K * 4
     mla_flop = sel * MLA_FLOP_PER_PAIR
-    gather = sel * w.d_qk * 2
+    row_bytes = dsa.MLA_FP8_ROW_BYTES if mcache is not None else w.d_qk * 2
+    gather = sel * row_bytes
     mla_compulsory = mq.numel() * 2 + out.numel() * 2 + lse.numel() * 4 + idx.numel() * 4
     mfma_peak = {"bf16": BF16_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS, "mxfp4": FP4_PEAK_TFLOPS}[w.dtype]
     t = {n: v * 1e-3 for n, v in ms.items()}
@@ -229,6 +248,16 @@ def stage_bench(args, dsa, synth, np, torch):
                 "gather_gbs": (gather + mla_compulsory) / t["mla"] / 1e9,
                 "frac_hbm": (gather + mla_compulsory) / t["mla"] / 1e9 / HBM_PEAK_GBS},
     }
+    if mcache is not None:
+        gb = sel * w.d_qk * 2
+        comp["mla"]["kv_row_bytes"] = row_bytes
+        comp["mla_bf16_kv"] = {"ms": ms["mla_bf16_kv"], "kv_row_bytes": w.d_qk * 2,
+                               "gather_gbs": (gb + mla_compulsory) / t["mla_bf16_kv"] / 1e9,
+                               "fp8_speedup": ms["mla_bf16_kv"] / ms["mla"]}
+        mb = lay.n_k * (w.d_qk * 2 + 8 + row_bytes)          # bf16 rows + slot in, fp8 rows out
+        comp["mla_kv_insert"] = {"ms": mla_insert_ms, "rows_per_s": lay.n_k / (mla_insert_ms * 1e-3),
+                                 "gbs": mb / (mla_insert_ms * 1e-3) / 1e9,
+                                 "frac_hbm": mb / (mla_insert_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if insert_ms is not None:
         ib = lay.n_k * (w.head_dim * 2 + 8 + w.head_dim + 4)  # bf16 keys + slot in, codes + scale out
         comp["k_insert"] = {"ms": insert_ms, "keys_per_s": lay.n_k / (insert_ms * 1e-3),
@@ -270,7 +299,8 @@ def stage_bench(args, dsa, synth, np, torch):
                 "traffic": None}
     elif dom == "mla":
         ach = comp["mla"]["gather_gbs"]
-        roof = {"kernel": "mla_bf16_kernel", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+        roof = {"kernel": "mla_bf16_kernel" if mcache is None else "mla_fp8kv_kernel",
+                "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
     else:
         ach = comp["topk"]["gbs"]
@@ -285,7 +315,9 @@ def stage_bench(args, dsa, synth, np, torch):
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{args.workload}: n_q={lay.n_q} n_k={lay.n_k} index {w.n_heads}x{w.head_dim} "
                                f"{w.dtype}, index_topk {K}, sparse MLA {w.mla_heads} heads "
-                               f"{w.d_qk}/{w.d_v} bf16", "valid_pairs": pairs, "selected_pairs": sel,
+                               f"{w.d_qk}/{w.d_v} bf16" +
+                               (" over the fp8 latent cache (656-B rows)" if mcache is not None else ""),
+                   "valid_pairs": pairs, "selected_pairs": sel,
                    "parallelism": "none (1 GPU)"},
         "components": comp, "roofline": roof,
     }

@@ -167,6 +167,31 @@ int dsa_indexer_k_insert(const void* k_raw, int32_t k_dtype, const float* norm_w
                          float* k_scale_cache, int64_t n_slots, void* stream);
 
 /*
+ * dsa_mla_kv_insert -- write new latent rows into the fp8 MLA cache.
+ *
+ * Passage: KimiK3DSAAttention.__init__ on the vLLM API page
+ * "vllm.models.kimi_k3.nvidia.dsa" (kv_cache_dtype "fp8_ds_mla": the latent
+ * cache holds fp8 latent values with per-tile scales and the rope part
+ * unquantised).
+ *
+ *   kv            [n_tokens, d_qk] of kv_dtype (F32 or BF16): the new rows, 512
+ *                 latent dims then 64 rope dims (16-byte aligned)
+ *   slot_mapping  int64 [n_tokens]: the cache row of each token; a negative slot
+ *                 or one >= n_slots writes nothing
+ *   kv_cache      uint8 [n_slots, 656] (16-byte aligned), the FP8_E4M3 kv
+ *                 operand of dsa_sparse_mla_fwd: row `slot` gets, per 128
+ *                 latent dims, the smallest power of two s with amax <= 448 s (1
+ *                 for an all-zero tile) at bytes 512 + 4 b (fp32) and the codes
+ *                 round-to-nearest-even(x / s) at bytes 128 b ..; then the rope
+ *                 dims rounded to bf16 at bytes 528 .. 655.
+ * Other slots are left untouched; two tokens must not share a slot.
+ * Supported: d_qk == 576.
+ */
+int dsa_mla_kv_insert(const void* kv, int32_t kv_dtype, const int64_t* slot_mapping,
+                      int64_t n_tokens, int32_t d_qk, uint8_t* kv_cache, int64_t n_slots,
+                      void* stream);
+
+/*
  * dsa_indexer_scores -- lightning-indexer scores over each row's window.
  *
  * Passage: the operands KimiK3DSAIndexer.forward and .score build on the vLLM API
@@ -296,18 +321,28 @@ int dsa_indexer_topk_noalloc(const void* q, const void* k, const float* k_scale,
  *   out[t, h, :] = sum_j softmax(l)_j * kv[J_j, :d_v],  lse[t, h] = logsumexp_j l_j
  * An all -1 row gives out = 0 and lse = -inf.  Duplicates count as listed.
  *
- *   q         [n_q, n_heads, d_qk] of dtype (F32 or BF16)
- *   kv        [n_kv, d_qk] of dtype; V = the first d_v columns of the same rows
+ *   q         [n_q, n_heads, d_qk] of dtype (F32 or BF16; BF16 for FP8_E4M3)
+ *   kv        [n_kv, d_qk] of dtype; V = the first d_v columns of the same rows.
+ *             FP8_E4M3 is the fp8 latent cache ("fp8_ds_mla", the kv_cache_dtype
+ *             of KimiK3DSAAttention on the same page), 656 bytes per row: 512 OCP
+ *             e4m3fn latent codes, 4 fp32 scales (latent dims 128 b .. 128 b + 127
+ *             are code * scale[b]), then the 64 rope dims in bf16 -- the rows
+ *             dsa_mla_kv_insert writes.  Its rows enter the kernel as those bf16
+ *             values (exact for the power-of-two scales the insert writes).
  *   topk_idx  int32 [n_q, index_topk]; entries in [0, n_kv) or -1 (an entry
  *             outside [0, n_kv) is skipped like -1)
- *   out       [n_q, n_heads, d_v] of dtype;  lse f32 [n_q, n_heads] or NULL
+ *   out       [n_q, n_heads, d_v] of dtype (BF16 for FP8_E4M3);  lse f32
+ *             [n_q, n_heads] or NULL
  *   workspace at least dsa_sparse_mla_workspace_size(...) bytes (may be 0).
- *   For few queries (BF16) each row's keys are split over several workgroups;
+ *   For few queries (BF16, FP8_E4M3) each row's keys are split over several
+ *   workgroups;
  *   the workspace then holds their normalised partial outputs in bf16 and
  *   their partial LSEs in fp32, merged by a second kernel.
  * Softmax statistics and accumulation are fp32; probabilities enter the
- * value product in the input type.  Supported: BF16 with d_qk == 576,
- * d_v == 512, n_heads a multiple of 32; F32 with d_qk <= 256, d_v <= d_qk.
+ * value product in the input type (bf16 for FP8_E4M3).  Supported: BF16 with
+ * d_qk == 576, d_v == 512, n_heads a multiple of 32; FP8_E4M3 with d_qk == 576,
+ * d_v == 512 (q and kv 16-byte aligned, out 8-byte aligned); F32 with
+ * d_qk <= 256, d_v <= d_qk.
  */
 size_t dsa_sparse_mla_workspace_size(int64_t n_q, int32_t n_heads, int32_t d_qk,
                                      int32_t d_v, int32_t index_topk,

@@ -240,3 +240,29 @@ def k_norm_quant_insert(k_raw, weight, bias, eps, slot_mapping, cache_codes, cac
     cache_codes[slots[ok]] = codes[ok]
     cache_scales[slots[ok]] = s[ok, 0]
     return cache_codes, cache_scales
+
+
+# ----------------------------------------------------------------------------
+# the fp8 latent KV cache of the sparse MLA ("fp8_ds_mla")
+# ----------------------------------------------------------------------------
+def mla_kv_quant(kv, d_latent: int = 512, block: int = 128):
+    """A latent row in the fp8 cache format that KimiK3DSAAttention selects with
+    kv_cache_dtype "fp8_ds_mla" (vLLM API page "vllm.models.kimi_k3.nvidia.dsa";
+    the page names the format, not its layout).
+
+    Readings: the d_latent latent dims (the value, and the first d_latent dims
+    of the key) are e4m3 codes with one fp32 scale per `block` dims, chosen by
+    the power-of-two rule of the index cache (the smallest power of two s with
+    amax <= 448 s); the rope dims after them stay bf16.  Returns (codes
+    [N, d_latent], scales [N, d_latent/block], rope [N, d_qk - d_latent]); the
+    row the attention reads is dequant_mla_kv(codes, scales, rope)."""
+    kv = np.asarray(kv, np.float64)
+    codes, s = quant_e4m3_blocks(kv[:, :d_latent], block)
+    return codes, s, round_bf16(kv[:, d_latent:])
+
+
+def dequant_mla_kv(codes, scales, rope, block: int = 128) -> np.ndarray:
+    """The latent row the attention reads: codes * scale of each block, then the
+    rope dims."""
+    lat = np.asarray(codes, np.float64) * np.repeat(np.asarray(scales, np.float64), block, axis=-1)
+    return np.concatenate([lat, np.asarray(rope, np.float64)], axis=-1)

@@ -6,8 +6,8 @@ current torch stream.  The entry points carry the names of the C ABI in
 ``include/dsa.h``:
 
     dsa_row_windows, dsa_indexer_prep, dsa_indexer_k_insert, dsa_indexer_scores,
-    dsa_topk, dsa_indexer_topk, dsa_indexer_topk_noalloc, dsa_sparse_mla_fwd
-    (+ workspace-size queries)
+    dsa_topk, dsa_indexer_topk, dsa_indexer_topk_noalloc, dsa_mla_kv_insert,
+    dsa_sparse_mla_fwd (+ workspace-size queries)
 
 A nonzero status raises ``DSAError``.  Importing this package does not load
 the library; ``load()`` does, and fails loudly when it is missing.
@@ -63,6 +63,7 @@ def _declare(lib):
         "dsa_indexer_prep": (ctypes.c_int, [P, P, P, P, P, I64, I64, I32, I32, I32, I32, F32, F32,
                                             I32, P, P, P, P, P]),
         "dsa_indexer_k_insert": (ctypes.c_int, [P, I32, P, P, F32, P, I64, I32, P, P, I64, P]),
+        "dsa_mla_kv_insert": (ctypes.c_int, [P, I32, P, I64, I32, P, I64, P]),
         "dsa_indexer_scores": (ctypes.c_int, [P, P, P, P, P, P, I64, I64, I32, I32, I32, P, I64, P]),
         "dsa_topk_workspace_size": (SZ, [I64, I64, I32]),
         "dsa_topk": (ctypes.c_int, [P, I64, P, P, I64, I64, I32, P, P, SZ, P]),
@@ -84,7 +85,7 @@ def _declare(lib):
 EXPORTS = ("dsa_status_string", "dsa_version", "dsa_row_windows", "dsa_indexer_prep",
            "dsa_indexer_k_insert", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
            "dsa_indexer_topk_workspace_size", "dsa_indexer_topk", "dsa_indexer_topk_noalloc",
-           "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd")
+           "dsa_mla_kv_insert", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd")
 
 
 # ---------------------------------------------------------------------------
@@ -205,6 +206,22 @@ def dsa_indexer_k_insert(k_raw, slot_mapping, k_cache, k_scale_cache, norm_weigh
     return k_cache, k_scale_cache
 
 
+MLA_FP8_ROW_BYTES = 656  # 512 e4m3 latent codes, 4 fp32 scales, 64 bf16 rope values
+
+
+def dsa_mla_kv_insert(kv, slot_mapping, kv_cache, stream=None):
+    """Latent rows kv [n, 576] (f32 / bf16) -> fp8 cache rows slot_mapping[i] of
+    kv_cache uint8 [n_slots, 656], updated in place; negative slots are skipped."""
+    lib = _lib_or_load()
+    n_tok, d_qk = kv.shape
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != MLA_FP8_ROW_BYTES:
+        raise DSAError("kv_cache must be uint8 [n_slots, 656]")
+    _check(lib.dsa_mla_kv_insert(_ptr(kv), _dtype_code(kv), _ptr(slot_mapping), n_tok, d_qk,
+                                 _ptr(kv_cache), kv_cache.shape[0], _stream(stream)),
+           "dsa_mla_kv_insert")
+    return kv_cache
+
+
 def dsa_indexer_scores(q, k, w, row_starts, row_ends, k_scale=None, scores=None, ld=None,
                        stream=None):
     """scores [n_q, ld] fp32; only in-window entries are written."""
@@ -293,7 +310,12 @@ def dsa_sparse_mla_fwd(q, kv, topk_idx, sm_scale: float, d_v: int, out=None, lse
     n_q, H, d_qk = q.shape
     n_kv = kv.shape[0]
     K = topk_idx.shape[1]
-    need = lib.dsa_sparse_mla_workspace_size(n_q, H, d_qk, d_v, K, _dtype_code(q))
+    # a uint8 kv [n_kv, 656] is the fp8 latent cache (bf16 q and out)
+    fp8_kv = kv.dtype == torch.uint8
+    if fp8_kv and (kv.dim() != 2 or kv.shape[1] != MLA_FP8_ROW_BYTES):
+        raise DSAError("an fp8 latent cache must be uint8 [n_kv, 656]")
+    code = DTYPE_FP8_E4M3 if fp8_kv else _dtype_code(q)
+    need = lib.dsa_sparse_mla_workspace_size(n_q, H, d_qk, d_v, K, code)
     with _on(stream):
         if out is None:
             out = torch.empty((n_q, H, d_v), dtype=q.dtype, device=q.device)
@@ -303,6 +325,6 @@ def dsa_sparse_mla_fwd(q, kv, topk_idx, sm_scale: float, d_v: int, out=None, lse
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(topk_idx), n_q, n_kv, H, d_qk, d_v, K,
-                                  sm_scale, _dtype_code(q), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  sm_scale, code, _ptr(out), _ptr(lse), _ptr(workspace),
                                   nbytes, _stream(stream)), "dsa_sparse_mla_fwd")
     return out, lse

@@ -135,6 +135,22 @@ int dsa_indexer_k_insert(const void* k_raw, int32_t k_dtype, const float* norm_w
                                                     k_scale_cache, n_slots, as_stream(stream)));
 }
 
+int dsa_mla_kv_insert(const void* kv, int32_t kv_dtype, const int64_t* slot_mapping,
+                      int64_t n_tokens, int32_t d_qk, uint8_t* kv_cache, int64_t n_slots,
+                      void* stream) {
+  if (n_tokens < 0 || n_slots < 0 || d_qk < 1) return DSA_ERR_INVALID_ARG;
+  if (kv_dtype != DSA_DTYPE_F32 && kv_dtype != DSA_DTYPE_BF16) {
+    if (kv_dtype == DSA_DTYPE_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+    return DSA_ERR_INVALID_ARG;
+  }
+  if (n_tokens > 0 && (!kv || !slot_mapping)) return DSA_ERR_INVALID_ARG;
+  if (n_slots > 0 && !kv_cache) return DSA_ERR_INVALID_ARG;
+  if (d_qk != 576) return DSA_ERR_UNSUPPORTED;
+  if (!aligned(kv, 16) || !aligned(kv_cache, 16)) return DSA_ERR_UNSUPPORTED;
+  return launch_status(dsa::launch_mla_kv_insert(kv, kv_dtype, slot_mapping, n_tokens, kv_cache,
+                                                 n_slots, as_stream(stream)));
+}
+
 int dsa_indexer_scores(const void* q, const void* k, const float* k_scale, const float* w,
                        const int32_t* row_starts, const int32_t* row_ends, int64_t n_q,
                        int64_t n_k, int32_t n_heads, int32_t head_dim, int32_t dtype,
@@ -225,15 +241,16 @@ int dsa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* topk_idx, i
   if (n_q < 0 || n_kv < 0 || n_q > INT32_MAX || n_kv > INT32_MAX) return DSA_ERR_INVALID_ARG;
   if (n_heads < 1 || d_qk < 1 || d_v < 1 || d_v > d_qk || index_topk < 1)
     return DSA_ERR_INVALID_ARG;
-  if (dtype != DSA_DTYPE_F32 && dtype != DSA_DTYPE_BF16) {
-    if (dtype == DSA_DTYPE_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  if (dtype != DSA_DTYPE_F32 && dtype != DSA_DTYPE_BF16 && dtype != DSA_DTYPE_FP8_E4M3)
     return DSA_ERR_INVALID_ARG;
-  }
   if (n_q > 0 && (!q || !topk_idx || !out)) return DSA_ERR_INVALID_ARG;
   if (n_q > 0 && n_kv > 0 && !kv) return DSA_ERR_INVALID_ARG;
   if (dtype == DSA_DTYPE_BF16) {
     if (d_qk != 576 || d_v != 512 || (n_heads % 32) != 0) return DSA_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 4)) return DSA_ERR_UNSUPPORTED;
+  } else if (dtype == DSA_DTYPE_FP8_E4M3) {
+    if (d_qk != 576 || d_v != 512) return DSA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 8)) return DSA_ERR_UNSUPPORTED;
   } else {
     if (d_qk > 256 || int64_t(index_topk) > 8192) return DSA_ERR_UNSUPPORTED;
   }

@@ -19,6 +19,9 @@ hipError_t launch_indexer_prep(const float* q_raw, const float* k_raw, const flo
                                float eps, int32_t dtype, void* q_out, void* k_out,
                                float* w_out, float* k_scale_out, hipStream_t stream);
 
+hipError_t launch_mla_kv_insert(const void* kv, int32_t kv_dtype, const int64_t* slot_mapping,
+                                int64_t n_tokens, uint8_t* kv_cache, int64_t n_slots,
+                                hipStream_t stream);
 hipError_t launch_indexer_k_insert(const void* k_raw, int32_t k_dtype, const float* weight,
                                    const float* bias, float eps, const int64_t* slot_mapping,
                                    int64_t n_tokens, int32_t head_dim, uint8_t* k_cache,

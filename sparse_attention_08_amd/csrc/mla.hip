@@ -802,6 +802,381 @@ __global__ __launch_bounds__(128) void mla_f32_kernel(const float* __restrict__ 
   if (lse && tid == 0) lse[t * H + h] = den > 0.0f ? mx + __logf(den) : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Sparse MLA over the fp8 latent cache ("fp8_ds_mla", the kv_cache_dtype of
+// KimiK3DSAAttention): a row is 656 bytes -- 512 e4m3 latent codes, 4 fp32
+// scales (one per 128 latent dims), 64 bf16 rope dims.  Queries and outputs
+// are bf16.
+//
+// One workgroup = one query x 128 heads (or one key slice of it), 8 waves of
+// 16 heads, on v_mfma_f32_16x16x32_bf16.  Per tile of 32 selected keys:
+//   gather   LDS-DMA of the 32 rows (41 16-byte pieces each) into one of three
+//            staging buffers, issued two tiles ahead;
+//   dequant  all 512 threads convert the staged tile once into a bf16 tile
+//            (v_cvt_scalef32_pk_bf16_fp8: code * scale; exact for the
+//            power-of-two scales the insert writes), in the slot layout of the
+//            bf16 kernel (conflict-free K-fragment and transposed V reads);
+//   S^T=K.Q^T keys on M (two 16-key tiles), the wave's 16 heads on N, 18 steps
+//            of 32 dims; lane l then holds keys 4g..4g+3 and 16+4g..16+4g+3
+//            (g = l / 16) of head l % 16;
+//   softmax  fp32, base 2, against the head's first finite tile max; a later
+//            tile above it by more than 2^32 makes the workgroup run the query
+//            again against the true max (as the bf16 kernel);
+//   O^T+=V^T.P^T  the eight probabilities of the lane, rounded to bf16, are
+//            its B fragment as they lie (K order: keys 4g..4g+3, 16+4g..+3),
+//            and the V fragment takes the same keys in two transposing reads;
+//            32 tiles of 16 value columns, O^T in 128 registers per lane.
+// ---------------------------------------------------------------------------
+constexpr int kRow8 = 656;
+constexpr int kLatentCodes = 512;
+constexpr int kScaleOff = 512;
+constexpr int kRopeOff = 528;
+constexpr int kPieces8 = kRow8 / 16;  // 41
+static_assert(kPieces8 * 16 == kRow8, "rows are whole 16-byte pieces");
+constexpr int kStage8 = kKT * kRow8;                         // 20992
+constexpr int kThreads8 = 512;
+constexpr int kWaves8 = kThreads8 / kWave;                   // 8
+constexpr int kHeads8 = 16;                                  // per wave
+constexpr int kHeadsPerBlock8 = kWaves8 * kHeads8;           // 128
+constexpr int kLoads8 = (kKT * kPieces8 + kWave - 1) / kWave;  // 21 wave loads per tile
+constexpr int kSteps8 = kDqk / 32;                           // 18 K-steps of 32 dims
+constexpr int kVTiles8 = kDv / 16;                           // 32 value tiles of 16 columns
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+struct Mla8Shared {
+  int idx[kMaxIdx + kKT];         // the slice's rows (-1 and out of range -> row 0)
+  uint32_t vmask[kMaxTiles + 1];  // per tile: bit j = key j valid
+  int wlast[kWaves8];
+  int redo[2];
+};
+
+__shared__ __attribute__((aligned(16))) uint8_t g_st0[kStage8];
+__shared__ __attribute__((aligned(16))) uint8_t g_st1[kStage8];
+__shared__ __attribute__((aligned(16))) uint8_t g_st2[kStage8];
+__shared__ __attribute__((aligned(16))) uint8_t g_t8[kTileBytes];
+// Q^T steps kQReg8 .. 17 (dims 32 kQReg8 .. 575) for the block's 128 heads, the
+// rest stays in registers: 16 bytes per (step j = st - kQReg8, lane group g,
+// head), at ((j * 4 + g) * 128 + head) * 16
+constexpr int kQReg8 = 12;
+constexpr int kQLds8 = kSteps8 - kQReg8;  // 6
+__shared__ __attribute__((aligned(16))) uint8_t g_q8[kQLds8 * 4 * kHeadsPerBlock8 * 16];
+
+__device__ __forceinline__ uint8_t* stage8(int i) {
+  const int b = i % 3;
+  return b == 0 ? g_st0 : b == 1 ? g_st1 : g_st2;
+}
+
+// Wave loads of tile lt into stage buffer sb: load v of wave w moves pieces
+// (w + 8 v) * 64 + lane of the tile's 32 * 41 (key-major, each key's row
+// contiguous as in memory).  Returns nothing; every wave issues kLoads8 / 8
+// rounded by its index (3 for waves 0..4, 2 for 5..7).
+__device__ __forceinline__ void dma_tile8(uint8_t* sb, const int* sidx, int lt,
+                                          const uint8_t* __restrict__ kv, int wave, int lane) {
+#pragma unroll
+  for (int v = 0; v < (kLoads8 + kWaves8 - 1) / kWaves8; ++v) {
+    const int ld = wave + kWaves8 * v;
+    if (ld < kLoads8) {
+      const int p = ld * kWave + lane;
+      if (p < kKT * kPieces8) {
+        const int key = p / kPieces8;
+        const int part = p - key * kPieces8;
+        const uint8_t* src = kv + int64_t(sidx[lt * kKT + key]) * kRow8 + part * 16;
+        asm volatile("global_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(src), "{m0}"(lds_addr(sb + ld * 1024))
+                     : "memory");
+      }
+    }
+  }
+}
+
+// Wait until this wave's loads of the current tile landed (the next tile's may
+// stay in flight).
+__device__ __forceinline__ void wait_tile8(bool next_in_flight, int wave) {
+  if (!next_in_flight) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  } else if (wave < kLoads8 - 2 * kWaves8) {
+    __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+  }
+  static_assert(kLoads8 - 2 * kWaves8 == 5, "waves 0..4 issue 3 loads per tile, 5..7 issue 2");
+}
+
+// The staged tile in sb into the bf16 tile (all 512 threads): thread -> key
+// tid / 16, latent dims 32 * (tid % 16) .. +32 (one scale) and rope dims
+// 4 * (tid % 16) .. +4.
+__device__ __forceinline__ void dequant_tile8(const uint8_t* sb, int tid) {
+  const int j = tid >> 4, part = tid & 15;
+  const uint8_t* row = sb + j * kRow8;
+  const uint4 c0 = *reinterpret_cast<const uint4*>(row + 32 * part);
+  const uint4 c1 = *reinterpret_cast<const uint4*>(row + 32 * part + 16);
+  const float sc = *reinterpret_cast<const float*>(row + kScaleOff + 4 * (part >> 2));
+  const uint2 rp = *reinterpret_cast<const uint2*>(row + kRopeOff + 8 * part);
+  const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  uint32_t o[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true);
+    o[2 * i] = __builtin_bit_cast(uint32_t, lo);
+    o[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
+  }
+  uint8_t* dst = g_t8 + kslot(j) * kRowA + 64 * part;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  *reinterpret_cast<uint2*>(g_t8 + kRegionA + (part >> 1) * 512 + j * 16 + (part & 1) * 8) = rp;
+}
+
+// A fragment of S^T = K . Q^T: key 16 mt + l % 16, dims 32 st + 8 (l / 16) .. +8.
+__device__ __forceinline__ bf16x8_t kfrag8(int mt, int st, int lane) {
+  const int key = 16 * mt + (lane & 15), g = lane >> 4;
+  const uint8_t* p = st < 16 ? g_t8 + kslot(key) * kRowA + (32 * st + 8 * g) * 2
+                             : g_t8 + kRegionA + (4 * (st - 16) + g) * 512 + key * 16;
+  return *reinterpret_cast<const bf16x8_t*>(p);
+}
+
+// A fragment of O^T += V^T . P^T: value column 16 n + l % 16, keys 4g..4g+3 and
+// 16+4g..16+4g+3 (g = l / 16), by two transposing reads: in each group of 16
+// lanes, lane 4m + q names key row k0 + m, columns 16 n + 4q .. +4.
+__device__ __forceinline__ bf16x8_t vfrag8(int n, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const int m = i >> 2, q = i & 3;
+  const uint8_t* r0 = g_t8 + kslot(4 * g + m) * kRowA + (16 * n + 4 * q) * 2;
+  const uint8_t* r1 = g_t8 + kslot(16 + 4 * g + m) * kRowA + (16 * n + 4 * q) * 2;
+  const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(r0));
+  const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(r1));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Step n of the S^T product: key tile n & 1, dims 32 st .. with st = kQReg8 ..
+// 17 (Q^T from LDS) for the first 2 kQLds8 steps, then 0 .. kQReg8 - 1.
+constexpr int kSN = 2 * kSteps8;  // 36
+constexpr int kSRing = 4;         // A fragments in flight
+constexpr int kQRing = 3;         // Q^T fragments from LDS in flight (one per step pair)
+constexpr int kVRing = 3;         // V fragments in flight (two reads each)
+__host__ __device__ constexpr int s_step8(int n) {
+  return (n >> 1) < kQLds8 ? kQReg8 + (n >> 1) : (n >> 1) - kQLds8;
+}
+// step n reads its Q^T fragment from LDS (at the first step of its pair)
+__host__ __device__ constexpr bool s_qread8(int n) { return (n & 1) == 0 && (n >> 1) < kQLds8; }
+
+// Issue order of the S^T phase: the rope Q^T reads and the first kSRing A
+// fragments, then each MFMA followed by the read kSRing steps ahead, the last
+// MFMAs each followed by the two reads of one of the first V fragments.
+template <int I>
+__device__ __forceinline__ void sched_s8() {
+  if constexpr (I == 0) {
+    constexpr int q0 = (kSRing + 1) / 2 < kQLds8 ? (kSRing + 1) / 2 : kQLds8;
+    __builtin_amdgcn_sched_group_barrier(0x100, kSRing + q0, 0);
+  }
+  if constexpr (I < kSN) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + kSRing < kSN)
+      __builtin_amdgcn_sched_group_barrier(0x100, s_qread8(I + kSRing) ? 2 : 1, 0);
+    else if constexpr (I + kSRing - kSN < kVRing)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    sched_s8<I + 1>();
+  }
+}
+
+// Issue order of the P.V phase: each MFMA followed by the two reads of the V
+// fragment kVRing tiles ahead.
+template <int I>
+__device__ __forceinline__ void sched_v8() {
+  if constexpr (I < kVTiles8) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + kVRing < kVTiles8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    sched_v8<I + 1>();
+  }
+}
+
+__global__ __launch_bounds__(kThreads8) void mla_fp8kv_kernel(
+    const __bf16* __restrict__ q, const uint8_t* __restrict__ kv,
+    const int32_t* __restrict__ idx, int n_kv, int H, int K, float sm_scale,
+    __bf16* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
+    float* __restrict__ part_lse, int nsplit) {
+  __shared__ __attribute__((aligned(16))) Mla8Shared sh;
+  const int64_t t = int64_t(gridDim.x) - 1 - blockIdx.x;  // longest rows first
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane >> 4;
+  const int h0 = int(blockIdx.y) * kHeadsPerBlock8 + wave * kHeads8;
+  const int head = h0 + (lane & 15);
+  const bool hvalid = head < H;
+  const float scale2 = sm_scale * kLog2e;
+
+  const int ntiles = (K + kKT - 1) / kKT;
+  const int i0 = int(int64_t(ntiles) * blockIdx.z / nsplit);
+  int i1 = int(int64_t(ntiles) * (blockIdx.z + 1) / nsplit);
+  const int32_t* irow = idx + t * K;
+  const int jbase = i0 * kKT;
+  const int nx = (i1 - i0) * kKT;
+  constexpr int kPer = kMaxIdx / kThreads8;
+  int rv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int x = tid + u * kThreads8;
+    const int j = jbase + x;
+    rv[u] = (x < nx && j < K) ? irow[j] : -1;
+  }
+  {
+    int wl = -1;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int x = tid + u * kThreads8;
+      const bool ok = unsigned(rv[u]) < unsigned(n_kv);  // -1 and out of range: masked
+      if (x < nx) sh.idx[x] = ok ? rv[u] : 0;
+      const uint64_t b = __ballot(x < nx && ok);
+      if (x < nx && lane == 0) sh.vmask[x / kKT] = uint32_t(b);
+      if (x < nx && lane == 32) sh.vmask[x / kKT] = uint32_t(b >> 32);
+      if (b != 0ull) wl = u * kThreads8 + wave * kWave + 63 - __builtin_clzll(b);
+    }
+    if (lane == 0) sh.wlast[wave] = wl;
+    __syncthreads();
+    int last = sh.wlast[0];
+#pragma unroll
+    for (int w = 1; w < kWaves8; ++w) last = max(last, sh.wlast[w]);
+    i1 = last < 0 ? i0 : i0 + last / kKT + 1;
+  }
+  // Q^T fragments: head h0 + l % 16 (a head past H reads head H-1: finite values
+  // whose results are never written), dims 32 st + 8 g .. +8; steps below
+  // kQReg8 in registers, the others in LDS
+  bf16x8_t qf[kQReg8];
+  {
+    const __bf16* qr = q + (t * H + (hvalid ? head : H - 1)) * int64_t(kDqk) + 8 * g;
+#pragma unroll
+    for (int st = 0; st < kQReg8; ++st) qf[st] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * st);
+#pragma unroll
+    for (int j = 0; j < kQLds8; ++j)
+      *reinterpret_cast<bf16x8_t*>(g_q8 + ((j * 4 + g) * kHeadsPerBlock8 + wave * kHeads8 +
+                                           (lane & 15)) * 16) =
+          *reinterpret_cast<const bf16x8_t*>(qr + 32 * (kQReg8 + j));
+  }
+  const int nt = i1 - i0;
+  if (tid < 2) sh.redo[tid] = 0;
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // Q^T landed before the first gather
+
+  f32x4v_t o[kVTiles8];
+  float m_ref = -FLT_MAX, m_max = -FLT_MAX, l_run = 0.0f;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int n = 0; n < kVTiles8; ++n) o[n] = f32x4v_t{};
+    l_run = 0.0f;
+    bool over = false;
+    if (nt > 0) dma_tile8(stage8(0), sh.idx, 0, kv, wave, lane);
+    if (nt > 1) dma_tile8(stage8(1), sh.idx, 1, kv, wave, lane);
+    for (int i = 0; i < nt; ++i) {
+      wait_tile8(i + 1 < nt, wave);
+      __syncthreads();  // tile i staged by every wave; the bf16 tile is free
+      dequant_tile8(stage8(i), tid);
+      __syncthreads();  // the bf16 tile is complete; stage buffer i % 3 is free
+      if (i + 2 < nt) dma_tile8(stage8(i + 2), sh.idx, i + 2, kv, wave, lane);
+      // S^T for the 32 keys x the wave's 16 heads: 36 MFMA steps, the steps with
+      // Q^T in LDS first, the two key tiles alternating; A fragments are read
+      // kSRing steps ahead, LDS Q^T fragments with the A fragment of their pair
+      const uint8_t* qlds = g_q8 + (g * kHeadsPerBlock8 + wave * kHeads8 + (lane & 15)) * 16;
+      bf16x8_t kb[kSRing], qb[kQRing];
+#pragma unroll
+      for (int n = 0; n < kSRing; ++n) {
+        kb[n] = kfrag8(n & 1, s_step8(n), lane);
+        if (s_qread8(n))
+          qb[(n >> 1) % kQRing] = *reinterpret_cast<const bf16x8_t*>(
+              qlds + (s_step8(n) - kQReg8) * 4 * kHeadsPerBlock8 * 16);
+      }
+      f32x4v_t s[2] = {f32x4v_t{}, f32x4v_t{}};
+#pragma unroll
+      for (int n = 0; n < kSN; ++n) {
+        const int st = s_step8(n);
+        const bf16x8_t b = st >= kQReg8 ? qb[(n >> 1) % kQRing] : qf[st < kQReg8 ? st : 0];
+        s[n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[n % kSRing], b, s[n & 1], 0, 0, 0);
+        if (n + kSRing < kSN) {
+          const int m = n + kSRing;
+          kb[n % kSRing] = kfrag8(m & 1, s_step8(m), lane);
+          if (s_qread8(m))
+            qb[(m >> 1) % kQRing] = *reinterpret_cast<const bf16x8_t*>(
+                qlds + (s_step8(m) - kQReg8) * 4 * kHeadsPerBlock8 * 16);
+        }
+      }
+      // the first V fragments, read while the softmax runs
+      bf16x8_t vb[kVRing];
+#pragma unroll
+      for (int n = 0; n < kVRing; ++n) vb[n] = vfrag8(n, lane);
+      sched_s8<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      // mask, tile max over the head's 32 keys (4 lanes), reference, P
+      const uint32_t vm = sh.vmask[i];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * mt + 4 * g + r;
+          s[mt][r] = ((vm >> key) & 1u) ? s[mt][r] : -INFINITY;
+          tm = fmaxf(tm, s[mt][r]);
+        }
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      tm *= scale2;
+      m_ref = m_ref == -FLT_MAX ? fmaxf(tm, -FLT_MAX) : m_ref;
+      m_max = fmaxf(m_max, tm);
+      over = over || tm > m_ref + kSpan;
+      bf16x8_t pb;
+      float ps = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const __bf16 p = __bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], scale2, -m_ref)));
+          pb[4 * mt + r] = p;
+          ps += float(p);
+        }
+      l_run += ps;
+      __builtin_amdgcn_sched_barrier(0);
+      // O^T += V^T . P^T over the 32 value tiles, V fragments kVRing tiles ahead
+#pragma unroll
+      for (int n = 0; n < kVTiles8; ++n) {
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[n % kVRing], pb, o[n], 0, 0, 0);
+        if (n + kVRing < kVTiles8) vb[n % kVRing] = vfrag8(n + kVRing, lane);
+      }
+      sched_v8<0>();
+    }
+    if (__ballot(over) != 0ull && lane == 0) sh.redo[pass] = 1;
+    __syncthreads();
+    if (sh.redo[pass] == 0) break;
+    m_ref = fmaxf(m_max, -FLT_MAX);
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_h = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (!hvalid) return;
+  // lane (head l % 16) holds value columns 16 n + 4 g .. +4 of its head
+  uint16_t* orow = nsplit == 1
+                       ? reinterpret_cast<uint16_t*>(out) + (t * H + head) * int64_t(kDv)
+                       : part_o + ((t * nsplit + blockIdx.z) * H + head) * int64_t(kDv);
+#pragma unroll
+  for (int n = 0; n < kVTiles8; ++n) {
+    const bf16x2_t a = {__bf16(o[n][0] * inv), __bf16(o[n][1] * inv)};
+    const bf16x2_t b = {__bf16(o[n][2] * inv), __bf16(o[n][3] * inv)};
+    *reinterpret_cast<uint2*>(orow + 16 * n + 4 * g) =
+        make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+  }
+  if (g == 0) {
+    if (nsplit == 1) {
+      if (lse) lse[t * H + head] = lse_h;
+    } else {
+      part_lse[(t * nsplit + blockIdx.z) * H + head] = lse_h;
+    }
+  }
+}
+
 // Number of key splits per query for the bf16 kernel (shared by the launcher
 // and the workspace query).
 int mla_splits(int64_t n_q, int32_t n_heads, int32_t K) {
@@ -822,7 +1197,7 @@ int mla_splits(int64_t n_q, int32_t n_heads, int32_t K) {
 size_t mla_workspace_bytes(int64_t n_q, int32_t n_heads, int32_t d_qk, int32_t d_v,
                            int32_t K, int32_t dtype) {
   (void)d_qk;
-  if (dtype != 1) return 0;
+  if (dtype != 1 && dtype != 2) return 0;
   const int s = mla_splits(n_q, n_heads, K);
   if (s == 1) return 0;
   // bf16 partial outputs, then fp32 partial LSEs
@@ -846,9 +1221,17 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
   uint16_t* part_o = static_cast<uint16_t*>(workspace);
   float* part_lse =
       s > 1 ? reinterpret_cast<float*>(part_o + size_t(n_q) * s * n_heads * d_v) : nullptr;
-  hipLaunchKernelGGL(mla_bf16_kernel, dim3(unsigned(n_q), hb, s), dim3(kThreads), 0, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(kv), idx, int(n_kv),
-                     n_heads, K, sm_scale, static_cast<__bf16*>(out), lse, part_o, part_lse, s);
+  static_assert(kHeadsPerBlock8 == kHeadsPerBlock, "one head-block count for both kernels");
+  if (dtype == 2)
+    hipLaunchKernelGGL(mla_fp8kv_kernel, dim3(unsigned(n_q), hb, s), dim3(kThreads8), 0, stream,
+                       static_cast<const __bf16*>(q), static_cast<const uint8_t*>(kv), idx,
+                       int(n_kv), n_heads, K, sm_scale, static_cast<__bf16*>(out), lse, part_o,
+                       part_lse, s);
+  else
+    hipLaunchKernelGGL(mla_bf16_kernel, dim3(unsigned(n_q), hb, s), dim3(kThreads), 0, stream,
+                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(kv), idx,
+                       int(n_kv), n_heads, K, sm_scale, static_cast<__bf16*>(out), lse, part_o,
+                       part_lse, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s == 1) return e;
   static_assert(kDv == 8 * kWave, "one wave per head row in the combine");

@@ -357,6 +357,67 @@ __global__ __launch_bounds__(256) void k_insert128_kernel(
   if (sub == 0) cache_scale[slot] = s;
 }
 
+// One latent row into the fp8 MLA cache: a wave per token, lane l holding
+// latent dims 8l .. 8l+7 (the 128-dim scale block of 16 lanes reduces its amax
+// with xor 1, 2, 4, 8), lanes 0..15 also four rope dims each.  Output row of
+// 656 bytes: 512 e4m3 codes, 4 fp32 power-of-two scales, 64 bf16 rope values.
+constexpr int kMlaLatent = 512, kMlaRope = 64, kMlaRow8 = 656;
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void mla_kv_insert_kernel(const void* __restrict__ kv,
+                                                           const int64_t* __restrict__ slots,
+                                                           int64_t n_tok, int64_t n_slots,
+                                                           uint8_t* __restrict__ cache) {
+  constexpr int D = kMlaLatent + kMlaRope;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = int64_t(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
+  if (row >= n_tok) return;  // whole waves: the xor reductions stay inside one row
+  const int64_t slot = slots[row];
+  if (slot < 0 || slot >= n_slots) return;
+  float x[8], r[4];
+  if constexpr (kBf16In) {
+    const uint16_t* src = static_cast<const uint16_t*>(kv) + row * D;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * lane);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_bits_to_f32(uint16_t(w4[j] & 0xFFFFu));
+      x[2 * j + 1] = bf16_bits_to_f32(uint16_t(w4[j] >> 16));
+    }
+    if (lane < 16) {
+      // bf16 rope values are copied as they are
+      const uint2 rp = *reinterpret_cast<const uint2*>(src + kMlaLatent + 4 * lane);
+      *reinterpret_cast<uint2*>(cache + slot * kMlaRow8 + kMlaLatent + 16 + 8 * lane) = rp;
+    }
+  } else {
+    const float* src = static_cast<const float*>(kv) + row * D;
+    const float4 a = *reinterpret_cast<const float4*>(src + 8 * lane);
+    const float4 b = *reinterpret_cast<const float4*>(src + 8 * lane + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    if (lane < 16) {
+      const float4 c = *reinterpret_cast<const float4*>(src + kMlaLatent + 4 * lane);
+      r[0] = c.x; r[1] = c.y; r[2] = c.z; r[3] = c.w;
+      const uint32_t lo = uint32_t(f32_to_bf16_bits(r[0])) | (uint32_t(f32_to_bf16_bits(r[1])) << 16);
+      const uint32_t hi = uint32_t(f32_to_bf16_bits(r[2])) | (uint32_t(f32_to_bf16_bits(r[3])) << 16);
+      *reinterpret_cast<uint2*>(cache + slot * kMlaRow8 + kMlaLatent + 16 + 8 * lane) =
+          make_uint2(lo, hi);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  const float s = pow2_scale(xor16_max<8>(amax));
+  uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo |= uint32_t(encode_e4m3(x[j] / s)) << (8 * j);
+    hi |= uint32_t(encode_e4m3(x[4 + j] / s)) << (8 * j);
+  }
+  uint8_t* dst = cache + slot * kMlaRow8;
+  *reinterpret_cast<uint2*>(dst + 8 * lane) = make_uint2(lo, hi);
+  if ((lane & 15) == 0) *reinterpret_cast<float*>(dst + kMlaLatent + 4 * (lane >> 4)) = s;
+}
+
 __global__ __launch_bounds__(256) void row_windows_kernel(const int32_t* __restrict__ cu_q,
                                                           const int32_t* __restrict__ cu_k,
                                                           int n_seqs, int64_t n_rows, int causal,
@@ -444,6 +505,20 @@ hipError_t launch_indexer_k_insert(const void* k_raw, int32_t k_dtype, const flo
   } else {
     return hipErrorInvalidValue;  // rejected by the C ABI before this point
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_kv_insert(const void* kv, int32_t kv_dtype, const int64_t* slot_mapping,
+                                int64_t n_tokens, uint8_t* kv_cache, int64_t n_slots,
+                                hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  const unsigned grid = unsigned((n_tokens + 3) / 4);
+  if (kv_dtype == 1)
+    hipLaunchKernelGGL(mla_kv_insert_kernel<true>, dim3(grid), dim3(256), 0, stream, kv,
+                       slot_mapping, n_tokens, n_slots, kv_cache);
+  else
+    hipLaunchKernelGGL(mla_kv_insert_kernel<false>, dim3(grid), dim3(256), 0, stream, kv,
+                       slot_mapping, n_tokens, n_slots, kv_cache);
   return hipGetLastError();
 }
 

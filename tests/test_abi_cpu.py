@@ -118,13 +118,34 @@ def test_mla_rejects_bad_arguments(lib):
     assert call(dqk=512) == UNSUPPORTED
     assert call(h=100) == UNSUPPORTED
     assert call(dv=600) == INVALID
-    assert call(dt=2) == UNSUPPORTED
+    assert call(dt=2, dqk=512) == UNSUPPORTED               # the fp8 latent cache: 576 only
+    assert call(dt=2, out=ctypes.c_void_p(FAKE32.value + 4)) == UNSUPPORTED  # out 8-aligned
+    assert call(dt=5) == INVALID
     assert call(k=0) == INVALID
     assert call(out=None) == INVALID
     # decode-sized call needs split workspace
     need = lib.dsa_sparse_mla_workspace_size(4, 128, 576, 512, 2048, 1)
     assert need == 4 * 16 * 128 * (512 * 2 + 4)     # 16 splits: bf16 partial o, fp32 partial lse
     assert call() == WORKSPACE
+    # the fp8 latent cache splits the same way
+    assert lib.dsa_sparse_mla_workspace_size(4, 128, 576, 512, 2048, 2) == need
+    assert call(dt=2) == WORKSPACE
+
+
+def test_mla_kv_insert_rejects_bad_arguments(lib):
+    a = [FAKE32, 1, FAKE, 4, 576, FAKE32, 8, None]
+    def call(i, v):
+        b = list(a)
+        b[i] = v
+        return lib.dsa_mla_kv_insert(*b)
+    assert call(4, 512) == UNSUPPORTED                    # rows are 512 latent + 64 rope
+    assert call(1, 2) == UNSUPPORTED                      # fp8 input rows
+    assert call(1, 7) == INVALID
+    assert call(0, None) == INVALID
+    assert call(2, None) == INVALID
+    assert call(5, None) == INVALID
+    assert call(3, -1) == INVALID
+    assert call(5, ctypes.c_void_p(FAKE32.value + 8)) == UNSUPPORTED  # cache 16-aligned
 
 
 def test_windows_and_prep_reject_bad_arguments(lib):

@@ -508,6 +508,162 @@ def test_mla_bf16_fewer_heads(dsa):
 
 
 # ---------------------------------------------------------------------------
+# sparse MLA over the fp8 latent cache (656-byte rows)
+# ---------------------------------------------------------------------------
+def _pack_mla_fp8(codes, scales, rope) -> np.ndarray:
+    """Cache rows [N, 656] from the oracle's quantisation: 512 e4m3 code bytes,
+    4 fp32 scales, 64 bf16 rope values (every value is exact in its format)."""
+    N = codes.shape[0]
+    c = torch.from_numpy(np.ascontiguousarray(codes, np.float32)).to(torch.float8_e4m3fn)
+    s = torch.from_numpy(np.ascontiguousarray(scales, np.float32))
+    r = torch.from_numpy(np.ascontiguousarray(rope, np.float32)).to(torch.bfloat16)
+    row = torch.cat([c.view(torch.uint8), s.view(torch.uint8).reshape(N, 16),
+                     r.view(torch.uint8).reshape(N, 128)], dim=1)
+    assert row.shape == (N, 656)
+    return row.numpy()
+
+
+def _fp8_cache(kv):
+    """(cache bytes [N, 656], the dequantised rows [N, 576] the kernel reads)."""
+    codes, s, rope = o_prep.mla_kv_quant(kv)
+    return _pack_mla_fp8(codes, s, rope), o_prep.dequant_mla_kv(codes, s, rope)
+
+
+def _mla_fp8_case(dsa, q, kv, idx, sm, what, rows=None, oracle_idx=None, cache=None):
+    """q bf16 values [n_q, H, 576]; kv the latent rows before quantisation."""
+    packed, kv_deq = _fp8_cache(kv)
+    cache_d = torch.from_numpy(packed).cuda() if cache is None else cache
+    qd = dev(q, torch.bfloat16)
+    say(f"mla fp8 {what}: n_q={q.shape[0]} H={q.shape[1]} n_kv={kv.shape[0]} K={idx.shape[1]}")
+    out, lse = dsa.dsa_sparse_mla_fwd(qd, cache_d, i32(idx), sm, 512)
+    assert out.dtype == torch.bfloat16
+    rows = list(range(q.shape[0])) if rows is None else list(rows)
+    oidx = idx if oracle_idx is None else oracle_idx
+    oo, ol = o_mla.sparse_mla(q, kv_deq, oidx, sm, 512, rows=rows)
+    tol = mla_lse_tol(q[rows], kv_deq, oidx[rows], sm, True, ol)
+    err = check_mla(host(out)[rows], oo, host(lse)[rows], ol, True, what, lse_tol=tol)
+    say(f"  max abs err {err:.2e}")
+
+
+def test_mla_fp8_prefill(dsa):
+    g = np.random.default_rng(211)
+    n_q, n_kv = 200, 3000                                  # one workgroup per query
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q))
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk, holes=True)
+    idx[0] = -1                                            # empty row: out 0, lse -inf
+    idx[1, 1:] = -1                                        # one key
+    idx[2, 33:] = -1                                       # a ragged last tile
+    _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, "prefill", rows=list(range(6)) +
+                  list(range(6, n_q, 9)))
+
+
+def test_mla_fp8_split_peaky(dsa):
+    g = np.random.default_rng(212)
+    n_q, n_kv = 6, 5000                                    # few queries: keys split
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q) * 800.0)
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk, holes=True)
+    _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, "split peaky")
+
+
+def test_mla_fp8_large_logit_growth(dsa):
+    # a later tile's max far above the first one's: the second pass
+    g = np.random.default_rng(213)
+    n_kv = 4096
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    kv[:, 512] += np.linspace(0.0, 40.0, n_kv, dtype=np.float32)
+    for n_q, what in ((12, "split"), (200, "prefill")):
+        q = synth.mla_q(P4K, 0, n_q)
+        q[:, :, 512] += 120.0
+        q = o_prep.round_bf16(q)
+        idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk)
+        _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, f"logit growth {what}",
+                      rows=range(0, n_q, 3))
+
+
+@pytest.mark.parametrize("n_q", [10, 300])
+def test_mla_fp8_out_of_range_indices(dsa, n_q):
+    g = np.random.default_rng(214)
+    n_kv = 900
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q))
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    idx = _random_topk_rows(g, n_q, n_kv, 512, holes=True)
+    bad = idx.copy()
+    pos = g.random(idx.shape) < 0.1
+    junk = g.choice(np.array([n_kv, n_kv + 1, 2 ** 31 - 1, -2, -(2 ** 31)], np.int64), idx.shape)
+    bad[pos] = junk[pos].astype(np.int32)
+    bad[0, :] = n_kv + 5
+    oracle_idx = np.where((bad >= 0) & (bad < n_kv), bad, -1).astype(np.int32)
+    _mla_fp8_case(dsa, q, kv, bad, P4K.sm_scale, f"out-of-range n_q={n_q}",
+                  rows=range(0, n_q, 1 if n_q < 50 else 11), oracle_idx=oracle_idx)
+
+
+@pytest.mark.parametrize("H", [96, 40])
+def test_mla_fp8_fewer_heads(dsa, H):
+    # 96: whole waves idle; 40: a wave with 8 of its 16 heads
+    g = np.random.default_rng(215)
+    n_q, n_kv = 30, 700
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q)[:, :H])
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    idx = _random_topk_rows(g, n_q, n_kv, 512)
+    _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, f"H={H}")
+
+
+def test_mla_fp8_wide_value_range(dsa):
+    # rows whose 128-dim tiles differ in magnitude by 2^-12 .. 2^6 (tiny tiles
+    # quantise to e4m3 subnormals), an all-zero row and tiles of zeros
+    g = np.random.default_rng(216)
+    n_q, n_kv = 8, 1500
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    tile_mag = 2.0 ** g.integers(-12, 7, size=(n_kv, 4))
+    kv[:, :512] *= np.repeat(tile_mag, 128, axis=1).astype(np.float32)
+    kv[5] = 0.0
+    kv[7, 128:256] = 0.0
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q))
+    idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk)
+    idx[0, :3] = [5, 7, 9]
+    _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, "wide value range")
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_mla_kv_insert_bytes(dsa, src):
+    # every written byte equals the oracle's quantisation; other slots untouched
+    g = np.random.default_rng(217)
+    n_tok, n_slots = 300, 700
+    kv = synth.mla_kv(P4K, 0, n_tok)
+    kv[:, :512] *= np.repeat(2.0 ** g.integers(-10, 8, size=(n_tok, 4)), 128, axis=1)
+    kv[3] = 0.0
+    kv[4, :128] = 0.0
+    kv = o_prep.round_bf16(kv) if src == "bf16" else o_prep.round_f32(kv)
+    slots = g.permutation(n_slots)[:n_tok].astype(np.int64)
+    slots[::17] = -1
+    slots[5] = n_slots + 3                                 # outside the cache: skipped
+    tdt = torch.bfloat16 if src == "bf16" else torch.float32
+    fill = g.integers(0, 256, size=(n_slots, 656)).astype(np.uint8)
+    cache = torch.from_numpy(fill.copy()).cuda()
+    say(f"mla kv insert {src}: n_tok={n_tok} n_slots={n_slots}")
+    dsa.dsa_mla_kv_insert(dev(kv, tdt), torch.from_numpy(slots).cuda(), cache)
+    got = cache.cpu().numpy()
+    want = fill.copy()
+    ok = (slots >= 0) & (slots < n_slots)
+    want[slots[ok]] = _pack_mla_fp8(*o_prep.mla_kv_quant(kv[ok]))
+    assert np.array_equal(got, want), f"{int((got != want).any(axis=1).sum())} rows differ"
+
+
+def test_mla_fp8_decode_from_inserted_cache(dsa):
+    # decode: the cache written by dsa_mla_kv_insert, read by the fp8 attention
+    g = np.random.default_rng(218)
+    n_q, n_kv = 4, 6000
+    kv = o_prep.round_bf16(synth.mla_kv(P4K, 0, n_kv))
+    cache = torch.zeros((n_kv, 656), dtype=torch.uint8, device="cuda")
+    dsa.dsa_mla_kv_insert(dev(kv, torch.bfloat16), torch.arange(n_kv, device="cuda"), cache)
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q))
+    idx = _random_topk_rows(g, n_q, n_kv, P4K.index_topk)
+    _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, "decode from inserted cache", cache=cache)
+
+
+# ---------------------------------------------------------------------------
 # input preparation
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])

@@ -92,3 +92,29 @@ def test_special_cases():
     np.testing.assert_allclose(o4[0], w29 * kv_big[29, :dv] + (1 - w29) * kv_big[28, :dv]
                                + np.exp(-260.0) * w29 * (kv_big[3, :dv] - kv_big[28, :dv]),
                                rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_latent_cache_rows():
+    # the fp8 latent row: e4m3 codes with a power-of-two scale per 128 latent
+    # dims, rope dims in bf16; dequantised rows are exact in bf16 (e4m3 times a
+    # power of two), and attention on them is attention on those rows
+    from oracle import prep
+    g = np.random.default_rng(33)
+    kv = prep.round_bf16(g.standard_normal((40, 576)) * 0.1 * np.exp2(g.integers(-3, 4, (40, 1))))
+    codes, sc, rope = prep.mla_kv_quant(kv)
+    assert codes.shape == (40, 512) and sc.shape == (40, 4) and rope.shape == (40, 64)
+    np.testing.assert_array_equal(rope, kv[:, 512:])
+    m, _ = np.frexp(sc)
+    assert np.all(m == 0.5)
+    amax = np.abs(kv[:, :512].reshape(40, 4, 128)).max(-1)
+    assert np.all(amax <= 448 * sc) and np.all(amax > 224 * sc)
+    deq = prep.dequant_mla_kv(codes, sc, rope)
+    np.testing.assert_array_equal(prep.round_bf16(deq), deq)
+    big = np.abs(codes) >= 2 ** -6
+    rel = np.abs(deq[:, :512] - kv[:, :512])[big] / np.abs(kv[:, :512])[big]
+    assert rel.max() <= 2 ** -4
+    q = g.standard_normal((4, 576))
+    idx = np.array([3, 17, -1, 8, 39])
+    o1, l1 = mla.attend_row(q, deq, idx, 576 ** -0.5, 512)
+    o2, l2 = mla.attend_row(q, np.asarray(deq), idx, 576 ** -0.5, 512)
+    np.testing.assert_array_equal(o1, o2)
