@@ -261,6 +261,129 @@ __device__ __forceinline__ void wait_tile(bool next_in_flight) {
   static_assert(kDmaPerWave == 9, "vmcnt immediate");
 }
 
+// ---------------------------------------------------------------------------
+// fp8 latent rows ("fp8_ds_mla", 656 bytes: 512 e4m3 codes, 4 fp32 scales, 64
+// bf16 rope values).  Wave w gathers the rows of keys w, w+4, ..., w+28 of a
+// tile into its own staging area (8 rows back to back, 41 16-byte pieces each:
+// piece p = 64 v + lane of load v is piece p % 41 of row p / 41), and later
+// converts the same rows into the bf16 tile layout above.  No other wave
+// touches a wave's staging area, so its only synchronisation is the wave's own
+// vector-memory count.
+constexpr int kRow8 = 656;
+constexpr int kPieces8 = kRow8 / 16;                          // 41
+constexpr int kRowsPerWave8 = kKT / kWaves;                   // 8
+constexpr int kWaveStage8 = kRowsPerWave8 * kRow8;            // 5248
+constexpr int kStage8 = kWaves * kWaveStage8;                 // 20992
+constexpr int kLoads8 = (kRowsPerWave8 * kPieces8 + kWave - 1) / kWave;  // 6 loads per wave
+static_assert(kPieces8 * 16 == kRow8, "rows are whole 16-byte pieces");
+
+__shared__ __attribute__((aligned(16))) uint8_t g_st8a[kStage8];
+__shared__ __attribute__((aligned(16))) uint8_t g_st8b[kStage8];
+
+// The rows of this wave's loads of local tile lt, read from the staged slice
+// ahead of the loads (and of the fragment reads they are issued between):
+// element v is the row of the piece lane l moves in load v.
+struct DmaRows8 {
+  int row[kLoads8];
+};
+__device__ __forceinline__ DmaRows8 dma_rows8(const int* sidx, int lt, int wave, int lane) {
+  int l = lane;
+  asm volatile("" : "+v"(l));  // recomputed here, not held in registers
+  DmaRows8 d;
+#pragma unroll
+  for (int v = 0; v < kLoads8; ++v) {
+    const int p = min(v * kWave + l, kRowsPerWave8 * kPieces8 - 1);
+    d.row[v] = sidx[lt * kKT + wave + kWaves * (p / kPieces8)];
+  }
+  return d;
+}
+
+// load v of this wave's gather into staging buffer `stage` (the last load moves
+// the 8 pieces left over: lanes 0..7)
+template <int V>
+__device__ __forceinline__ void dma_stage8(uint8_t* stage, const DmaRows8& rows,
+                                           const uint8_t* __restrict__ kv, int wave, int lane) {
+  constexpr int kLast = kRowsPerWave8 * kPieces8 - (kLoads8 - 1) * kWave;  // 8
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  if (V + 1 < kLoads8 || l < kLast) {
+    const int p = V * kWave + l;
+    const int part = p - (p / kPieces8) * kPieces8;
+    const uint8_t* src = kv + uint64_t(uint32_t(rows.row[V])) * kRow8 + part * 16;
+    asm volatile("global_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "{m0}"(lds_addr(stage + wave * kWaveStage8 + V * 1024))
+                 : "memory");
+  }
+}
+
+template <int V = 0>
+__device__ __forceinline__ void dma_stage8_at(int v, uint8_t* stage, const DmaRows8& rows,
+                                              const uint8_t* __restrict__ kv, int wave, int lane) {
+  if constexpr (V < kLoads8) {
+    if (v == V) dma_stage8<V>(stage, rows, kv, wave, lane);
+    else dma_stage8_at<V + 1>(v, stage, rows, kv, wave, lane);
+  }
+}
+
+__device__ __forceinline__ void dma_tile8(uint8_t* stage, const int* sidx, int lt,
+                                          const uint8_t* __restrict__ kv, int wave, int lane) {
+  const DmaRows8 rows = dma_rows8(sidx, lt, wave, lane);
+#pragma unroll
+  for (int v = 0; v < kLoads8; ++v) dma_stage8_at(v, stage, rows, kv, wave, lane);
+}
+
+// Wait until this wave's gather of the tile before the last one issued has
+// landed (the last one's kLoads8 loads may stay in flight).
+__device__ __forceinline__ void wait_stage8(bool next_in_flight) {
+  if (next_in_flight) {
+    __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
+  static_assert(kLoads8 == 6, "vmcnt immediate");
+}
+
+// This wave's 8 staged rows into tile buffer B.  Latent: row k of the wave
+// (key wave + 4 k) is one pass in which lane l converts codes 8 l .. 8 l + 7
+// (scale l / 16) into the 16-byte chunk l of the row's bf16 slot, so every read
+// and write of the pass covers consecutive bytes.  Rope: one pass, lane
+// l = 8 c + k moving rope dims 8 c .. 8 c + 7 of row k.  code * scale is exact
+// in bf16 for the power-of-two scales of the cache
+// (v_cvt_scalef32_pk_bf16_fp8).
+template <int B>
+__device__ __forceinline__ void dequant_stage8(const uint8_t* stage, int wave, int lane_in) {
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));  // addresses rebuilt here, not held in registers
+  const uint8_t* rows = stage + wave * kWaveStage8;
+  constexpr int kHalf = kRowsPerWave8 / 2;  // rows read together (register budget)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint2 w[kHalf];
+    float sc[kHalf];
+#pragma unroll
+    for (int j = 0; j < kHalf; ++j) {
+      const uint8_t* row = rows + (kHalf * h + j) * kRow8;
+      w[j] = *reinterpret_cast<const uint2*>(row + 8 * lane);
+      sc[j] = *reinterpret_cast<const float*>(row + 512 + 4 * (lane >> 4));
+    }
+#pragma unroll
+    for (int j = 0; j < kHalf; ++j) {
+      const int k = kHalf * h + j;
+      const uint32_t y0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j].x, sc[j], false));
+      const uint32_t y1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j].x, sc[j], true));
+      const uint32_t y2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j].y, sc[j], false));
+      const uint32_t y3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j].y, sc[j], true));
+      *reinterpret_cast<uint4*>(kvbuf<B>() + kslot(wave + kWaves * k) * kRowA + 16 * lane) =
+          make_uint4(y0, y1, y2, y3);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one half's registers at a time
+  }
+  const int rk = lane & 7, rc = lane >> 3;
+  const uint4 rope = *reinterpret_cast<const uint4*>(rows + rk * kRow8 + 528 + 16 * rc);
+  *reinterpret_cast<uint4*>(kvbuf<B>() + kRegionA + rc * 512 + (wave + kWaves * rk) * 16) = rope;
+}
+
 // V fragment m = 2n + ks (value tile n, key step ks) of the tile in buffer B (or
 // `buf` when B < 0): the A operand of the V^T . P^T MFMA (8 keys x 1 value column
 // per lane), read from the row-major tile with ds_read_b64_tr_b16: in each group of
@@ -287,10 +410,11 @@ __device__ __forceinline__ bf16x8_t vfrag(const uint8_t* buf, int m, int lane) {
 // the fragment reads run two steps ahead of their MFMA.  With kDma, the
 // LDS-DMA loads of a later tile (into buffer BD) are issued between the MFMAs
 // (the wave can issue them while the matrix core works).
-template <int B, int BD, bool kDma, int BV>
+template <int B, int BD, bool kDma, int BV, bool kF8 = false>
 __device__ __forceinline__ f32x16_t qk_tile(bf16x8_t (&fr)[4], const bf16x8_t (&qf)[kQSteps],
                                             uint32_t vmask, int lane, const int* sidx, int lt_dma,
-                                            const uint8_t* __restrict__ kv, int wave) {
+                                            const uint8_t* __restrict__ kv, int wave,
+                                            uint8_t* stage = nullptr) {
   const int kk = lane & 31;
   const int h = lane >> 5;
   const uint8_t* ka = kvbuf<B>() + kslot(kk) * kRowA + h * 16;  // latent K-steps 0..31
@@ -301,7 +425,9 @@ __device__ __forceinline__ f32x16_t qk_tile(bf16x8_t (&fr)[4], const bf16x8_t (&
     return *reinterpret_cast<const bf16x8_t*>(st < 32 ? ka + st * 32 : kr + (st - 32) * 1024);
   };
   DmaRows rows{};
-  if constexpr (kDma) rows = dma_rows(sidx, lt_dma, lane);  // ahead of the ring reads
+  if constexpr (kDma && !kF8) rows = dma_rows(sidx, lt_dma, lane);  // ahead of the ring reads
+  DmaRows8 rows8{};
+  if constexpr (kDma && kF8) rows8 = dma_rows8(sidx, lt_dma, wave, lane);
   // fragment reads four steps ahead: one explicit wait per MFMA.  With BV >= 0
   // the last four steps read V fragments 0..3 of buffer BV into the ring for
   // the P.V that follows (two LDS reads each), so that it starts without a wait.
@@ -320,7 +446,10 @@ __device__ __forceinline__ f32x16_t qk_tile(bf16x8_t (&fr)[4], const bf16x8_t (&
     else mfma_v(s, fr[st % 4], qf[st]);
     if (st + 4 < kQSteps) fr[st % 4] = frag(st + 4);
     else if constexpr (BV >= 0) fr[st % 4] = vfrag<BV>(nullptr, st + 4 - kQSteps, lane);
-    if constexpr (kDma) {
+    if constexpr (kDma && kF8) {
+      // the gather of a later tile into the wave's staging rows
+      if (st % 4 == 1 && st / 4 < kLoads8) dma_stage8_at(st / 4, stage, rows8, kv, wave, lane);
+    } else if constexpr (kDma) {
       // the gather of a later tile, spread between the MFMAs
       if (st % 4 == 1 && st / 4 < kKT / kWaves) dma_latent<BD>(rows, st / 4, kv, wave, lane);
       if (st == 33) dma_rope<BD>(rows, kv, wave, lane);
@@ -507,12 +636,47 @@ __device__ __forceinline__ void tile_step(MlaShared& sh, int i, int nt, const ui
   vm = sh.vmask[i + 1];  // the next tile's mask, read well before it is needed
 }
 
+// One tile step i over fp8 rows (tile buffer B = i % 3, staging buffer i % 2):
+// S(i) = K(i).Q^T with the gather of tile i+2 into the staging buffer tile i
+// left, O += P(i-1).V(i-1) with the softmax of S(i), then the wave's rows of
+// tile i+1 (staged one step earlier) into tile buffer (i+1) % 3, free since
+// every wave passed this step's barrier after its P.V of tile i-2.
+template <int B>
+__device__ __forceinline__ void tile_step8(MlaShared& sh, int i, int nt, const uint8_t* kvb,
+                                           const bf16x8_t (&qf)[kQSteps], f32x16_t (&o)[kVTiles],
+                                           bf16x8_t& p0, bf16x8_t& p1, uint32_t& vm,
+                                           float& m_ref, float& m_max, bool& over, float& l_run,
+                                           float scale2, int wave, int lane) {
+  wait_lgkm<0>();  // this wave's conversion writes have landed
+  __builtin_amdgcn_s_barrier();  // tile i converted by every wave
+  Softmax sm;
+  bf16x8_t fr[4];
+  if (i + 2 < nt) {
+    sm.s = qk_tile<B, 0, true, (B + 2) % 3, true>(fr, qf, vm, lane, sh.idx, i + 2, kvb, wave,
+                                                  (i & 1) ? g_st8b : g_st8a);
+  } else {
+    sm.s = qk_tile<B, 0, false, (B + 2) % 3>(fr, qf, vm, lane, sh.idx, 0, kvb, wave);
+  }
+  pv_tile<(B + 2) % 3, true, false>(fr, nullptr, p0, p1, o, lane, sm, scale2, m_ref, m_max, over,
+                                    l_run);
+  p0 = sm.p0();
+  p1 = sm.p1();
+  if (i + 1 < nt) {
+    wait_stage8(i + 2 < nt);
+    dequant_stage8<(B + 1) % 3>((i & 1) ? g_st8a : g_st8b, wave, lane);
+  }
+  vm = sh.vmask[i + 1];
+}
+
 // One workgroup: one query x 128 heads (wave w: heads 32w .. 32w+31 of the
 // block's head range), or one key slice of it in split mode.  The query's Q^T
 // stays in registers (144 per lane), O [32 heads x 512] in 256 accumulation
-// registers per lane.
-__global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
+// registers per lane.  kF8: kv holds fp8 rows (656 bytes), gathered into
+// per-wave staging rows and converted to bf16 tiles one step ahead of use (three
+// tile buffers); otherwise bf16 rows are gathered straight into four tile buffers.
+template <bool kF8>
+__device__ __forceinline__ void mla_body(
+    const __bf16* __restrict__ q, const void* __restrict__ kv,
     const int32_t* __restrict__ idx, int n_kv, int H, int K, float sm_scale,
     __bf16* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_lse, int nsplit) {
@@ -584,9 +748,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     i1 = last < 0 ? i0 : i0 + last / kKT + 1;
   }
   const int nt = i1 - i0;
-  // tiles are run in groups of four after tile 0: pad with masked tiles that
-  // gather row 0 (finite values: a masked key's P is 0, and 0 * V must stay 0)
-  const int nt4 = nt > 0 ? 1 + 4 * ((nt + 2) / 4) : 0;
+  // tiles are run in groups of four (fp8: three) after tile 0: pad with masked
+  // tiles that gather row 0 (finite values: a masked key's P is 0, and 0 * V
+  // must stay 0)
+  const int nt4 = nt <= 0 ? 0 : kF8 ? 1 + 3 * ((nt + 1) / 3) : 1 + 4 * ((nt + 2) / 4);
   for (int x = nt * kKT + tid; x < nt4 * kKT; x += kThreads) {
     sh.idx[x] = 0;
     if ((x & (kKT - 1)) == 0) sh.vmask[x / kKT] = 0u;
@@ -608,40 +773,82 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     l_run = 0.0f;
     bool over = false;
     bf16x8_t p0 = bf16x8_t{}, p1 = bf16x8_t{};
-    if (nt4 > 0) dma_tile<0>(sh.idx, 0, kvb, wave, lane);
-    if (nt4 > 1) dma_tile<1>(sh.idx, 1, kvb, wave, lane);
-    if (nt4 > 0) {
-      // tile 0: no P.V yet
-      wait_tile(nt4 > 1);
-      __builtin_amdgcn_s_barrier();
-      if (nt4 > 2) dma_tile<2>(sh.idx, 2, kvb, wave, lane);
-      {
-        Softmax sm;
+    if constexpr (kF8) {
+      if (nt4 > 0) dma_tile8(g_st8a, sh.idx, 0, kvb, wave, lane);
+      if (nt4 > 1) dma_tile8(g_st8b, sh.idx, 1, kvb, wave, lane);
+      if (nt4 > 0) {
+        // tile 0: converted, then S and softmax only
+        wait_stage8(nt4 > 1);
+        dequant_stage8<0>(g_st8a, wave, lane);
+        wait_lgkm<0>();
+        __builtin_amdgcn_s_barrier();
+        {
+          Softmax sm;
+          bf16x8_t fr[4];
+          if (nt4 > 2)
+            sm.s = qk_tile<0, 0, true, -1, true>(fr, qf, sh.vmask[0], lane, sh.idx, 2, kvb, wave,
+                                                 g_st8a);
+          else
+            sm.s = qk_tile<0, 0, false, -1>(fr, qf, sh.vmask[0], lane, sh.idx, 0, kvb, wave);
+          softmax_all(sm, scale2, m_ref, m_max, over, l_run);
+          p0 = sm.p0();
+          p1 = sm.p1();
+        }
+        if (nt4 > 1) {
+          wait_stage8(nt4 > 2);
+          dequant_stage8<1>(g_st8b, wave, lane);
+        }
+        uint32_t vm = sh.vmask[1];
+        for (int i = 1; i < nt4; i += 3) {
+          tile_step8<1>(sh, i, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
+                        wave, lane);
+          tile_step8<2>(sh, i + 1, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
+                        wave, lane);
+          tile_step8<0>(sh, i + 2, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
+                        wave, lane);
+        }
+        const int lb = (nt4 - 1) % 3;
+        const uint8_t* buf = lb == 0 ? g_kv0 : lb == 1 ? g_kv1 : g_kv2;
+        Softmax none;
         bf16x8_t fr[4];
-        sm.s = qk_tile<0, 0, false, -1>(fr, qf, sh.vmask[0], lane, sh.idx, 0, kvb, wave);
-        softmax_all(sm, scale2, m_ref, m_max, over, l_run);
-        p0 = sm.p0();
-        p1 = sm.p1();
+        pv_tile<-1, false, true>(fr, buf, p0, p1, o, lane, none, scale2, m_ref, m_max, over, l_run);
       }
-      uint32_t vm = sh.vmask[1];
-      // tiles 1 .. nt4-1 in groups of four (one exit: a loop left in the middle
-      // makes the register allocator copy O out of the accumulation registers)
-      for (int i = 1; i < nt4; i += 4) {
-        tile_step<1>(sh, i, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave, lane);
-        tile_step<2>(sh, i + 1, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
-                     lane);
-        tile_step<3>(sh, i + 2, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
-                     lane);
-        tile_step<0>(sh, i + 3, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
-                     lane);
+    } else {
+      if (nt4 > 0) dma_tile<0>(sh.idx, 0, kvb, wave, lane);
+      if (nt4 > 1) dma_tile<1>(sh.idx, 1, kvb, wave, lane);
+      if (nt4 > 0) {
+        // tile 0: no P.V yet
+        wait_tile(nt4 > 1);
+        __builtin_amdgcn_s_barrier();
+        if (nt4 > 2) dma_tile<2>(sh.idx, 2, kvb, wave, lane);
+        {
+          Softmax sm;
+          bf16x8_t fr[4];
+          sm.s = qk_tile<0, 0, false, -1>(fr, qf, sh.vmask[0], lane, sh.idx, 0, kvb, wave);
+          softmax_all(sm, scale2, m_ref, m_max, over, l_run);
+          p0 = sm.p0();
+          p1 = sm.p1();
+        }
+        uint32_t vm = sh.vmask[1];
+        // tiles 1 .. nt4-1 in groups of four (one exit: a loop left in the middle
+        // makes the register allocator copy O out of the accumulation registers)
+        for (int i = 1; i < nt4; i += 4) {
+          tile_step<1>(sh, i, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave, lane);
+          tile_step<2>(sh, i + 1, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
+                       lane);
+          tile_step<3>(sh, i + 2, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
+                       lane);
+          tile_step<0>(sh, i + 3, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
+                       lane);
+        }
+        // P.V of the last tile: no gather is in flight any more, so its buffer can
+        // be chosen at run time
+        const int lb = (nt4 - 1) & 3;
+        const uint8_t* buf = lb == 0 ? g_kv0 : lb == 1 ? g_kv1 : lb == 2 ? g_kv2 : g_kv3;
+        Softmax none;
+        bf16x8_t fr[4];
+        pv_tile<-1, false, true>(fr, buf, p0, p1, o, lane, none, scale2, m_ref, m_max, over, l_run);
       }
-      // P.V of the last tile: no gather is in flight any more, so its buffer can
-      // be chosen at run time
-      const int lb = (nt4 - 1) & 3;
-      const uint8_t* buf = lb == 0 ? g_kv0 : lb == 1 ? g_kv1 : lb == 2 ? g_kv2 : g_kv3;
-      Softmax none;
-      bf16x8_t fr[4];
-      pv_tile<-1, false, true>(fr, buf, p0, p1, o, lane, none, scale2, m_ref, m_max, over, l_run);
     }
     o_fence(o);  // the last MFMAs into O finish before O is read or cleared
     // the whole workgroup agrees on a second pass (its waves share barriers)
@@ -668,7 +875,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   // bytes per head: 16 bytes of padding move successive heads 4 banks apart),
   // four consecutive columns per 8-byte write, then reads back whole head rows
   // (lane j: columns 8 j .. 8 j + 7) and writes each with one 1 KB store.
-  uint8_t* eb = wave == 0 ? g_kv0 : wave == 1 ? g_kv1 : wave == 2 ? g_kv2 : g_kv3;
+  // (fp8: three tile buffers, so wave 3 stages its block after the others, in buffer 0)
+  if constexpr (kF8) {
+    if (wave == 3) __syncthreads();
+  }
+  uint8_t* eb = wave == 0 ? g_kv0 : wave == 1 ? g_kv1 : wave == 2 ? g_kv2 : kF8 ? g_kv0 : g_kv3;
   {
     uint8_t* wb = eb + (lane_e & 31) * kEpRow + 8 * half_e;
 #pragma unroll
@@ -701,6 +912,26 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       part_lse[(t * nsplit + blockIdx.z) * H + head_e] = lse_h;
     }
   }
+  if constexpr (kF8) {
+    if (wave < 3) __syncthreads();  // buffer 0 is free for wave 3
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
+    const int32_t* __restrict__ idx, int n_kv, int H, int K, float sm_scale,
+    __bf16* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
+    float* __restrict__ part_lse, int nsplit) {
+  mla_body<false>(q, kv, idx, n_kv, H, K, sm_scale, out, lse, part_o, part_lse, nsplit);
+}
+
+// The same over the fp8 latent cache (656-byte rows).
+__global__ __launch_bounds__(kThreads, 1) void mla_fp8_kernel(
+    const __bf16* __restrict__ q, const uint8_t* __restrict__ kv,
+    const int32_t* __restrict__ idx, int n_kv, int H, int K, float sm_scale,
+    __bf16* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
+    float* __restrict__ part_lse, int nsplit) {
+  mla_body<true>(q, kv, idx, n_kv, H, K, sm_scale, out, lse, part_o, part_lse, nsplit);
 }
 
 // Merge split partials (bf16, normalised per split): out = sum_s e^{lse_s - L} o_s
@@ -802,381 +1033,6 @@ __global__ __launch_bounds__(128) void mla_f32_kernel(const float* __restrict__ 
   if (lse && tid == 0) lse[t * H + h] = den > 0.0f ? mx + __logf(den) : -INFINITY;
 }
 
-// ---------------------------------------------------------------------------
-// Sparse MLA over the fp8 latent cache ("fp8_ds_mla", the kv_cache_dtype of
-// KimiK3DSAAttention): a row is 656 bytes -- 512 e4m3 latent codes, 4 fp32
-// scales (one per 128 latent dims), 64 bf16 rope dims.  Queries and outputs
-// are bf16.
-//
-// One workgroup = one query x 128 heads (or one key slice of it), 8 waves of
-// 16 heads, on v_mfma_f32_16x16x32_bf16.  Per tile of 32 selected keys:
-//   gather   LDS-DMA of the 32 rows (41 16-byte pieces each) into one of three
-//            staging buffers, issued two tiles ahead;
-//   dequant  all 512 threads convert the staged tile once into a bf16 tile
-//            (v_cvt_scalef32_pk_bf16_fp8: code * scale; exact for the
-//            power-of-two scales the insert writes), in the slot layout of the
-//            bf16 kernel (conflict-free K-fragment and transposed V reads);
-//   S^T=K.Q^T keys on M (two 16-key tiles), the wave's 16 heads on N, 18 steps
-//            of 32 dims; lane l then holds keys 4g..4g+3 and 16+4g..16+4g+3
-//            (g = l / 16) of head l % 16;
-//   softmax  fp32, base 2, against the head's first finite tile max; a later
-//            tile above it by more than 2^32 makes the workgroup run the query
-//            again against the true max (as the bf16 kernel);
-//   O^T+=V^T.P^T  the eight probabilities of the lane, rounded to bf16, are
-//            its B fragment as they lie (K order: keys 4g..4g+3, 16+4g..+3),
-//            and the V fragment takes the same keys in two transposing reads;
-//            32 tiles of 16 value columns, O^T in 128 registers per lane.
-// ---------------------------------------------------------------------------
-constexpr int kRow8 = 656;
-constexpr int kLatentCodes = 512;
-constexpr int kScaleOff = 512;
-constexpr int kRopeOff = 528;
-constexpr int kPieces8 = kRow8 / 16;  // 41
-static_assert(kPieces8 * 16 == kRow8, "rows are whole 16-byte pieces");
-constexpr int kStage8 = kKT * kRow8;                         // 20992
-constexpr int kThreads8 = 512;
-constexpr int kWaves8 = kThreads8 / kWave;                   // 8
-constexpr int kHeads8 = 16;                                  // per wave
-constexpr int kHeadsPerBlock8 = kWaves8 * kHeads8;           // 128
-constexpr int kLoads8 = (kKT * kPieces8 + kWave - 1) / kWave;  // 21 wave loads per tile
-constexpr int kSteps8 = kDqk / 32;                           // 18 K-steps of 32 dims
-constexpr int kVTiles8 = kDv / 16;                           // 32 value tiles of 16 columns
-
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4v_t __attribute__((ext_vector_type(4)));
-
-struct Mla8Shared {
-  int idx[kMaxIdx + kKT];         // the slice's rows (-1 and out of range -> row 0)
-  uint32_t vmask[kMaxTiles + 1];  // per tile: bit j = key j valid
-  int wlast[kWaves8];
-  int redo[2];
-};
-
-__shared__ __attribute__((aligned(16))) uint8_t g_st0[kStage8];
-__shared__ __attribute__((aligned(16))) uint8_t g_st1[kStage8];
-__shared__ __attribute__((aligned(16))) uint8_t g_st2[kStage8];
-__shared__ __attribute__((aligned(16))) uint8_t g_t8[kTileBytes];
-// Q^T steps kQReg8 .. 17 (dims 32 kQReg8 .. 575) for the block's 128 heads, the
-// rest stays in registers: 16 bytes per (step j = st - kQReg8, lane group g,
-// head), at ((j * 4 + g) * 128 + head) * 16
-constexpr int kQReg8 = 12;
-constexpr int kQLds8 = kSteps8 - kQReg8;  // 6
-__shared__ __attribute__((aligned(16))) uint8_t g_q8[kQLds8 * 4 * kHeadsPerBlock8 * 16];
-
-__device__ __forceinline__ uint8_t* stage8(int i) {
-  const int b = i % 3;
-  return b == 0 ? g_st0 : b == 1 ? g_st1 : g_st2;
-}
-
-// Wave loads of tile lt into stage buffer sb: load v of wave w moves pieces
-// (w + 8 v) * 64 + lane of the tile's 32 * 41 (key-major, each key's row
-// contiguous as in memory).  Returns nothing; every wave issues kLoads8 / 8
-// rounded by its index (3 for waves 0..4, 2 for 5..7).
-__device__ __forceinline__ void dma_tile8(uint8_t* sb, const int* sidx, int lt,
-                                          const uint8_t* __restrict__ kv, int wave, int lane) {
-#pragma unroll
-  for (int v = 0; v < (kLoads8 + kWaves8 - 1) / kWaves8; ++v) {
-    const int ld = wave + kWaves8 * v;
-    if (ld < kLoads8) {
-      const int p = ld * kWave + lane;
-      if (p < kKT * kPieces8) {
-        const int key = p / kPieces8;
-        const int part = p - key * kPieces8;
-        const uint8_t* src = kv + int64_t(sidx[lt * kKT + key]) * kRow8 + part * 16;
-        asm volatile("global_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(src), "{m0}"(lds_addr(sb + ld * 1024))
-                     : "memory");
-      }
-    }
-  }
-}
-
-// Wait until this wave's loads of the current tile landed (the next tile's may
-// stay in flight).
-__device__ __forceinline__ void wait_tile8(bool next_in_flight, int wave) {
-  if (!next_in_flight) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  } else if (wave < kLoads8 - 2 * kWaves8) {
-    __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
-  }
-  static_assert(kLoads8 - 2 * kWaves8 == 5, "waves 0..4 issue 3 loads per tile, 5..7 issue 2");
-}
-
-// The staged tile in sb into the bf16 tile (all 512 threads): thread -> key
-// tid / 16, latent dims 32 * (tid % 16) .. +32 (one scale) and rope dims
-// 4 * (tid % 16) .. +4.
-__device__ __forceinline__ void dequant_tile8(const uint8_t* sb, int tid) {
-  const int j = tid >> 4, part = tid & 15;
-  const uint8_t* row = sb + j * kRow8;
-  const uint4 c0 = *reinterpret_cast<const uint4*>(row + 32 * part);
-  const uint4 c1 = *reinterpret_cast<const uint4*>(row + 32 * part + 16);
-  const float sc = *reinterpret_cast<const float*>(row + kScaleOff + 4 * (part >> 2));
-  const uint2 rp = *reinterpret_cast<const uint2*>(row + kRopeOff + 8 * part);
-  const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  uint32_t o[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false);
-    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true);
-    o[2 * i] = __builtin_bit_cast(uint32_t, lo);
-    o[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
-  }
-  uint8_t* dst = g_t8 + kslot(j) * kRowA + 64 * part;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-  *reinterpret_cast<uint2*>(g_t8 + kRegionA + (part >> 1) * 512 + j * 16 + (part & 1) * 8) = rp;
-}
-
-// A fragment of S^T = K . Q^T: key 16 mt + l % 16, dims 32 st + 8 (l / 16) .. +8.
-__device__ __forceinline__ bf16x8_t kfrag8(int mt, int st, int lane) {
-  const int key = 16 * mt + (lane & 15), g = lane >> 4;
-  const uint8_t* p = st < 16 ? g_t8 + kslot(key) * kRowA + (32 * st + 8 * g) * 2
-                             : g_t8 + kRegionA + (4 * (st - 16) + g) * 512 + key * 16;
-  return *reinterpret_cast<const bf16x8_t*>(p);
-}
-
-// A fragment of O^T += V^T . P^T: value column 16 n + l % 16, keys 4g..4g+3 and
-// 16+4g..16+4g+3 (g = l / 16), by two transposing reads: in each group of 16
-// lanes, lane 4m + q names key row k0 + m, columns 16 n + 4q .. +4.
-__device__ __forceinline__ bf16x8_t vfrag8(int n, int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const int m = i >> 2, q = i & 3;
-  const uint8_t* r0 = g_t8 + kslot(4 * g + m) * kRowA + (16 * n + 4 * q) * 2;
-  const uint8_t* r1 = g_t8 + kslot(16 + 4 * g + m) * kRowA + (16 * n + 4 * q) * 2;
-  const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(r0));
-  const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(r1));
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Step n of the S^T product: key tile n & 1, dims 32 st .. with st = kQReg8 ..
-// 17 (Q^T from LDS) for the first 2 kQLds8 steps, then 0 .. kQReg8 - 1.
-constexpr int kSN = 2 * kSteps8;  // 36
-constexpr int kSRing = 4;         // A fragments in flight
-constexpr int kQRing = 3;         // Q^T fragments from LDS in flight (one per step pair)
-constexpr int kVRing = 3;         // V fragments in flight (two reads each)
-__host__ __device__ constexpr int s_step8(int n) {
-  return (n >> 1) < kQLds8 ? kQReg8 + (n >> 1) : (n >> 1) - kQLds8;
-}
-// step n reads its Q^T fragment from LDS (at the first step of its pair)
-__host__ __device__ constexpr bool s_qread8(int n) { return (n & 1) == 0 && (n >> 1) < kQLds8; }
-
-// Issue order of the S^T phase: the rope Q^T reads and the first kSRing A
-// fragments, then each MFMA followed by the read kSRing steps ahead, the last
-// MFMAs each followed by the two reads of one of the first V fragments.
-template <int I>
-__device__ __forceinline__ void sched_s8() {
-  if constexpr (I == 0) {
-    constexpr int q0 = (kSRing + 1) / 2 < kQLds8 ? (kSRing + 1) / 2 : kQLds8;
-    __builtin_amdgcn_sched_group_barrier(0x100, kSRing + q0, 0);
-  }
-  if constexpr (I < kSN) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (I + kSRing < kSN)
-      __builtin_amdgcn_sched_group_barrier(0x100, s_qread8(I + kSRing) ? 2 : 1, 0);
-    else if constexpr (I + kSRing - kSN < kVRing)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    sched_s8<I + 1>();
-  }
-}
-
-// Issue order of the P.V phase: each MFMA followed by the two reads of the V
-// fragment kVRing tiles ahead.
-template <int I>
-__device__ __forceinline__ void sched_v8() {
-  if constexpr (I < kVTiles8) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (I + kVRing < kVTiles8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    sched_v8<I + 1>();
-  }
-}
-
-__global__ __launch_bounds__(kThreads8) void mla_fp8kv_kernel(
-    const __bf16* __restrict__ q, const uint8_t* __restrict__ kv,
-    const int32_t* __restrict__ idx, int n_kv, int H, int K, float sm_scale,
-    __bf16* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_lse, int nsplit) {
-  __shared__ __attribute__((aligned(16))) Mla8Shared sh;
-  const int64_t t = int64_t(gridDim.x) - 1 - blockIdx.x;  // longest rows first
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int g = lane >> 4;
-  const int h0 = int(blockIdx.y) * kHeadsPerBlock8 + wave * kHeads8;
-  const int head = h0 + (lane & 15);
-  const bool hvalid = head < H;
-  const float scale2 = sm_scale * kLog2e;
-
-  const int ntiles = (K + kKT - 1) / kKT;
-  const int i0 = int(int64_t(ntiles) * blockIdx.z / nsplit);
-  int i1 = int(int64_t(ntiles) * (blockIdx.z + 1) / nsplit);
-  const int32_t* irow = idx + t * K;
-  const int jbase = i0 * kKT;
-  const int nx = (i1 - i0) * kKT;
-  constexpr int kPer = kMaxIdx / kThreads8;
-  int rv[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int x = tid + u * kThreads8;
-    const int j = jbase + x;
-    rv[u] = (x < nx && j < K) ? irow[j] : -1;
-  }
-  {
-    int wl = -1;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int x = tid + u * kThreads8;
-      const bool ok = unsigned(rv[u]) < unsigned(n_kv);  // -1 and out of range: masked
-      if (x < nx) sh.idx[x] = ok ? rv[u] : 0;
-      const uint64_t b = __ballot(x < nx && ok);
-      if (x < nx && lane == 0) sh.vmask[x / kKT] = uint32_t(b);
-      if (x < nx && lane == 32) sh.vmask[x / kKT] = uint32_t(b >> 32);
-      if (b != 0ull) wl = u * kThreads8 + wave * kWave + 63 - __builtin_clzll(b);
-    }
-    if (lane == 0) sh.wlast[wave] = wl;
-    __syncthreads();
-    int last = sh.wlast[0];
-#pragma unroll
-    for (int w = 1; w < kWaves8; ++w) last = max(last, sh.wlast[w]);
-    i1 = last < 0 ? i0 : i0 + last / kKT + 1;
-  }
-  // Q^T fragments: head h0 + l % 16 (a head past H reads head H-1: finite values
-  // whose results are never written), dims 32 st + 8 g .. +8; steps below
-  // kQReg8 in registers, the others in LDS
-  bf16x8_t qf[kQReg8];
-  {
-    const __bf16* qr = q + (t * H + (hvalid ? head : H - 1)) * int64_t(kDqk) + 8 * g;
-#pragma unroll
-    for (int st = 0; st < kQReg8; ++st) qf[st] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * st);
-#pragma unroll
-    for (int j = 0; j < kQLds8; ++j)
-      *reinterpret_cast<bf16x8_t*>(g_q8 + ((j * 4 + g) * kHeadsPerBlock8 + wave * kHeads8 +
-                                           (lane & 15)) * 16) =
-          *reinterpret_cast<const bf16x8_t*>(qr + 32 * (kQReg8 + j));
-  }
-  const int nt = i1 - i0;
-  if (tid < 2) sh.redo[tid] = 0;
-  __syncthreads();
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // Q^T landed before the first gather
-
-  f32x4v_t o[kVTiles8];
-  float m_ref = -FLT_MAX, m_max = -FLT_MAX, l_run = 0.0f;
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int n = 0; n < kVTiles8; ++n) o[n] = f32x4v_t{};
-    l_run = 0.0f;
-    bool over = false;
-    if (nt > 0) dma_tile8(stage8(0), sh.idx, 0, kv, wave, lane);
-    if (nt > 1) dma_tile8(stage8(1), sh.idx, 1, kv, wave, lane);
-    for (int i = 0; i < nt; ++i) {
-      wait_tile8(i + 1 < nt, wave);
-      __syncthreads();  // tile i staged by every wave; the bf16 tile is free
-      dequant_tile8(stage8(i), tid);
-      __syncthreads();  // the bf16 tile is complete; stage buffer i % 3 is free
-      if (i + 2 < nt) dma_tile8(stage8(i + 2), sh.idx, i + 2, kv, wave, lane);
-      // S^T for the 32 keys x the wave's 16 heads: 36 MFMA steps, the steps with
-      // Q^T in LDS first, the two key tiles alternating; A fragments are read
-      // kSRing steps ahead, LDS Q^T fragments with the A fragment of their pair
-      const uint8_t* qlds = g_q8 + (g * kHeadsPerBlock8 + wave * kHeads8 + (lane & 15)) * 16;
-      bf16x8_t kb[kSRing], qb[kQRing];
-#pragma unroll
-      for (int n = 0; n < kSRing; ++n) {
-        kb[n] = kfrag8(n & 1, s_step8(n), lane);
-        if (s_qread8(n))
-          qb[(n >> 1) % kQRing] = *reinterpret_cast<const bf16x8_t*>(
-              qlds + (s_step8(n) - kQReg8) * 4 * kHeadsPerBlock8 * 16);
-      }
-      f32x4v_t s[2] = {f32x4v_t{}, f32x4v_t{}};
-#pragma unroll
-      for (int n = 0; n < kSN; ++n) {
-        const int st = s_step8(n);
-        const bf16x8_t b = st >= kQReg8 ? qb[(n >> 1) % kQRing] : qf[st < kQReg8 ? st : 0];
-        s[n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[n % kSRing], b, s[n & 1], 0, 0, 0);
-        if (n + kSRing < kSN) {
-          const int m = n + kSRing;
-          kb[n % kSRing] = kfrag8(m & 1, s_step8(m), lane);
-          if (s_qread8(m))
-            qb[(m >> 1) % kQRing] = *reinterpret_cast<const bf16x8_t*>(
-                qlds + (s_step8(m) - kQReg8) * 4 * kHeadsPerBlock8 * 16);
-        }
-      }
-      // the first V fragments, read while the softmax runs
-      bf16x8_t vb[kVRing];
-#pragma unroll
-      for (int n = 0; n < kVRing; ++n) vb[n] = vfrag8(n, lane);
-      sched_s8<0>();
-      __builtin_amdgcn_sched_barrier(0);
-      // mask, tile max over the head's 32 keys (4 lanes), reference, P
-      const uint32_t vm = sh.vmask[i];
-      float tm = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * mt + 4 * g + r;
-          s[mt][r] = ((vm >> key) & 1u) ? s[mt][r] : -INFINITY;
-          tm = fmaxf(tm, s[mt][r]);
-        }
-      tm = fmaxf(tm, __shfl_xor(tm, 16));
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      tm *= scale2;
-      m_ref = m_ref == -FLT_MAX ? fmaxf(tm, -FLT_MAX) : m_ref;
-      m_max = fmaxf(m_max, tm);
-      over = over || tm > m_ref + kSpan;
-      bf16x8_t pb;
-      float ps = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const __bf16 p = __bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], scale2, -m_ref)));
-          pb[4 * mt + r] = p;
-          ps += float(p);
-        }
-      l_run += ps;
-      __builtin_amdgcn_sched_barrier(0);
-      // O^T += V^T . P^T over the 32 value tiles, V fragments kVRing tiles ahead
-#pragma unroll
-      for (int n = 0; n < kVTiles8; ++n) {
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[n % kVRing], pb, o[n], 0, 0, 0);
-        if (n + kVRing < kVTiles8) vb[n % kVRing] = vfrag8(n + kVRing, lane);
-      }
-      sched_v8<0>();
-    }
-    if (__ballot(over) != 0ull && lane == 0) sh.redo[pass] = 1;
-    __syncthreads();
-    if (sh.redo[pass] == 0) break;
-    m_ref = fmaxf(m_max, -FLT_MAX);
-  }
-
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_h = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-  if (!hvalid) return;
-  // lane (head l % 16) holds value columns 16 n + 4 g .. +4 of its head
-  uint16_t* orow = nsplit == 1
-                       ? reinterpret_cast<uint16_t*>(out) + (t * H + head) * int64_t(kDv)
-                       : part_o + ((t * nsplit + blockIdx.z) * H + head) * int64_t(kDv);
-#pragma unroll
-  for (int n = 0; n < kVTiles8; ++n) {
-    const bf16x2_t a = {__bf16(o[n][0] * inv), __bf16(o[n][1] * inv)};
-    const bf16x2_t b = {__bf16(o[n][2] * inv), __bf16(o[n][3] * inv)};
-    *reinterpret_cast<uint2*>(orow + 16 * n + 4 * g) =
-        make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
-  }
-  if (g == 0) {
-    if (nsplit == 1) {
-      if (lse) lse[t * H + head] = lse_h;
-    } else {
-      part_lse[(t * nsplit + blockIdx.z) * H + head] = lse_h;
-    }
-  }
-}
-
 // Number of key splits per query for the bf16 kernel (shared by the launcher
 // and the workspace query).
 int mla_splits(int64_t n_q, int32_t n_heads, int32_t K) {
@@ -1221,9 +1077,8 @@ hipError_t launch_sparse_mla(const void* q, const void* kv, const int32_t* idx, 
   uint16_t* part_o = static_cast<uint16_t*>(workspace);
   float* part_lse =
       s > 1 ? reinterpret_cast<float*>(part_o + size_t(n_q) * s * n_heads * d_v) : nullptr;
-  static_assert(kHeadsPerBlock8 == kHeadsPerBlock, "one head-block count for both kernels");
   if (dtype == 2)
-    hipLaunchKernelGGL(mla_fp8kv_kernel, dim3(unsigned(n_q), hb, s), dim3(kThreads8), 0, stream,
+    hipLaunchKernelGGL(mla_fp8_kernel, dim3(unsigned(n_q), hb, s), dim3(kThreads), 0, stream,
                        static_cast<const __bf16*>(q), static_cast<const uint8_t*>(kv), idx,
                        int(n_kv), n_heads, K, sm_scale, static_cast<__bf16*>(out), lse, part_o,
                        part_lse, s);

@@ -121,7 +121,7 @@ def scan(lines):
 
 
 @pytest.fixture(scope="module")
-def kernel_asm(tmp_path_factory):
+def mla_asm(tmp_path_factory):
     try:
         cc = _build.hipcc()
     except RuntimeError:
@@ -131,8 +131,13 @@ def kernel_asm(tmp_path_factory):
            "-o", str(out)]
     p = subprocess.run(cmd, capture_output=True, text=True)
     assert p.returncode == 0, p.stderr
-    text = out.read_text()
-    start = next(m.start() for m in re.finditer(r"^(\S*" + KERNEL + r"\S*):", text, re.M))
+    return out.read_text()
+
+
+@pytest.fixture(scope="module", params=[KERNEL, "mla_fp8_kernel"])
+def kernel_asm(mla_asm, request):
+    text, kernel = mla_asm, request.param
+    start = next(m.start() for m in re.finditer(r"^(\S*" + kernel + r"\S*):", text, re.M))
     end = text.index(".Lfunc_end", start)
     body = []
     for raw in text[start:end].splitlines()[1:]:
@@ -141,7 +146,7 @@ def kernel_asm(tmp_path_factory):
             continue
         body.append(ln)
     meta = text[text.index(".name:           " + next(
-        n for n in re.findall(r"\.name:\s+(\S+)", text) if KERNEL in n)):]
+        n for n in re.findall(r"\.name:\s+(\S+)", text) if kernel in n)):]
     return body, meta
 
 
