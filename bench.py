@@ -66,19 +66,37 @@ def traffic_from_profile(kernel: str):
     return k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(host_inputs, seconds: float = 20.0):
-    """Oracle (float64 numpy) over a stratified row sample of the same workload
-    (the same seeded inputs the GPU run uses): indexer scores of each sampled
-    row, its top-k, and sparse attention over the selection.  Rate in the unit
-    of ``value``: indexer pairs per second of oracle time."""
+def blas_threads() -> int:
+    """Threads of the BLAS numpy calls into (the oracle's matrix products)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                   or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(host_inputs, seconds: float = 12.0, threads: int | None = None):
+    """Oracle (float64 numpy) over a row sample of the same workload (the same
+    seeded inputs the GPU run uses): indexer scores of each sampled row, its
+    top-k, and sparse attention over the selection.  Rate in the unit of
+    ``value``: indexer pairs per second of oracle time.  threads: BLAS thread
+    limit (None = the library default, all cores)."""
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=threads, user_api="blas") if threads else contextlib.nullcontext()
+    except Exception:
+        ctx = contextlib.nullcontext()
+    with ctx:
+        return _cpu_baseline(host_inputs, seconds)
+
+
+def _cpu_baseline(host_inputs, seconds):
     import numpy as np
     import synth
     from oracle import indexer as o_idx, mla as o_mla, prep as o_prep, topk as o_topk, windows as o_win
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores = blas_threads()
     w = synth.WORKLOADS["prefill4k"]
     lay = synth.layout(w)
     rows = host_inputs["rows"]
@@ -107,9 +125,83 @@ def cpu_baseline(host_inputs, seconds: float = 20.0):
             break
     dt = time.perf_counter() - t0
     return {"value": pairs / dt, "unit": "indexer pairs/s", "cores": int(cores), "kind": "oracle",
+            "blas_threads": int(cores),
             "sample": f"{done} of {lay.n_q} query rows in a seeded random order (stopped after "
                       f"{seconds:.0f} s or all rows), each through indexer scores, top-k and sparse "
                       f"MLA in float64: {pairs} indexer pairs in {dt:.1f} s"}
+
+
+def stage_cpu_baseline(w, lay, inp, fp8_kv: bool, seconds: float = 10.0, wall_s: float = 60.0):
+    """Oracle (float64) on a seeded random sample of the workload's query rows:
+    per row, query prep, indexer scores over its window, top-k and sparse MLA
+    over the selection.  Key prep (and the fp8 latent quantisation) is done once
+    per key in the pipeline, so it runs outside the timed part (each key once,
+    cached in chunks), as do the device-to-host copies of the row's operands.
+    Stops after ``seconds`` of oracle time or ``wall_s`` in all.  Rate: indexer
+    pairs per second of oracle time; ``full_workload_s`` extrapolates it by
+    pair count."""
+    import numpy as np
+    import torch
+    from oracle import indexer as o_idx, mla as o_mla, prep as o_prep, topk as o_topk, windows as o_win
+    rs, re = o_win.row_windows(lay.cu_q, lay.cu_k)
+    pos_q, pos_k = lay.positions(), lay.key_positions()
+    H, D, C = w.n_heads, w.head_dim, 4096
+    chunks = {}
+
+    def keys(a, b):
+        """prepared keys [a, b) (codes / values and scales), prepared once per chunk"""
+        for c in range(a // C, (b - 1) // C + 1):
+            if c not in chunks:
+                lo, hi = c * C, min(c * C + C, lay.n_k)
+                pk = o_prep.prepare_indexer_inputs(
+                    np.zeros((1, H, D)), inp["k_raw"][lo:hi].double().cpu().numpy(),
+                    np.zeros((1, H)), np.zeros(1), pos_k[lo:hi], w.dtype, w.rope_dim,
+                    w.rope_main_dim, w.rope_theta)
+                chunks[c] = (pk["k"], pk["k_scale"])
+        ks = [chunks[c] for c in range(a // C, (b - 1) // C + 1)]
+        k = np.concatenate([x[0] for x in ks])[a - (a // C) * C:][:b - a]
+        sc = None if ks[0][1] is None else np.concatenate([x[1] for x in ks])[a - (a // C) * C:][:b - a]
+        return k, sc
+
+    order = np.random.default_rng(7).permutation(lay.n_q)
+    t_or, pairs, done = 0.0, 0, 0
+    wall0 = time.perf_counter()
+    for t in order:
+        t = int(t)
+        a, b = int(rs[t]), int(re[t])
+        if b <= a:
+            continue
+        q_raw = inp["q_raw"][t:t + 1].double().cpu().numpy()
+        wt = inp["w"][t:t + 1].double().cpu().numpy()
+        k, k_scale = keys(a, b)
+        t0 = time.perf_counter()
+        pq = o_prep.prepare_indexer_inputs(q_raw, k[:1], wt, np.array([pos_q[t]]), np.zeros(1),
+                                           w.dtype, w.rope_dim, w.rope_main_dim, w.rope_theta)
+        sc = o_idx.score_row(pq["q"][0], k, pq["w"][0], k_scale)
+        full = np.full(lay.n_k, -np.inf, np.float32)
+        full[a:b] = sc
+        idx = o_topk.topk_row(full, a, b, w.index_topk)
+        t_or += time.perf_counter() - t0
+        sel = idx[idx >= 0]
+        kv = o_prep.round_bf16(inp["mla_kv"][torch.from_numpy(sel).to(inp["mla_kv"].device)]
+                               .double().cpu().numpy())
+        if fp8_kv:
+            kv = o_prep.dequant_mla_kv(*o_prep.mla_kv_quant(kv))
+        mq = o_prep.round_bf16(inp["mla_q"][t].double().cpu().numpy())
+        t0 = time.perf_counter()
+        o_mla.attend_row(mq, kv, np.arange(sel.size), w.sm_scale, w.d_v)
+        t_or += time.perf_counter() - t0
+        pairs += b - a
+        done += 1
+        if t_or > seconds or time.perf_counter() - wall0 > wall_s:
+            break
+    total = int(np.maximum(np.asarray(re, np.int64) - np.asarray(rs, np.int64), 0).sum())
+    rate = pairs / t_or
+    return {"value": rate, "unit": "indexer pairs/s", "cores": blas_threads(), "kind": "oracle",
+            "blas_threads": blas_threads(), "full_workload_s": total / rate,
+            "sample": f"{done} of {lay.n_q} query rows in a seeded random order, each through query "
+                      f"prep, indexer scores, top-k and sparse MLA in float64 ({pairs} of {total} "
+                      f"indexer pairs, {t_or:.1f} s of oracle time)"}
 
 
 def stage_bench(args, dsa, synth, np, torch):
@@ -153,6 +245,7 @@ def stage_bench(args, dsa, synth, np, torch):
                                             w.rope_dim, w.rope_main_dim, w.rope_theta)
     mq = inp["mla_q"].to(torch.bfloat16)
     mkv = inp["mla_kv"].to(torch.bfloat16)
+    cpu_inp = None if args.no_cpu else {n: inp[n] for n in ("q_raw", "k_raw", "w", "mla_q", "mla_kv")}
     del inp
     mla_insert_ms, mcache = None, None
     if fp8_cache:
@@ -307,7 +400,10 @@ def stage_bench(args, dsa, synth, np, torch):
         roof = {"kernel": "topk_rows_kernel", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
     total = sum(ms_path.values())
-    return {
+    extra = {}
+    if cpu_inp is not None:
+        extra["cpu_baseline"] = stage_cpu_baseline(w, lay, cpu_inp, mcache is not None)
+    res = {
         "metric": "indexer q·k pairs/s + top-k rows/s + sparse-MLA TFLOP/s (per stage)",
         "value": pairs / (total * 1e-3), "unit": "indexer pairs/s (sum of the stage medians)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": total,
@@ -321,6 +417,8 @@ def stage_bench(args, dsa, synth, np, torch):
                    "parallelism": "none (1 GPU)"},
         "components": comp, "roofline": roof,
     }
+    res.update(extra)
+    return res
 
 
 def main():
@@ -387,7 +485,7 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    stage_ms = {"indexer": [], "topk": [], "mla": []}
+    stage_ms = {"indexer": [], "topk": [], "mla": [], "step": []}
 
     def step(record: bool):
         e = [ev() for _ in range(4)]
@@ -411,11 +509,16 @@ def main():
         stage_ms["indexer"].append(e[0].elapsed_time(e[1]))
         stage_ms["topk"].append(e[1].elapsed_time(e[2]))
         stage_ms["mla"].append(e[2].elapsed_time(e[3]))
+        stage_ms["step"].append(e[0].elapsed_time(e[3]))
     ms_step = wall * 1e3 / args.steps
+    step_ev = stage_ms.pop("step")
 
     pairs = lay.n_q * (lay.n_q + 1) // 2                               # valid (t, s), s <= t
     mla_pairs = sum(min(t + 1, K) for t in range(lay.n_q))            # selected (t, j)
     avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
+    pct = lambda v, q: round(float(np.percentile(v, q)), 4)
+    stats = {s: {"mean": round(float(np.mean(v)), 4), "p10": pct(v, 10), "median": pct(v, 50),
+                 "p90": pct(v, 90)} for s, v in list(stage_ms.items()) + [("step", step_ev)]}
     idx_flop = pairs * 2 * w.n_heads * w.head_dim
     mla_flop = mla_pairs * MLA_FLOP_PER_PAIR
     topk_bytes = pairs * 4 + lay.n_q * K * 4                          # valid scores read + idx written
@@ -426,6 +529,8 @@ def main():
         "topk_gbs": topk_bytes / (avg["topk"] * 1e-3) / 1e9,
         "sparse_mla_tflops": mla_flop / (avg["mla"] * 1e-3) / 1e12,
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
+        # per-launch HIP-event times over the timed steps (ms): mean, p10, median, p90
+        "stage_ms_stats": stats,
     }
     # dominant kernel of the step
     dom = max(avg, key=avg.get)
@@ -451,6 +556,8 @@ def main():
         "unit": "indexer pairs/s (whole step: indexer + top-k + sparse MLA)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_p10_median_p90": [stats["step"]["p10"], stats["step"]["median"],
+                                        stats["step"]["p90"]],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "prefill4k: one causal sequence T=4096, bf16; indexer 64 heads x 128 "
@@ -461,7 +568,9 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu:
+        # all cores (the BLAS default), then one BLAS thread on the same sample order
         line["cpu_baseline"] = cpu_baseline(host_inputs)
+        line["cpu_baseline"]["one_core"] = cpu_baseline(host_inputs, threads=1)
     print(json.dumps(line), flush=True)
 
 
