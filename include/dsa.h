@@ -23,6 +23,11 @@
  *   - Every call returns DSA_OK (0) or a negative dsa_status.  Arguments are
  *     validated on the host before anything is enqueued; on error nothing is
  *     enqueued and no output is touched.
+ *   - Size limits of every entry point: row and key counts <= INT32_MAX,
+ *     1 <= index_topk <= 65536 (sparse MLA also n_heads <= 65536).  A
+ *     workspace-size query returns 0 for an empty problem and SIZE_MAX for sizes
+ *     beyond these limits (or whose workspace does not fit in size_t), which no
+ *     workspace satisfies; the call itself rejects such sizes.
  *   - Device-side values are never trusted for addressing: every kernel clamps
  *     a window to [0, n_k] (a window that ends before it starts is empty), and
  *     the attention skips an index outside [0, n_kv) exactly like -1.  A NaN

@@ -9,6 +9,8 @@
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
+constexpr int32_t kMaxK = 65536;          // index_topk limit of every entry point
+constexpr int32_t kMaxMlaHeads = 65536;   // sparse MLA heads
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -51,7 +53,7 @@ int check_topk(const float* scores, int64_t ld, const int32_t* rs, const int32_t
   if (K < 1) return DSA_ERR_INVALID_ARG;
   if (ld < n_cols) return DSA_ERR_INVALID_ARG;
   if (n_q > 0 && (!scores || !rs || !re || !out)) return DSA_ERR_INVALID_ARG;
-  if (K > 65536) return DSA_ERR_UNSUPPORTED;
+  if (K > kMaxK) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
@@ -166,6 +168,7 @@ int dsa_indexer_scores(const void* q, const void* k, const float* k_scale, const
 
 size_t dsa_topk_workspace_size(int64_t n_q, int64_t n_cols, int32_t index_topk) {
   if (n_q <= 0 || n_cols < 0 || index_topk < 1) return 0;
+  if (n_q > INT32_MAX || n_cols > INT32_MAX || index_topk > kMaxK) return SIZE_MAX;
   return dsa::topk_workspace_bytes(n_q, n_cols, index_topk);
 }
 
@@ -186,12 +189,20 @@ size_t dsa_indexer_topk_workspace_size(int64_t n_q, int64_t n_k, int32_t n_heads
   (void)n_heads;
   (void)head_dim;
   if (n_q <= 0 || n_k <= 0 || index_topk < 1) return 0;
+  if (n_q > INT32_MAX || n_k > INT32_MAX || index_topk > kMaxK) return SIZE_MAX;
   if (fused_rows(n_q, dtype, index_topk)) return 0;
   if (dsa::indexer_topk_fused(n_q, dtype, index_topk))
     return n_k > 8192 ? dsa::indexer_topk_fused_workspace_bytes(n_q, index_topk) : 0;
-  // the score matrix, then the top-k's own workspace (256-byte aligned)
-  const size_t scores = (size_t(n_q) * size_t(n_k) * sizeof(float) + 255) & ~size_t(255);
-  return scores + dsa::topk_workspace_bytes(n_q, n_k, index_topk);
+  // the score matrix, then the top-k's own workspace (256-byte aligned); at the
+  // largest sizes the sum no longer fits in size_t
+  size_t scores = 0, total = 0;
+  if (__builtin_mul_overflow(size_t(n_q) * sizeof(float), size_t(n_k), &scores) ||
+      __builtin_add_overflow(scores, size_t(255), &scores))
+    return SIZE_MAX;
+  scores &= ~size_t(255);
+  if (__builtin_add_overflow(scores, dsa::topk_workspace_bytes(n_q, n_k, index_topk), &total))
+    return SIZE_MAX;
+  return total;
 }
 
 int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const float* w,
@@ -203,7 +214,7 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const f
                          dtype);
   if (st != DSA_OK) return st;
   if (index_topk < 1 || (n_q > 0 && !topk_idx)) return DSA_ERR_INVALID_ARG;
-  if (index_topk > 65536) return DSA_ERR_UNSUPPORTED;
+  if (index_topk > kMaxK) return DSA_ERR_UNSUPPORTED;
   const size_t need =
       dsa_indexer_topk_workspace_size(n_q, n_k, n_heads, head_dim, dtype, index_topk);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
@@ -231,6 +242,7 @@ int dsa_indexer_topk(const void* q, const void* k, const float* k_scale, const f
 size_t dsa_sparse_mla_workspace_size(int64_t n_q, int32_t n_heads, int32_t d_qk, int32_t d_v,
                                      int32_t index_topk, int32_t dtype) {
   if (n_q <= 0 || n_heads < 1 || index_topk < 1) return 0;
+  if (n_q > INT32_MAX || n_heads > kMaxMlaHeads || index_topk > kMaxK) return SIZE_MAX;
   return dsa::mla_workspace_bytes(n_q, n_heads, d_qk, d_v, index_topk, dtype);
 }
 
@@ -241,6 +253,7 @@ int dsa_sparse_mla_fwd(const void* q, const void* kv, const int32_t* topk_idx, i
   if (n_q < 0 || n_kv < 0 || n_q > INT32_MAX || n_kv > INT32_MAX) return DSA_ERR_INVALID_ARG;
   if (n_heads < 1 || d_qk < 1 || d_v < 1 || d_v > d_qk || index_topk < 1)
     return DSA_ERR_INVALID_ARG;
+  if (n_heads > kMaxMlaHeads || index_topk > kMaxK) return DSA_ERR_UNSUPPORTED;
   if (dtype != DSA_DTYPE_F32 && dtype != DSA_DTYPE_BF16 && dtype != DSA_DTYPE_FP8_E4M3)
     return DSA_ERR_INVALID_ARG;
   if (n_q > 0 && (!q || !topk_idx || !out)) return DSA_ERR_INVALID_ARG;
