@@ -113,8 +113,14 @@ def test_fp8_latent_cache_rows():
     big = np.abs(codes) >= 2 ** -6
     rel = np.abs(deq[:, :512] - kv[:, :512])[big] / np.abs(kv[:, :512])[big]
     assert rel.max() <= 2 ** -4
-    q = g.standard_normal((4, 576))
-    idx = np.array([3, 17, -1, 8, 39])
-    o1, l1 = mla.attend_row(q, deq, idx, 576 ** -0.5, 512)
-    o2, l2 = mla.attend_row(q, np.asarray(deq), idx, 576 ** -0.5, 512)
-    np.testing.assert_array_equal(o1, o2)
+    # rows already on the grid come back exactly: e4m3 codes whose block maximum
+    # is 448 (which fixes the scale) times a power of two per block
+    codes0 = prep.round_e4m3(g.standard_normal((6, 4, 128)) * 100.0)
+    codes0[:, :, 0] = 448.0 * np.sign(g.standard_normal((6, 4)) + 0.5)
+    e = g.integers(-12, 3, (6, 4)).astype(np.float64)
+    lat = (codes0 * np.exp2(e)[..., None]).reshape(6, 512)
+    rope0 = prep.round_bf16(g.standard_normal((6, 64)))
+    c2, s2, r2 = prep.mla_kv_quant(np.concatenate([lat, rope0], axis=1))
+    np.testing.assert_array_equal(c2, codes0.reshape(6, 512))
+    np.testing.assert_array_equal(s2, np.exp2(e))
+    np.testing.assert_array_equal(prep.dequant_mla_kv(c2, s2, r2)[:, :512], lat)
