@@ -747,15 +747,9 @@ __device__ __forceinline__ void mla_body(
     for (int w = 1; w < kWaves; ++w) last = max(last, sh.wlast[w]);
     i1 = last < 0 ? i0 : i0 + last / kKT + 1;
   }
+  // tiles 1 .. nt-1 run in groups of four (fp8: three: the tile buffers of each
+  // step are static); steps past the last tile are skipped, no tile is padded
   const int nt = i1 - i0;
-  // tiles are run in groups of four (fp8: three) after tile 0: pad with masked
-  // tiles that gather row 0 (finite values: a masked key's P is 0, and 0 * V
-  // must stay 0)
-  const int nt4 = nt <= 0 ? 0 : kF8 ? 1 + 3 * ((nt + 1) / 3) : 1 + 4 * ((nt + 2) / 4);
-  for (int x = nt * kKT + tid; x < nt4 * kKT; x += kThreads) {
-    sh.idx[x] = 0;
-    if ((x & (kKT - 1)) == 0) sh.vmask[x / kKT] = 0u;
-  }
   if (tid < 2) sh.redo[tid] = 0;
   __syncthreads();
   // Q^T has landed before the first gather is issued.  (The gathers are inline
@@ -774,18 +768,18 @@ __device__ __forceinline__ void mla_body(
     bool over = false;
     bf16x8_t p0 = bf16x8_t{}, p1 = bf16x8_t{};
     if constexpr (kF8) {
-      if (nt4 > 0) dma_tile8(g_st8a, sh.idx, 0, kvb, wave, lane);
-      if (nt4 > 1) dma_tile8(g_st8b, sh.idx, 1, kvb, wave, lane);
-      if (nt4 > 0) {
+      if (nt > 0) dma_tile8(g_st8a, sh.idx, 0, kvb, wave, lane);
+      if (nt > 1) dma_tile8(g_st8b, sh.idx, 1, kvb, wave, lane);
+      if (nt > 0) {
         // tile 0: converted, then S and softmax only
-        wait_stage8(nt4 > 1);
+        wait_stage8(nt > 1);
         dequant_stage8<0>(g_st8a, wave, lane);
         wait_lgkm<0>();
         __builtin_amdgcn_s_barrier();
         {
           Softmax sm;
           bf16x8_t fr[4];
-          if (nt4 > 2)
+          if (nt > 2)
             sm.s = qk_tile<0, 0, true, -1, true>(fr, qf, sh.vmask[0], lane, sh.idx, 2, kvb, wave,
                                                  g_st8a);
           else
@@ -794,33 +788,35 @@ __device__ __forceinline__ void mla_body(
           p0 = sm.p0();
           p1 = sm.p1();
         }
-        if (nt4 > 1) {
-          wait_stage8(nt4 > 2);
+        if (nt > 1) {
+          wait_stage8(nt > 2);
           dequant_stage8<1>(g_st8b, wave, lane);
         }
         uint32_t vm = sh.vmask[1];
-        for (int i = 1; i < nt4; i += 3) {
-          tile_step8<1>(sh, i, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
+        for (int i = 1; i < nt; i += 3) {
+          tile_step8<1>(sh, i, nt, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
                         wave, lane);
-          tile_step8<2>(sh, i + 1, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
-                        wave, lane);
-          tile_step8<0>(sh, i + 2, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
-                        wave, lane);
+          if (i + 1 < nt)
+            tile_step8<2>(sh, i + 1, nt, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run,
+                          scale2, wave, lane);
+          if (i + 2 < nt)
+            tile_step8<0>(sh, i + 2, nt, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run,
+                          scale2, wave, lane);
         }
-        const int lb = (nt4 - 1) % 3;
+        const int lb = (nt - 1) % 3;
         const uint8_t* buf = lb == 0 ? g_kv0 : lb == 1 ? g_kv1 : g_kv2;
         Softmax none;
         bf16x8_t fr[4];
         pv_tile<-1, false, true>(fr, buf, p0, p1, o, lane, none, scale2, m_ref, m_max, over, l_run);
       }
     } else {
-      if (nt4 > 0) dma_tile<0>(sh.idx, 0, kvb, wave, lane);
-      if (nt4 > 1) dma_tile<1>(sh.idx, 1, kvb, wave, lane);
-      if (nt4 > 0) {
+      if (nt > 0) dma_tile<0>(sh.idx, 0, kvb, wave, lane);
+      if (nt > 1) dma_tile<1>(sh.idx, 1, kvb, wave, lane);
+      if (nt > 0) {
         // tile 0: no P.V yet
-        wait_tile(nt4 > 1);
+        wait_tile(nt > 1);
         __builtin_amdgcn_s_barrier();
-        if (nt4 > 2) dma_tile<2>(sh.idx, 2, kvb, wave, lane);
+        if (nt > 2) dma_tile<2>(sh.idx, 2, kvb, wave, lane);
         {
           Softmax sm;
           bf16x8_t fr[4];
@@ -830,20 +826,24 @@ __device__ __forceinline__ void mla_body(
           p1 = sm.p1();
         }
         uint32_t vm = sh.vmask[1];
-        // tiles 1 .. nt4-1 in groups of four (one exit: a loop left in the middle
-        // makes the register allocator copy O out of the accumulation registers)
-        for (int i = 1; i < nt4; i += 4) {
-          tile_step<1>(sh, i, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave, lane);
-          tile_step<2>(sh, i + 1, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
-                       lane);
-          tile_step<3>(sh, i + 2, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
-                       lane);
-          tile_step<0>(sh, i + 3, nt4, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave,
-                       lane);
+        // tiles 1 .. nt-1 in groups of four, the steps past nt skipped (one exit:
+        // a loop left in the middle makes the register allocator copy O out of
+        // the accumulation registers)
+        for (int i = 1; i < nt; i += 4) {
+          tile_step<1>(sh, i, nt, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2, wave, lane);
+          if (i + 1 < nt)
+            tile_step<2>(sh, i + 1, nt, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
+                         wave, lane);
+          if (i + 2 < nt)
+            tile_step<3>(sh, i + 2, nt, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
+                         wave, lane);
+          if (i + 3 < nt)
+            tile_step<0>(sh, i + 3, nt, kvb, qf, o, p0, p1, vm, m_ref, m_max, over, l_run, scale2,
+                         wave, lane);
         }
         // P.V of the last tile: no gather is in flight any more, so its buffer can
         // be chosen at run time
-        const int lb = (nt4 - 1) & 3;
+        const int lb = (nt - 1) & 3;
         const uint8_t* buf = lb == 0 ? g_kv0 : lb == 1 ? g_kv1 : lb == 2 ? g_kv2 : g_kv3;
         Softmax none;
         bf16x8_t fr[4];
