@@ -43,6 +43,10 @@
 // Split mode writes per-split partials to the workspace -- the normalised output
 // in bf16, the lse in fp32 -- and a combine kernel merges them with the
 // log-sum-exp weights.
+//
+// fp8 kernel (the same body over 656-byte fp8 latent rows): each wave gathers
+// its 8 rows of a tile into its own staging rows and converts them to the bf16
+// tile layout one step ahead of use (three tile buffers).
 // The fp32 kernel (small head dims) is plain VALU code.
 #include <cfloat>
 #include <cmath>
@@ -105,9 +109,9 @@ __device__ __forceinline__ int acc_row(int r, int half) {
 }
 
 struct MlaShared {
-  int idx[kMaxIdx + 3 * kKT];     // this workgroup's slice of the top-k row (-1 -> row 0),
-                                  // plus up to 3 padding tiles
-  uint32_t vmask[kMaxTiles + 3];  // per tile: bit j set = selected key j is valid
+  int idx[kMaxIdx];               // this workgroup's slice of the top-k row (-1 -> row 0)
+  uint32_t vmask[kMaxTiles + 1];  // per tile: bit j set = selected key j is valid (one
+                                  // past the last: read ahead, never used)
   int wlast[kWaves];              // per wave: last valid position of its index loads, or -1
   int redo[2];                    // per pass: some head needs the second pass
 };

@@ -626,6 +626,30 @@ def test_mla_fp8_wide_value_range(dsa):
     _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, "wide value range")
 
 
+def _tile_count_rows(g, n_q, n_kv, K):
+    """Rows with 1 .. 9 tiles of selected keys (partial last tiles too), -1 after."""
+    idx = np.full((n_q, K), -1, np.int32)
+    for t in range(n_q):
+        n = min(K, 32 * (t % 9 + 1) - (t % 3) * 7)
+        idx[t, :n] = np.sort(g.choice(n_kv, size=n, replace=False))
+    return idx
+
+
+@pytest.mark.parametrize("n_q", [8, 200])
+def test_mla_tile_counts(dsa, n_q):
+    # every remainder of the tile loop's groups (four tiles for bf16 rows, three
+    # for fp8 rows) on the one-workgroup-per-query launch and on split slices
+    g = np.random.default_rng(219)
+    n_kv = 2000
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q))
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    idx = _tile_count_rows(g, n_q, n_kv, 512)
+    rows = list(range(n_q)) if n_q < 50 else list(range(0, 27)) + list(range(100, 127))
+    _mla_case(dsa, q, o_prep.round_bf16(kv), idx, P4K.sm_scale, P4K.d_v, True,
+              f"tile counts bf16 n_q={n_q}", rows=rows)
+    _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, f"tile counts n_q={n_q}", rows=rows)
+
+
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 def test_mla_kv_insert_bytes(dsa, src):
     # every written byte equals the oracle's quantisation; other slots untouched
