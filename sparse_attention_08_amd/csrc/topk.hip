@@ -109,7 +109,9 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
     int skip_long, int skip_below) {
   __shared__ uint32_t keys[CAP];
   __shared__ SelectShared<kThreads> sh;
-  const int64_t row = blockIdx.x;
+  // last rows first: in a causal prefill they hold the longest windows, and
+  // starting them first leaves the short ones for the end of the launch
+  const int64_t row = int64_t(gridDim.x) - 1 - blockIdx.x;
   const int a = max(row_starts[row], 0);  // windows are clamped to the columns [0, n_cols)
   const int b = min(row_ends[row], n_cols);
   const int n = b > a ? b - a : 0;
