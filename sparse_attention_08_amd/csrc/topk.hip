@@ -271,23 +271,27 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
 // search) finds the digit that holds their k-th key, every key below that digit
 // goes, and when that leaves room for a piece the held keys above the floor are
 // compacted in place; otherwise (a crowded digit: many equal keys) they are
-// shrunk in place to their exact top k.  The scores are read once.  47 KB of
-// LDS: three workgroups per CU.
+// shrunk in place to their exact top k.  The scores are read once.  The held
+// keys carry their offsets in the window: 16-bit for windows of at most 65536
+// keys (38.8 KB of LDS, at most 128 VGPRs: four workgroups per CU, which the
+// per-piece barriers need more than anything else), else 32-bit (47.2 KB: three).
 constexpr int kPiece = 2048;
 constexpr int kSlack = 128;  // held keys past k that the histogram shrink may keep
 constexpr int kHeldCap = kMaxSplitK + kPiece + kSlack;
 
+template <typename ColT>
 struct StreamShared {
   uint32_t keys[kHeldCap];
-  int32_t cols[kHeldCap];
+  ColT cols[kHeldCap];  // offset of each held key in the row's window
   uint32_t wcnt[2 * kWaves];
   SelectShared<kThreads> sel;
 };
 
-__global__ __launch_bounds__(kThreads) void topk_stream_kernel(
+template <typename ColT>
+__global__ __launch_bounds__(kThreads, sizeof(ColT) == 2 ? 4 : 1) void topk_stream_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
     const int32_t* __restrict__ row_ends, int n_cols, int32_t K, int32_t* __restrict__ out) {
-  __shared__ StreamShared sh;
+  __shared__ StreamShared<ColT> sh;
   constexpr int kPer = kPiece / kThreads;  // keys per thread per piece
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -322,13 +326,13 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
     int s_lo, s_hi;
     select_segment<kThreads>(cnt, s_lo, s_hi);
     uint32_t hk[kHeldPer];
-    int32_t hc[kHeldPer];
+    ColT hc[kHeldPer];
     uint32_t gt = 0u, eq = 0u;
 #pragma unroll
     for (int j = 0; j < kHeldPer; ++j) {
       const int i = s_lo + j * kWave + lane;
       hk[j] = i < s_hi ? sh.keys[i] : 0u;
-      hc[j] = i < s_hi ? sh.cols[i] : 0;
+      hc[j] = i < s_hi ? sh.cols[i] : ColT(0);
     }
 #pragma unroll
     for (int j = 0; j < kHeldPer; ++j) {
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
       if (keep) {
         const int at = base + __popcll(bal & lt);
         sh.keys[at] = v[j];
-        sh.cols[at] = a + lo + wave * (kPiece / kWaves) + j * kWave + lane;
+        sh.cols[at] = ColT(lo + wave * (kPiece / kWaves) + j * kWave + lane);
       }
       base += __popcll(bal);
     }
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
     __syncthreads();
     if (lo + m >= n) {
       select_topk<kThreads>(LdsKeys{sh.keys}, ncand, uint32_t(ncand), K, sh.sel,
-                            [&](uint32_t p, int i, uint32_t) { dst[p] = sh.cols[i]; });
+                            [&](uint32_t p, int i, uint32_t) { dst[p] = a + int(sh.cols[i]); });
       for (int p = (ncand < K ? ncand : K) + tid; p < K; p += kThreads) dst[p] = -1;
       return;
     }
@@ -468,8 +472,13 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_start
       e = hipGetLastError();
     }
     if (e != hipSuccess || !stream_long) return e;
-    hipLaunchKernelGGL(topk_stream_kernel, dim3(unsigned(n_q)), dim3(kThreads), 0, stream, scores,
-                       ld, row_starts, row_ends, int(n_cols), K, out);
+    // windows are clamped to the columns, so n_cols bounds every offset
+    if (n_cols <= 65536)
+      hipLaunchKernelGGL(topk_stream_kernel<uint16_t>, dim3(unsigned(n_q)), dim3(kThreads), 0,
+                         stream, scores, ld, row_starts, row_ends, int(n_cols), K, out);
+    else
+      hipLaunchKernelGGL(topk_stream_kernel<uint32_t>, dim3(unsigned(n_q)), dim3(kThreads), 0,
+                         stream, scores, ld, row_starts, row_ends, int(n_cols), K, out);
     return hipGetLastError();
   }
   const Candidates cd = Candidates::at(workspace, n_q, K);

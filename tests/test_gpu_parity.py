@@ -231,6 +231,22 @@ def test_topk_many_long_rows_stream_shrinks(dsa):
         _topk_case(dsa, S, rs, re, K, f"stream shrinks K={K}")
 
 
+def test_topk_stream_path_wide_offsets(dsa):
+    # more than 65536 columns: the stream kernel holds 32-bit window offsets (16-bit
+    # ones up to 65536); windows start past 0 and run past offset 65535
+    g = np.random.default_rng(109)
+    n_q, n = 1030, 70000
+    S = g.standard_normal((n_q, n)).astype(np.float32)
+    S[::3] = np.round(S[::3] * 4) / 4                       # crowded digits: many equal keys
+    S[1::7, 60000:] += 2.0                                  # the top keys late in the window
+    rs = g.integers(0, 3000, n_q).astype(np.int32)
+    re = np.minimum(n, rs + g.integers(9000, 70000, n_q)).astype(np.int32)
+    re[:4] = [n, n, 66000, 65537]
+    rs[:4] = [0, 1, 0, 0]
+    assert dsa._lib_or_load().dsa_topk_workspace_size(n_q, n, 2048) == 0
+    _topk_case(dsa, S, rs, re, 2048, "stream, offsets past 65535")
+
+
 def test_topk_many_rows_large_k_global_path(dsa):
     # k above 2048 over long windows: one workgroup per row re-reads from memory
     g = np.random.default_rng(106)
