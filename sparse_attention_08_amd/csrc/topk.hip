@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads, sizeof(ColT) == 2 ? 4 : 1) void topk_stre
     const int32_t* __restrict__ row_ends, int n_cols, int32_t K, int32_t* __restrict__ out) {
   __shared__ StreamShared<ColT> sh;
   constexpr int kPer = kPiece / kThreads;  // keys per thread per piece
-  const int64_t row = blockIdx.x;
+  const int64_t row = int64_t(gridDim.x) - 1 - blockIdx.x;  // last (causal: longest) rows first
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
