@@ -371,8 +371,7 @@ __global__ __launch_bounds__(256) void mla_kv_insert_kernel(const void* __restri
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = int64_t(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
   if (row >= n_tok) return;  // whole waves: the xor reductions stay inside one row
-  const int64_t slot = slots[row];
-  if (slot < 0 || slot >= n_slots) return;
+  const int64_t slot = slots[row];  // checked after the row's loads are issued: no serial round trip
   float x[8], r[4];
   if constexpr (kBf16In) {
     const uint16_t* src = static_cast<const uint16_t*>(kv) + row * D;
@@ -383,19 +382,21 @@ __global__ __launch_bounds__(256) void mla_kv_insert_kernel(const void* __restri
       x[2 * j] = bf16_bits_to_f32(uint16_t(w4[j] & 0xFFFFu));
       x[2 * j + 1] = bf16_bits_to_f32(uint16_t(w4[j] >> 16));
     }
-    if (lane < 16) {
-      // bf16 rope values are copied as they are
-      const uint2 rp = *reinterpret_cast<const uint2*>(src + kMlaLatent + 4 * lane);
-      *reinterpret_cast<uint2*>(cache + slot * kMlaRow8 + kMlaLatent + 16 + 8 * lane) = rp;
-    }
+    uint2 rp = make_uint2(0u, 0u);
+    if (lane < 16) rp = *reinterpret_cast<const uint2*>(src + kMlaLatent + 4 * lane);
+    if (slot < 0 || slot >= n_slots) return;
+    // bf16 rope values are copied as they are
+    if (lane < 16) *reinterpret_cast<uint2*>(cache + slot * kMlaRow8 + kMlaLatent + 16 + 8 * lane) = rp;
   } else {
     const float* src = static_cast<const float*>(kv) + row * D;
     const float4 a = *reinterpret_cast<const float4*>(src + 8 * lane);
     const float4 b = *reinterpret_cast<const float4*>(src + 8 * lane + 4);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < 16) c = *reinterpret_cast<const float4*>(src + kMlaLatent + 4 * lane);
+    if (slot < 0 || slot >= n_slots) return;
     if (lane < 16) {
-      const float4 c = *reinterpret_cast<const float4*>(src + kMlaLatent + 4 * lane);
       r[0] = c.x; r[1] = c.y; r[2] = c.z; r[3] = c.w;
       const uint32_t lo = uint32_t(f32_to_bf16_bits(r[0])) | (uint32_t(f32_to_bf16_bits(r[1])) << 16);
       const uint32_t hi = uint32_t(f32_to_bf16_bits(r[2])) | (uint32_t(f32_to_bf16_bits(r[3])) << 16);
