@@ -10,8 +10,9 @@
 // Workgroup (row t, chunk c) of 4 waves:
 //   * windows of 8193 .. 131072 keys are cut into 16 chunks of at most 8192
 //     keys (as on the split path of dsa_topk); the workgroup computes the
-//     scores of its chunk (each wave streams 32-key tiles from global memory,
-//     fragments of the next tile in flight while the current one is on the
+//     scores of its chunk (each wave streams 32-key tiles: bf16 keys through
+//     two private LDS buffers by LDS-DMA, fp8 / fp4 keys straight into
+//     registers, the next tile in flight while the current one is on the
 //     matrix core) straight into LDS as order-preserving keys, selects the
 //     chunk's top-k and writes it as candidates (key, column); the merge kernel
 //     of the split top-k then selects the row's top-k from the candidates;
@@ -35,6 +36,18 @@ using ixcore::OpFp4;
 using ixcore::OpFp8;
 using ixcore::QueryRow;
 
+// Per-wave LDS buffers of the key stream (LDS-DMA, one tile in flight): bf16
+// keys over 33..64 heads only.  There the kernel's registers allow one wave per
+// SIMD anyway, and the DMA stream beats direct fragment loads on 256-byte keys
+// (decode: 0.357 -> 0.325 ms); it loses on the fp8 ones (0.203 -> 0.244 ms),
+// and with up to 32 heads the 64 KB of buffers would halve the workgroups per
+// CU, so those stream into registers.
+template <class Op, int MT>
+struct FusedBufs {
+  static constexpr int kNB = Op::kRowBytes == 256 && MT == 2 ? 2 : 0;
+  static constexpr int kBytes = kNB > 0 ? kNB * ixcore::LdsTile<Op, Op::kKeyScale>::kBytes : 16;
+};
+
 struct FusedShared {
   uint32_t keys[kMaxSplitK + kCap];  // running candidates [0, ncand), then new keys
   int32_t cols[kMaxSplitK];          // columns of the running candidates
@@ -45,13 +58,14 @@ struct FusedShared {
 
 // Scores of keys [s_lo, s_lo + m) of row qr into out[0, m) as order-preserving
 // keys; returns this thread's count of selectable keys.  Each wave streams its
-// 32-key tiles (every 4th) with the next tile's loads in flight.
+// 32-key tiles (every 4th) with the next tile's loads in flight (into tbuf, the
+// wave's LDS buffers, when FusedBufs gives it any).
 template <class Op, int MT, bool kScaled>
 __device__ __forceinline__ uint32_t score_range(const QueryRow<Op, MT>& qr,
                                                 const uint8_t* __restrict__ k,
                                                 const float* __restrict__ k_scale, int s_lo,
                                                 int m, uint32_t* out, int lane, int wave,
-                                                uint32_t& kmin, uint32_t& kmax) {
+                                                uint32_t& kmin, uint32_t& kmax, uint8_t* tbuf) {
   constexpr int NW = kThreads / kWave;
   const int nt = (m + kKeyTile - 1) / kKeyTile;
   const int hi = s_lo + m;
@@ -68,7 +82,12 @@ __device__ __forceinline__ uint32_t score_range(const QueryRow<Op, MT>& qr,
       }
     }
   };
-  ixcore::stream_tiles<Op, MT, kScaled>(qr, k, k_scale, s_lo, hi, wave, NW, nt, lane, put);
+  constexpr int kNB = FusedBufs<Op, MT>::kNB;
+  if constexpr (kNB > 0)
+    ixcore::stream_tiles_lds<Op, MT, kScaled, kNB>(qr, k, k_scale, s_lo, hi, wave, NW, nt, lane,
+                                                   tbuf, put);
+  else
+    ixcore::stream_tiles<Op, MT, kScaled>(qr, k, k_scale, s_lo, hi, wave, NW, nt, lane, put);
   return cnt;
 }
 
@@ -81,6 +100,8 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
     int32_t* __restrict__ cand_col, int32_t* __restrict__ cand_cnt) {
   constexpr bool kScaled = Op::kKeyScale;  // fp8 / fp4 keys carry a scale
   __shared__ FusedShared sh;
+  constexpr int kTBytes = FusedBufs<Op, MT>::kBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[kThreads / kWave][kTBytes];
   const int64_t t = blockIdx.x;
   const int c = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -101,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
     const int m = lo < n ? min(clen, n - lo) : 0;
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     const uint32_t cnt = score_range<Op, MT, kScaled>(qr, k, k_scale, a + lo, m, sh.keys, lane,
-                                                      wave, kmin, kmax);
+                                                      wave, kmin, kmax, tbuf[wave]);
     KeyRange kr;
     const uint32_t n_sel =
         block_count_range<kThreads>(cnt, kmin, kmax, sh.sel, kr);  // also orders the LDS writes
@@ -125,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
     const int m = lo < n ? min(kCap, n - lo) : 0;
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // not used: the running candidates join the keys
     const uint32_t cnt = score_range<Op, MT, kScaled>(qr, k, k_scale, a + lo, m, sh.keys + ncand,
-                                                      lane, wave, kmin, kmax);
+                                                      lane, wave, kmin, kmax, tbuf[wave]);
     const uint32_t n_sel = ncand + block_sum<kThreads>(cnt, sh.sel.tmp);
     const int total = int(ncand) + m;
     const int nc = int(ncand);
