@@ -17,7 +17,7 @@ workload on this host.
 GEMM through torch.matmul and a device copy), so that the kernel's fraction can
 be read against the box as well as against the published peak.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 300] [--warmup 20] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -266,8 +266,10 @@ def stage_cpu_baseline(w, lay, inp, fp8_kv: bool, seconds: float = 10.0, wall_s:
 def stage_bench(args, dsa, synth, np, torch):
     """Each stage of the path timed on its own on one of the other workloads (THD
     varlen prefill, decode, fp8 64K prefill).  HBM-bound stages (all of decode,
-    and every standalone top-k) get a 1 GiB write between repetitions so that
-    their inputs are not served from the 256 MB last-level cache."""
+    and every standalone top-k) get a 1 GiB read between repetitions so that
+    their inputs are not served from the 256 MB last-level cache.  Each stage is
+    repeated at least --steps times and until --min-time seconds have passed;
+    the median is reported, with p10 / p90 in components["stage_ms_stats"]."""
     dev = "cuda"
     fp8_cache = args.workload == "decode_fp8"
     mx = args.workload == "mxfp4_64k"
@@ -353,22 +355,30 @@ def stage_bench(args, dsa, synth, np, torch):
         fns["indexer_topk"] = lambda: dsa.dsa_indexer_topk(q, k, wt, rs, re, K, k_scale=ks, out=idx2,
                                                            workspace=fws)
         hbm_bound["indexer_topk"] = w.decode
-    ms = {}
+    ms, ms_stats = {}, {}
     for name in fns:
         f = fns[name]
         for _ in range(args.warmup):
             f()
-        times = []
-        for _ in range(args.steps):
-            if hbm_bound[name]:
-                flush.sum()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            f()
-            e1.record()
-            times.append((e0, e1))
         torch.cuda.synchronize()
-        ms[name] = float(np.median([a.elapsed_time(b) for a, b in times]))
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            for _ in range(args.steps):
+                if hbm_bound[name]:
+                    flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                f()
+                e1.record()
+                times.append((e0, e1))
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_start >= args.min_time or len(times) >= 20 * args.steps:
+                break
+        v = [a.elapsed_time(b) for a, b in times]
+        ms[name] = float(np.median(v))
+        ms_stats[name] = {"median": round(ms[name], 5), "p10": round(float(np.percentile(v, 10)), 5),
+                          "p90": round(float(np.percentile(v, 90)), 5), "reps": len(v)}
     rs_h, re_h = rs.cpu().numpy().astype(np.int64), re.cpu().numpy().astype(np.int64)
     pairs = int((re_h - rs_h).sum())
     sel = int((idx >= 0).sum().item())
@@ -400,6 +410,7 @@ def stage_bench(args, dsa, synth, np, torch):
                 "gather_gbs": (gather + mla_compulsory) / t["mla"] / 1e9,
                 "frac_hbm": (gather + mla_compulsory) / t["mla"] / 1e9 / HBM_PEAK_GBS},
     }
+    comp["stage_ms_stats"] = ms_stats   # per stage: median, p10, p90 (ms) and repetitions
     if mcache is not None:
         gb = sel * w.d_qk * 2
         comp["mla"]["kv_row_bytes"] = row_bytes
@@ -484,8 +495,11 @@ def stage_bench(args, dsa, synth, np, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=300,
+                    help="timed steps (prefill4k: about 0.5 s); per stage the minimum repetitions")
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--min-time", type=float, default=0.5,
+                    help="stage workloads: repeat each stage until this many seconds have passed")
     ap.add_argument("--workload", default="prefill4k",
                     choices=["prefill4k", "prefill4k_stages", "thd", "decode", "decode_fp8",
                              "fp8_64k", "mxfp4_64k"],
