@@ -373,7 +373,7 @@ def stage_bench(args, dsa, synth, np, torch):
                 e1.record()
                 times.append((e0, e1))
             torch.cuda.synchronize()
-            if time.perf_counter() - t_start >= args.min_time or len(times) >= 20 * args.steps:
+            if time.perf_counter() - t_start >= args.min_time or len(times) >= 4000:
                 break
         v = [a.elapsed_time(b) for a, b in times]
         ms[name] = float(np.median(v))
