@@ -10,9 +10,9 @@
 // Workgroup (row t, chunk c) of 4 waves:
 //   * windows of 8193 .. 131072 keys are cut into 16 chunks of at most 8192
 //     keys (as on the split path of dsa_topk); the workgroup computes the
-//     scores of its chunk (each wave streams 32-key tiles: bf16 keys through
-//     two private LDS buffers by LDS-DMA, fp8 / fp4 keys straight into
-//     registers, the next tile in flight while the current one is on the
+//     scores of its chunk (each wave streams 32-key tiles: bf16 keys over
+//     33..64 heads through two private LDS buffers by LDS-DMA, other keys
+//     straight into registers, the next tile in flight while the current one is on the
 //     matrix core) straight into LDS as order-preserving keys, selects the
 //     chunk's top-k and writes it as candidates (key, column); the merge kernel
 //     of the split top-k then selects the row's top-k from the candidates;
