@@ -72,6 +72,8 @@ __device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t*
   return block_count_range<kThreads>(cnt, lo, hi, sh, kr);  // also orders the LDS writes
 }
 
+constexpr int kShortRow = 2048;  // windows of at most this many keys and k: no selection
+
 // Whole row by one workgroup; writes topk_idx[row] including the -1 padding.
 // Windows of at most CAP keys are held in LDS.
 template <int CAP>
@@ -84,6 +86,47 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64
   int32_t* dst = out + row * int64_t(K);
   uint32_t n_sel;
   auto emit = [&](uint32_t p, int i, uint32_t) { dst[p] = a + i; };
+  if (n <= K && n <= kShortRow) {
+    // every selectable key is selected: the ordered compaction straight from the
+    // scores in registers (wave w: its contiguous segment, lane-strided), one
+    // barrier for the wave totals, no LDS copy of the keys
+    constexpr int kPer = kShortRow / kThreads;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const uint64_t lt = lanemask_lt();
+    int s_lo, s_hi;
+    select_segment<kThreads>(n, s_lo, s_hi);  // at most kShortRow / kWaves keys
+    float x[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = s_lo + j * kWave + lane;
+      x[j] = i < s_hi ? src[i] : -INFINITY;
+    }
+    uint64_t m[kPer];
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      m[j] = __ballot(score_key(x[j]) != 0u);
+      cnt += uint32_t(__popcll(m[j]));
+    }
+    if (lane == 0) sh.seg_cnt[wave] = cnt;
+    __syncthreads();
+    uint32_t base = 0u, total = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = sh.seg_cnt[w];
+      base += w < wave ? c : 0u;
+      total += c;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if ((m[j] >> lane) & 1ull)
+        dst[base + uint32_t(__popcll(m[j] & lt))] = a + s_lo + j * kWave + lane;
+      base += uint32_t(__popcll(m[j]));
+    }
+    for (uint32_t p = total + threadIdx.x; p < uint32_t(K); p += kThreads) dst[p] = -1;
+    return;
+  }
   if (n <= CAP) {
     KeyRange kr;
     n_sel = load_keys<CAP>(src, n, keys, sh, kr);
