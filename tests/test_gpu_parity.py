@@ -626,6 +626,25 @@ def test_mla_fp8_fewer_heads(dsa, H):
     _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, f"H={H}")
 
 
+@pytest.mark.parametrize("n_q,kv_fmt", [(40, "bf16"), (200, "bf16"), (40, "fp8"), (200, "fp8")])
+def test_mla_more_heads_than_a_block(dsa, n_q, kv_fmt):
+    # 160 heads: two head blocks of the grid, the second with one busy wave of
+    # four; 40 queries run the split launch with its combine, 200 the direct one
+    g = np.random.default_rng(216)
+    n_kv, H = 700, 160
+    q = np.concatenate([synth.mla_q(P4K, 0, n_q), synth.mla_q(P4K, 1000, 1000 + n_q)[:, :H - 128]],
+                       axis=1)
+    q = o_prep.round_bf16(q)
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    idx = _random_topk_rows(g, n_q, n_kv, 512, holes=True)
+    rows = range(0, n_q, 1 if n_q < 50 else 9)
+    if kv_fmt == "bf16":
+        _mla_case(dsa, q, o_prep.round_bf16(kv), idx, P4K.sm_scale, P4K.d_v, True, f"bf16 H={H}",
+                  rows=rows)
+    else:
+        _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, f"H={H}", rows=rows)
+
+
 def test_mla_fp8_wide_value_range(dsa):
     # rows whose 128-dim tiles differ in magnitude by 2^-12 .. 2^6 (tiny tiles
     # quantise to e4m3 subnormals), an all-zero row and tiles of zeros
