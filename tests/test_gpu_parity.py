@@ -94,7 +94,7 @@ def test_topk_ties_and_specials(dsa):
     rs = g.integers(0, n, n_q).astype(np.int32)
     re = np.minimum(n, rs + g.integers(0, 500, n_q)).astype(np.int32)
     rs[:3] = [0, 5, 9]; re[:3] = [0, 5, 10]                 # empty, empty, one key
-    for K in (1, 7, 64, 333):
+    for K in (1, 7, 64, 333, 2500):                          # 2500: every row whole, k past 2048
         _topk_case(dsa, S, rs, re, K, f"ties K={K}")
 
 
