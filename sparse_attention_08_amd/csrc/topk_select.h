@@ -18,17 +18,23 @@ constexpr int kMergeThreads = 1024;
 constexpr int kCandCap = 1024;   // boundary-bin keys refined on their own
 constexpr int kRankMax = 128;    // up to this many: refined by counting ranks
 
-template <int NT>
+// BINS: histogram bins (a power of two, at most 2^11: the radix digit); CC: keys
+// of the boundary digit refined on their own.  Smaller values take less LDS.
+template <int NT, int BINS = kBins, int CC = kCandCap>
 struct SelectShared {
   static constexpr int kNW = NT / kWave;
-  uint32_t hist[kBins];
+  static constexpr int kB = BINS;
+  static constexpr int kCC = CC;
+  static constexpr int kDigitBits = __builtin_ctz(BINS);
+  static_assert((BINS & (BINS - 1)) == 0 && BINS <= 2048 && BINS % NT == 0, "histogram bins");
+  uint32_t hist[BINS];
   uint32_t tmp[3 * kNW];
   uint32_t seg_cnt[2 * kNW];
   uint32_t wsum[kNW];  // radix pass: wave totals of the bin counts
   uint32_t pick[3];    // radix pass: the digit, the rank left, the digit's count
   uint32_t ccount;     // boundary-bin keys gathered
-  alignas(16) uint32_t ckey[kCandCap + 4];  // the boundary bin's keys (4 zero keys after the last) ...
-  uint8_t cwave[kCandCap];      // ... and the wave whose segment each came from
+  alignas(16) uint32_t ckey[CC + 4];  // the boundary bin's keys (4 zero keys after the last) ...
+  uint8_t cwave[CC];                  // ... and the wave whose segment each came from
 };
 
 // Keys of a row held in LDS, or read (and mapped) from the fp32 scores.
@@ -127,9 +133,9 @@ struct KeyRange {
 // reduction of per-thread values (two barriers: the first also orders the
 // caller's earlier LDS writes, the second the reuse of tmp).  Returns the count
 // and fills kr.
-template <int NT>
+template <int NT, int B, int C>
 __device__ __forceinline__ uint32_t block_count_range(uint32_t cnt, uint32_t lo, uint32_t hi,
-                                                      SelectShared<NT>& sh, KeyRange& kr) {
+                                                      SelectShared<NT, B, C>& sh, KeyRange& kr) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -159,9 +165,9 @@ __device__ __forceinline__ uint32_t block_count_range(uint32_t cnt, uint32_t lo,
   return cnt;
 }
 
-template <int NT>
+template <int NT, int B = kBins, int C = kCandCap>
 struct RadixSearch {
-  SelectShared<NT>& sh;
+  SelectShared<NT, B, C>& sh;
   uint32_t kmin = 0u;
   int shift = 0;        // d's bits below the digits picked so far
   uint32_t pmask = 0u;
@@ -170,7 +176,7 @@ struct RadixSearch {
 
   template <class Keys>
   __device__ __forceinline__ void init(const Keys& key, int n, int K, const KeyRange& kr) {
-    for (int i = int(threadIdx.x); i < kBins; i += NT) sh.hist[i] = 0u;
+    for (int i = int(threadIdx.x); i < B; i += NT) sh.hist[i] = 0u;
     uint32_t lo = kr.lo, hi = kr.hi;
     if (kr.known) {
       __syncthreads();  // orders the clears before the first pass's counts
@@ -201,11 +207,12 @@ struct RadixSearch {
   template <class Keys>
   __device__ __forceinline__ uint32_t pass(const Keys& keys, int cnt) {
     constexpr int NW = NT / kWave;
-    constexpr int kBPT = kBins / NT;  // histogram bins owned per thread in the scan
+    constexpr int kBPT = B / NT;  // histogram bins owned per thread in the scan
     const int tid = int(threadIdx.x);
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int nb = shift < 11 ? shift : 11;
+    constexpr int kDig = SelectShared<NT, B, C>::kDigitBits;
+    const int nb = shift < kDig ? shift : kDig;
     shift -= nb;
     const uint32_t dmask = (1u << nb) - 1u;
     const uint32_t km = kmin, pm = pmask, pf = prefix;
@@ -264,7 +271,7 @@ struct RadixSearch {
 // equal parts (close scores spread over the histogram instead of piling into a
 // few bins, also across a power of two), and narrow ranges need fewer passes.
 // After the first pass every key
-// outside the boundary digit is decided; when that digit holds at most kCandCap
+// outside the boundary digit is decided; when that digit holds at most CC
 // keys they are gathered (with the wave whose segment they came from) in one
 // more pass over the keys, and the rest of the search runs on them alone: by
 // counting ranks for at most kRankMax of them, else by radix passes over the
@@ -290,9 +297,9 @@ __device__ __forceinline__ void select_segment(int n, int& s_lo, int& s_hi) {
   s_hi = min(n, s_lo + seg);
 }
 
-template <int NT, class Keys>
+template <int NT, class Keys, int B, int C>
 __device__ __forceinline__ SelectThreshold select_search(const Keys& key, int n, uint32_t n_sel,
-                                                         int K, SelectShared<NT>& sh,
+                                                         int K, SelectShared<NT, B, C>& sh,
                                                          const KeyRange& kr = KeyRange{}) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -306,10 +313,10 @@ __device__ __forceinline__ SelectThreshold select_search(const Keys& key, int n,
   bool counted = false;
   if (n_sel > uint32_t(K)) {
     if (tid == 0) sh.ccount = 0u;  // ordered by the barriers of init
-    RadixSearch<NT> rs{sh};
+    RadixSearch<NT, B, C> rs{sh};
     rs.init(key, n, K, kr);
     const uint32_t in_bin = rs.shift > 0 ? rs.pass(key, n) : 0u;
-    if (rs.shift > 0 && in_bin <= uint32_t(kCandCap)) {
+    if (rs.shift > 0 && in_bin <= uint32_t(C)) {
       // gather the boundary digit's keys; count the keys above it per segment
       const uint32_t bin_max = rs.prefix | ~rs.pmask;  // largest d with the boundary digit
       const uint32_t kmin = rs.kmin, pmask = rs.pmask, prefix = rs.prefix;
@@ -385,9 +392,9 @@ __device__ __forceinline__ SelectThreshold select_search(const Keys& key, int n,
   return r;
 }
 
-template <int NT, class Keys, class Emit>
+template <int NT, class Keys, class Emit, int B, int C>
 __device__ __forceinline__ void select_topk(const Keys& key, int n, uint32_t n_sel, int K,
-                                            SelectShared<NT>& sh, Emit emit,
+                                            SelectShared<NT, B, C>& sh, Emit emit,
                                             const KeyRange& kr = KeyRange{}) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
