@@ -8,7 +8,8 @@
 //   1. every score is mapped to an order-preserving u32 key (score_key; -inf ->
 //      0 = not selectable) and the selectable keys are counted;
 //   2. if more than k are selectable, the k-th largest key is found exactly with
-//      MSB-first radix passes of at most 11 bits (2048-bin LDS histogram) that
+//      MSB-first radix passes of at most 11 bits (a 2048-bin LDS histogram; 10
+//      bits and 1024 bins in the rows kernels, for the LDS it frees) that
 //      start at the highest bit in which the selectable keys differ: after them
 //      `thr` is the k-th key and `need_eq` says how many keys equal to it (the
 //      lowest-indexed ones) belong to the selection;

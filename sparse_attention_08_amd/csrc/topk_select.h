@@ -23,8 +23,6 @@ constexpr int kRankMax = 128;    // up to this many: refined by counting ranks
 template <int NT, int BINS = kBins, int CC = kCandCap>
 struct SelectShared {
   static constexpr int kNW = NT / kWave;
-  static constexpr int kB = BINS;
-  static constexpr int kCC = CC;
   static constexpr int kDigitBits = __builtin_ctz(BINS);
   static_assert((BINS & (BINS - 1)) == 0 && BINS <= 2048 && BINS % NT == 0, "histogram bins");
   uint32_t hist[BINS];
