@@ -20,7 +20,8 @@
 //
 // Work layouts:
 //   rows     one workgroup per row; windows of at most 8192 keys are held in
-//            LDS, longer ones are re-read from global memory by each pass;
+//            registers, longer ones are re-read from global memory by each
+//            pass (the split path's chunks hold theirs in LDS);
 //   stream   many rows over more than 8192 columns: the rows kernel takes the
 //            windows of at most 8192 keys, and a second kernel streams each
 //            longer window through LDS with its running top-k;
@@ -40,125 +41,147 @@ namespace {
 
 using namespace topksel;
 
-// Keys of scores[a .. a+n) into LDS (n <= CAP); returns the selectable count.
-// Every thread issues a batch of loads (CAP / 2 / kThreads of them) before it
-// waits for any: a load-then-store loop would wait a full memory round trip
-// per element.
-// The selection state of the rows kernels: a 1024-bin histogram (10-bit digits)
-// and up to 704 boundary-digit keys refined on their own take 7.7 KB instead of
-// 13.4 KB, which makes room for six workgroups per CU beside 4096 keys (five
-// with the 2048-bin state) and four beside 8192 (three): 30.2 -> 28.5 us at
-// prefill4k, 434 -> 397 us at THD.
+// The selection state of the rows and chunk kernels: a 1024-bin histogram
+// (10-bit digits) and up to 704 boundary-digit keys refined on their own take
+// 7.7 KB instead of 13.4 KB (with keys in LDS this made room for six
+// workgroups per CU beside 4096 keys instead of five: 30.2 -> 28.5 us at
+// prefill4k, 434 -> 397 us at THD).
 using RowSel = SelectShared<kThreads, 1024, 704>;
-
-template <int CAP>
-__device__ __forceinline__ uint32_t load_keys(const float* src, int n, uint32_t* keys,
-                                              RowSel& sh, KeyRange& kr) {
-  constexpr int kPer = CAP / 2 / kThreads;
-  uint32_t cnt = 0, lo = 0xFFFFFFFFu, hi = 0u;
-  for (int base = 0; base < n; base += kPer * kThreads) {
-    float v[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = base + int(threadIdx.x) + j * kThreads;
-      v[j] = i < n ? src[i] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = base + int(threadIdx.x) + j * kThreads;
-      if (i < n) {
-        const uint32_t k = score_key(v[j]);
-        keys[i] = k;
-        if (k != 0u) {
-          ++cnt;
-          lo = min(lo, k);
-          hi = max(hi, k);
-        }
-      }
-    }
-  }
-  return block_count_range<kThreads>(cnt, lo, hi, sh, kr);  // also orders the LDS writes
-}
 
 constexpr int kShortRow = 2048;  // windows of at most this many keys and k: no selection
 
-// Whole row by one workgroup; writes topk_idx[row] including the -1 padding.
-// Windows of at most CAP keys are held in LDS.
-template <int CAP>
-__device__ __forceinline__ void row_topk(const float* __restrict__ scores, int64_t ld,
-                                         int64_t row, int a, int b, int32_t K,
-                                         int32_t* __restrict__ out, uint32_t* keys,
-                                         RowSel& sh) {
-  const int n = b > a ? b - a : 0;
-  const float* src = scores + row * ld + a;
-  int32_t* dst = out + row * int64_t(K);
-  uint32_t n_sel;
-  auto emit = [&](uint32_t p, int i, uint32_t) { dst[p] = a + i; };
-  if (n <= K && n <= kShortRow) {
-    // every selectable key is selected: the ordered compaction straight from the
-    // scores in registers (wave w: its contiguous segment, lane-strided), one
-    // barrier for the wave totals, no LDS copy of the keys
-    constexpr int kPer = kShortRow / kThreads;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const uint64_t lt = lanemask_lt();
-    int s_lo, s_hi;
-    select_segment<kThreads>(n, s_lo, s_hi);  // at most kShortRow / kWaves keys
-    float x[kPer];
+// A window of at most min(k, kShortRow) keys: every selectable key is
+// selected.  The ordered compaction straight from the scores in registers (wave
+// w: its contiguous segment, lane-strided), one barrier for the wave totals, no
+// LDS copy of the keys.
+__device__ __forceinline__ void row_topk_short(const float* __restrict__ src, int n, int a,
+                                               int32_t K, int32_t* __restrict__ dst,
+                                               RowSel& sh) {
+  constexpr int kPer = kShortRow / kThreads;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const uint64_t lt = lanemask_lt();
+  int s_lo, s_hi;
+  select_segment<kThreads>(n, s_lo, s_hi);  // at most kShortRow / kWaves keys
+  float x[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+  for (int j = 0; j < kPer; ++j) {
+    const int i = s_lo + j * kWave + lane;
+    x[j] = i < s_hi ? src[i] : -INFINITY;
+  }
+  uint64_t m[kPer];
+  uint32_t cnt = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    m[j] = __ballot(score_key(x[j]) != 0u);
+    cnt += uint32_t(__popcll(m[j]));
+  }
+  if (lane == 0) sh.seg_cnt[wave] = cnt;
+  __syncthreads();
+  uint32_t base = 0u, total = 0u;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = sh.seg_cnt[w];
+    base += w < wave ? c : 0u;
+    total += c;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if ((m[j] >> lane) & 1ull)
+      dst[base + uint32_t(__popcll(m[j] & lt))] = a + s_lo + j * kWave + lane;
+    base += uint32_t(__popcll(m[j]));
+  }
+  for (uint32_t p = total + threadIdx.x; p < uint32_t(K); p += kThreads) dst[p] = -1;
+}
+
+// A window too long for the keys to be held: every pass re-reads (and maps)
+// the scores from global memory.  Returns the selectable count; the caller
+// writes the -1 padding.
+__device__ __forceinline__ uint32_t row_topk_global(const float* __restrict__ src, int n, int a,
+                                                    int32_t K, int32_t* __restrict__ dst,
+                                                    RowSel& sh) {
+  uint32_t cnt = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) cnt += (score_key(src[i]) != 0u);
+  const uint32_t n_sel = block_sum<kThreads>(cnt, sh.tmp);
+  select_topk<kThreads>(GlobalKeys{src}, n, n_sel, K, sh,
+                        [&](uint32_t p, int i, uint32_t) { dst[p] = a + i; });
+  return n_sel;
+}
+
+// The n keys of scores src[0 .. n) into registers, in the layout of the
+// ordered compaction: thread (wave w, lane l) holds key s_lo + j * 64 + l of
+// its wave's segment [s_lo, s_hi) in k[j] (key 0 past s_hi; n <= PER * kThreads).
+// Every load is issued before any is used.  Returns the selectable count and
+// the range of the selectable keys.
+template <int PER>
+__device__ __forceinline__ uint32_t load_keys_regs(const float* __restrict__ src, int n,
+                                                   uint32_t (&k)[PER], int& s_lo, RowSel& sh,
+                                                   KeyRange& kr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int s_hi;
+  select_segment<kThreads>(n, s_lo, s_hi);  // at most PER * kWave keys per wave
+  {
+    float x[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
       const int i = s_lo + j * kWave + lane;
       x[j] = i < s_hi ? src[i] : -INFINITY;
     }
-    uint64_t m[kPer];
-    uint32_t cnt = 0u;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      m[j] = __ballot(score_key(x[j]) != 0u);
-      cnt += uint32_t(__popcll(m[j]));
-    }
-    if (lane == 0) sh.seg_cnt[wave] = cnt;
-    __syncthreads();
-    uint32_t base = 0u, total = 0u;
+    for (int j = 0; j < PER; ++j) k[j] = score_key(x[j]);  // -inf -> 0: not selectable
+  }
+  uint32_t cnt = 0, lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t c = sh.seg_cnt[w];
-      base += w < wave ? c : 0u;
-      total += c;
+  for (int j = 0; j < PER; ++j) {
+    if (k[j] != 0u) {
+      ++cnt;
+      lo = min(lo, k[j]);
+      hi = max(hi, k[j]);
     }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if ((m[j] >> lane) & 1ull)
-        dst[base + uint32_t(__popcll(m[j] & lt))] = a + s_lo + j * kWave + lane;
-      base += uint32_t(__popcll(m[j]));
-    }
-    for (uint32_t p = total + threadIdx.x; p < uint32_t(K); p += kThreads) dst[p] = -1;
+  }
+  return block_count_range<kThreads>(cnt, lo, hi, sh, kr);
+}
+
+// Whole row [a, a + n) by one workgroup; writes dst[0 .. K) including the -1
+// padding.  A window of at most min(k, kShortRow) keys takes the short path;
+// one of at most CAP keys keeps them in registers (CAP / kThreads per thread),
+// so none of the selection's passes reads LDS and the selection state is the
+// only LDS a row takes; a longer one re-reads the scores from memory per pass.
+template <int CAP>
+__device__ __forceinline__ void row_topk(const float* __restrict__ src, int n, int a, int32_t K,
+                                         int32_t* __restrict__ dst, RowSel& sh) {
+  static_assert(CAP % kThreads == 0, "whole keys per thread");
+  uint32_t n_sel;
+  if (n <= K && n <= kShortRow) {
+    row_topk_short(src, n, a, K, dst, sh);
     return;
   }
   if (n <= CAP) {
+    uint32_t k[CAP / kThreads];
+    int s_lo;
     KeyRange kr;
-    n_sel = load_keys<CAP>(src, n, keys, sh, kr);
-    select_topk<kThreads>(LdsKeys{keys}, n, n_sel, K, sh, emit, kr);
+    n_sel = load_keys_regs(src, n, k, s_lo, sh, kr);
+    select_topk<kThreads>(RegKeys<CAP / kThreads>{k, s_lo}, n, n_sel, K, sh,
+                          [&](uint32_t p, int i, uint32_t) { dst[p] = a + i; }, kr);
   } else {
-    uint32_t cnt = 0;
-    for (int i = threadIdx.x; i < n; i += kThreads) cnt += (score_key(src[i]) != 0u);
-    n_sel = block_sum<kThreads>(cnt, sh.tmp);
-    select_topk<kThreads>(GlobalKeys{src}, n, n_sel, K, sh, emit);
+    n_sel = row_topk_global(src, n, a, K, dst, sh);
   }
   const uint32_t k_eff = n_sel < uint32_t(K) ? n_sel : uint32_t(K);
   for (uint32_t p = k_eff + threadIdx.x; p < uint32_t(K); p += kThreads) dst[p] = -1;
 }
 
 // Rows whose window is longer than CAP (skip_long) or at most `skip_below`
-// keys are left to another launch.  CAP = 4096 takes 29.8 KB of LDS instead of
-// 46.2 KB: five workgroups per CU instead of three, which hides more of each
-// row's load latency, so windows of at most 4096 keys go to that instance.
+// keys are left to another launch.  The keys of a window stay in registers
+// (CAP / kThreads per thread: 76 VGPRs at 4096, six workgroups per CU; 108 at
+// 8192, four), and the selection state is the only LDS (7.7 KB): against
+// holding the keys in LDS, 28.8 -> 27.4 us at prefill4k and 387 -> 354 us at
+// THD, the same output.  Windows too long for the registers (possible only
+// when k is past the stream path's limit) re-read the scores from memory.
 template <int CAP>
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_starts,
     const int32_t* __restrict__ row_ends, int n_cols, int32_t K, int32_t* __restrict__ out,
     int skip_long, int skip_below) {
-  __shared__ uint32_t keys[CAP];
   __shared__ RowSel sh;
   // last rows first: in a causal prefill they hold the longest windows, and
   // starting them first leaves the short ones for the end of the launch
@@ -167,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
   const int b = min(row_ends[row], n_cols);
   const int n = b > a ? b - a : 0;
   if ((skip_long && n > CAP) || n <= skip_below) return;
-  row_topk<CAP>(scores, ld, row, a, b, K, out, keys, sh);
+  row_topk<CAP>(scores + row * ld + a, n, a, K, out + row * int64_t(K), sh);
 }
 
 // Split path, phase 1: workgroup (row, c) selects the top-k of chunk c.
@@ -176,7 +199,6 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
     const int32_t* __restrict__ row_ends, int n_cols, int32_t K, int32_t* __restrict__ out,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col,
     int32_t* __restrict__ cand_cnt) {
-  __shared__ uint32_t keys[kCap];
   __shared__ RowSel sh;
   const int64_t row = blockIdx.x;
   const int c = blockIdx.y;
@@ -185,18 +207,20 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   const int n = b > a ? b - a : 0;
   const int clen = split_chunk_len(n);
   if (clen == 0) {
-    if (c == 0) row_topk<kCap>(scores, ld, row, a, b, K, out, keys, sh);
+    if (c == 0) row_topk<kCap>(scores + row * ld + a, n, a, K, out + row * int64_t(K), sh);
     return;
   }
   const int64_t slot = row * kMaxChunks + c;
   const int lo = c * clen;
-  const int m = lo < n ? min(clen, n - lo) : 0;
+  const int m = lo < n ? min(clen, n - lo) : 0;  // at most kCap
+  uint32_t k[kCap / kThreads];
+  int s_lo;
   KeyRange kr;
-  const uint32_t n_sel = load_keys<kCap>(scores + row * ld + a + lo, m, keys, sh, kr);
+  const uint32_t n_sel = load_keys_regs(scores + row * ld + a + lo, m, k, s_lo, sh, kr);
   uint32_t* ck = cand_key + slot * K;
   int32_t* cc = cand_col + slot * K;
   select_topk<kThreads>(
-      LdsKeys{keys}, m, n_sel, K, sh,
+      RegKeys<kCap / kThreads>{k, s_lo}, m, n_sel, K, sh,
       [&](uint32_t p, int i, uint32_t k) {
         ck[p] = k;
         cc[p] = a + lo + i;

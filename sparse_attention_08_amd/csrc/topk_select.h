@@ -112,6 +112,30 @@ __device__ __forceinline__ void for_segment(const Keys& key, int s_lo, int s_hi,
   }
 }
 
+// A row's keys held in registers: thread (wave w, lane l) holds key
+// s_lo + j * 64 + l of its wave's compaction segment [s_lo, s_hi) in k[j]
+// (key 0 past s_hi), so the passes below read no LDS.  The overloads of
+// for_keys and for_segment visit this thread's registers.
+template <int PER>
+struct RegKeys {
+  const uint32_t (&k)[PER];
+  int s_lo;
+};
+// all of this thread's keys (0 past the segment: never counted)
+template <int NT, int PER, class F>
+__device__ __forceinline__ void for_keys(const RegKeys<PER>& key, int, F f) {
+#pragma unroll
+  for (int j = 0; j < PER; ++j) f(key.s_lo + j * kWave + int(threadIdx.x & (kWave - 1)), key.k[j]);
+}
+template <int PER, class F>
+__device__ __forceinline__ void for_segment(const RegKeys<PER>& key, int s_lo, int s_hi, int lane,
+                                            F f) {
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (s_lo + j * kWave < s_hi) f(s_lo + j * kWave + lane, key.k[j]);
+  }
+}
+
 // Radix search for the k-th largest selectable key.  init() takes the min and
 // max of the selectable keys (and clears the histogram, ordered by its
 // barriers); the digits are then taken from d = key - kmin over the bits of
