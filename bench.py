@@ -306,6 +306,7 @@ def stage_bench(args, dsa, synth, np, torch):
                                             w.rope_dim, w.rope_main_dim, w.rope_theta)
     mq = inp["mla_q"].to(torch.bfloat16)
     mkv = inp["mla_kv"].to(torch.bfloat16)
+    inp_w_nonneg = (inp["w"] >= 0).all(dim=1).cpu().numpy()
     cpu_inp = None if args.no_cpu else {n: inp[n] for n in ("q_raw", "k_raw", "w", "mla_q", "mla_kv")}
     del inp
     mla_insert_ms, mcache = None, None
@@ -428,10 +429,22 @@ def stage_bench(args, dsa, synth, np, torch):
                             "frac_hbm": ib / (insert_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if fused:
         fb = idx_bytes - pairs * 4 + lay.n_q * K * 4       # q + k + w read, indices written
+        # rows the fused kernels write without scoring: windows of at most k keys
+        # with no negative head weight (the prefill kernel skips a block of four
+        # rows only when all four are such rows)
+        wn = np.asarray(inp_w_nonneg)
+        whole = ((re_h - rs_h) <= K) & wn
+        if lay.n_q > 256:
+            nb = (lay.n_q + 3) // 4
+            pad = np.ones(nb * 4, bool)
+            pad[:lay.n_q] = whole
+            whole = np.repeat(pad.reshape(nb, 4).all(axis=1), 4)[:lay.n_q]
+        scored = pairs - int((re_h - rs_h)[whole].sum())
         comp["indexer_topk_fused"] = {"ms": ms["indexer_topk"],
                                       "pairs_per_s": pairs / t["indexer_topk"],
-                                      "tflops": idx_flop / t["indexer_topk"] / 1e12,
-                                      "frac_mfma_peak": idx_flop / t["indexer_topk"] / 1e12 / mfma_peak,
+                                      "pairs_scored": scored,
+                                      "tflops": scored * 2 * hd / t["indexer_topk"] / 1e12,
+                                      "frac_mfma_peak": scored * 2 * hd / t["indexer_topk"] / 1e12 / mfma_peak,
                                       "gbs": fb / t["indexer_topk"] / 1e9,
                                       "frac_hbm": fb / t["indexer_topk"] / 1e9 / HBM_PEAK_GBS,
                                       "vs_unfused": (ms["indexer"] + ms["topk"]) / ms["indexer_topk"]}
@@ -587,6 +600,22 @@ def main():
     ms_step = wall * 1e3 / args.steps
     step_ev = stage_ms.pop("step")
 
+    # the fused indexer + top-k (no score matrix), timed after the steps on the
+    # same inputs and checked against the composed selection of the last step
+    idx_f = torch.empty_like(idx)
+    for _ in range(args.warmup):
+        dsa.dsa_indexer_topk(q, k, wt, rs, re, K, out=idx_f)
+    fused_ev = []
+    for _ in range(args.steps):
+        e0, e1 = ev(), ev()
+        e0.record()
+        dsa.dsa_indexer_topk(q, k, wt, rs, re, K, out=idx_f)
+        e1.record()
+        fused_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx), "fused and composed indexer + top-k disagree"
+    fused_ms = [a.elapsed_time(b) for a, b in fused_ev]
+
     pairs = lay.n_q * (lay.n_q + 1) // 2                               # valid (t, s), s <= t
     mla_pairs = sum(min(t + 1, K) for t in range(lay.n_q))            # selected (t, j)
     avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
@@ -605,6 +634,16 @@ def main():
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
         # per-launch HIP-event times over the timed steps (ms): mean, p10, median, p90
         "stage_ms_stats": stats,
+        # dsa_indexer_topk on the same inputs: the scores stay in LDS (no score
+        # matrix); a row whose window holds at most k keys and whose head weights
+        # are >= 0 is its whole window and is written without scoring
+        "indexer_topk_fused": {
+            "ms": {"mean": round(float(np.mean(fused_ms)), 4), "p10": pct(fused_ms, 10),
+                   "median": pct(fused_ms, 50), "p90": pct(fused_ms, 90)},
+            "composed_over_fused": (avg["indexer"] + avg["topk"]) / float(np.mean(fused_ms)),
+            "pairs_scored": pairs - sum(t + 1 for t in range(min(lay.n_q, K))),
+            "step_ms_with_fused": float(np.mean(fused_ms)) + avg["mla"],
+        },
     }
     # dominant kernel of the step
     dom = max(avg, key=avg.get)

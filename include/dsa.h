@@ -276,6 +276,11 @@ int dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_starts,
  *   n_k <= 8192).
  * Otherwise (F32, or index_topk > 2048) the scores go through the workspace
  * (n_q * n_k * 4 bytes, plus dsa_topk's workspace).
+ * In the bf16, fp8 and MXFP4 paths (index_topk <= 2048), a row whose window
+ * holds at most index_topk keys and whose head weights are all >= 0 is written
+ * as its whole window (columns a .. b-1, then -1) without being scored: none of
+ * its scores can be -inf, so the selection is every key.  Key scales must be
+ * positive, as dsa_indexer_prep and dsa_indexer_k_insert write them.
  */
 size_t dsa_indexer_topk_workspace_size(int64_t n_q, int64_t n_k, int32_t n_heads,
                                        int32_t head_dim, int32_t dtype,

@@ -80,6 +80,19 @@ struct OpFp4 {
 
 constexpr int kKeyTile = 32;
 
+// A window of at most k keys selects every key whose score is not -inf.  With
+// no negative head weight no score is: w * ReLU(x) is >= 0 or +inf (NaN, from
+// an infinite weight against a zero logit, is not a valid score), and the key
+// scales are positive.  True (uniform over the wave) when row t's H weights are
+// all >= 0; such a row's top-k is its whole window and the fused kernels write
+// it without scoring.
+__device__ __forceinline__ bool row_weights_nonneg(const float* __restrict__ w, int64_t t, int H,
+                                                   int lane) {
+  bool ok = true;
+  for (int h = lane; h < H; h += kWave) ok = ok && w[t * H + h] >= 0.0f;
+  return __ballot(!ok) == 0ull;
+}
+
 // q[t] fragments and the matching head weights of one query row, per lane.
 // MXFP4 queries: token t's H code rows (64 bytes each) are followed by its H
 // scale quads (4 E8M0 bytes each), so a token takes H * 68 bytes.

@@ -111,6 +111,12 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_chunk_kernel(
   const int n = b > a ? b - a : 0;
   const int clen = split_chunk_len(n);
   if (clen == 0 && c != 0) return;
+  if (n <= K && ixcore::row_weights_nonneg(w, t, H, lane)) {
+    // the whole window is the top-k (row_weights_nonneg): written without scoring
+    int32_t* dst = out + t * int64_t(K);
+    for (int j = threadIdx.x; j < K; j += kThreads) dst[j] = j < n ? a + j : -1;
+    return;
+  }
 
   QueryRow<Op, MT> qr;
   qr.load(q, w, t, H, lane);

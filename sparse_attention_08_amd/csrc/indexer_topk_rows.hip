@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kFThreads) void indexer_topk_rows_kernel(
   __shared__ int win[2 * kFRows];
   __shared__ int span[2];
   __shared__ int scored[kFRows];  // per row: every key before it is in the ring
+  __shared__ bool trivial[kFRows];  // per row: its top-k is its whole window
   __shared__ __attribute__((aligned(16))) Held<ColT> held[kFRows];
 
   const int tid = threadIdx.x;
@@ -165,6 +166,15 @@ __global__ __launch_bounds__(kFThreads) void indexer_topk_rows_kernel(
     scored[tid] = a;
   }
   __syncthreads();
+  // rows of at most k keys and no negative weight are their whole windows
+  // (row_weights_nonneg); a workgroup whose rows all are returns before any load
+  if (tid < kFRows * kWave) {
+    const int r = tid / kWave;
+    const int64_t t = t0 + r;
+    const bool whole = t >= n_q || (win[kFRows + r] - win[r] <= K &&
+                                    ixcore::row_weights_nonneg(w, t, H, lane));
+    if (lane == 0) trivial[r] = whole;
+  }
   if (tid == 0) {
     int lo = INT_MAX, hi = INT_MIN;
     for (int i = 0; i < kFRows; ++i)
@@ -176,6 +186,16 @@ __global__ __launch_bounds__(kFThreads) void indexer_topk_rows_kernel(
     span[1] = hi;
   }
   __syncthreads();
+  static_assert(kFRows == 4, "four rows per workgroup");
+  if (trivial[0] && trivial[1] && trivial[2] && trivial[3]) {
+    for (int r = 0; r < kFRows; ++r) {
+      const int64_t t = t0 + r;
+      if (t >= n_q) continue;
+      const int a = win[r], n = win[kFRows + r] - a;
+      for (int j = tid; j < K; j += kFThreads) out[t * int64_t(K) + j] = j < n ? a + j : -1;
+    }
+    return;
+  }
   const int lo = __builtin_amdgcn_readfirstlane(span[0]);
   const int hi = __builtin_amdgcn_readfirstlane(span[1]);
   const int nchunks = hi > lo ? (hi - lo + CK - 1) / CK : 0;

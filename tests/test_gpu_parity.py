@@ -903,6 +903,32 @@ def test_indexer_topk_prefill_ties_and_signs(dsa):
         _fused_vs_unfused(dsa, q, k, wt, None, i32(rs), i32(re), K, f"ties K={K}")
 
 
+@pytest.mark.parametrize("n_q", [200, 1200])
+def test_indexer_topk_short_windows(dsa, n_q):
+    # windows of at most k keys: with no negative weight in the row every key is
+    # selected and the fused kernels write the window without scoring it; a row
+    # with one negative weight is scored.  200 rows take the decode kernel, 1200
+    # the prefill kernel (blocks of four rows that are all short skip their loads)
+    g = np.random.default_rng(305)
+    n_k, K = 5000, 2048
+    lay = synth.layout_from_lengths([n_k])
+    p, _, _ = canonical_indexer(P4K, lay, "bf16", rope=False)
+    p = dict(p, q=p["q"][:n_q], w=p["w"][:n_q].copy())
+    rs = g.integers(0, n_k, n_q).astype(np.int32)
+    re = np.minimum(n_k, rs + g.integers(0, K + 1, n_q)).astype(np.int32)  # at most K keys
+    re[::7] = np.minimum(n_k, rs[::7] + g.integers(K + 1, n_k + 1, len(rs[::7])))  # some longer
+    p["w"][3::11, 5] = -0.25  # one negative weight: scored
+    q, k, wt, _ = to_device_indexer(p, "bf16")
+    say(f"fused short windows: n_q={n_q}")
+    _, ref = _fused_vs_unfused(dsa, q, k, wt, None, i32(rs), i32(re), K, f"short n_q={n_q}")
+    r = host(ref)
+    for t in range(n_q):
+        n = re[t] - rs[t]
+        if n <= K:
+            np.testing.assert_array_equal(r[t, :n], np.arange(rs[t], re[t]))
+            assert (r[t, n:] == -1).all()
+
+
 def test_indexer_topk_prefill_wide_columns(dsa):
     # more than 65536 keys: the held columns are 32-bit
     g = np.random.default_rng(304)
