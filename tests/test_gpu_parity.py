@@ -685,6 +685,24 @@ def test_mla_tile_counts(dsa, n_q):
     _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, f"tile counts n_q={n_q}", rows=rows)
 
 
+@pytest.mark.parametrize("n_q", [8, 200])
+def test_mla_index_width_not_a_tile_multiple(dsa, n_q):
+    # index rows whose width is not a whole number of 32-key tiles: the row's
+    # last tile runs past its end, and with few queries the split slices divide
+    # a tile count that is not a multiple of the number of splits
+    g = np.random.default_rng(223)
+    n_kv = 3000
+    q = o_prep.round_bf16(synth.mla_q(P4K, 0, n_q))
+    kv = synth.mla_kv(P4K, 0, n_kv)
+    rows = list(range(n_q)) if n_q < 50 else list(range(0, 20)) + list(range(180, 200))
+    for K in (100, 1007):
+        idx = _random_topk_rows(g, n_q, n_kv, K, holes=True)
+        assert (idx[rows, K - 1] >= 0).any()  # some rows use the row's last column
+        _mla_case(dsa, q, o_prep.round_bf16(kv), idx, P4K.sm_scale, P4K.d_v, True,
+                  f"width {K} bf16 n_q={n_q}", rows=rows)
+        _mla_fp8_case(dsa, q, kv, idx, P4K.sm_scale, f"width {K} n_q={n_q}", rows=rows)
+
+
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 def test_mla_kv_insert_bytes(dsa, src):
     # every written byte equals the oracle's quantisation; other slots untouched
